@@ -1,0 +1,203 @@
+"""CPU oracle for certified quantized-KV decode attention (numpy front end).
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
+CPU-baseline leg may import this package; the product path never does.  The
+arithmetic lives in kvq_oracle.c (plain C loops, fp64) and follows
+"Runtime-Certified Bounded-Error Quantized Attention", technical summary,
+Methodology 1 (tiered INT8-key / INT4-value storage with FP16 originals) and
+Methodology 2 (key and value error terms computed online).  The readings of
+the page used here are spelled out in kvq_oracle.c's header.
+
+All fp16 arrays are numpy float16 (IEEE binary16); layouts are those of the
+header of kvq_oracle.c.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+D = 128
+BLK = 64
+VG = 32
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_build.LIB) or os.path.getmtime(_build.LIB) < os.path.getmtime(_build.SRC):
+            _build.build()
+        L = ctypes.CDLL(_build.LIB)
+        P = ctypes.c_void_p
+        i32, i64, f32 = ctypes.c_int, ctypes.c_int64, ctypes.c_float
+        L.kvqo_f16_to_f64.argtypes = [ctypes.c_uint16]
+        L.kvqo_f16_to_f64.restype = ctypes.c_double
+        L.kvqo_f32_to_f16.argtypes = [f32]
+        L.kvqo_f32_to_f16.restype = ctypes.c_uint16
+        L.kvqo_f32_to_f16_array.argtypes = [P, P, i64]
+        L.kvqo_f32_to_f16_array.restype = None
+        L.kvqo_tree128.argtypes = [P]
+        L.kvqo_tree128.restype = ctypes.c_double
+        L.kvqo_qnorm.argtypes = [P]
+        L.kvqo_qnorm.restype = f32
+        L.kvqo_group_qnorm.argtypes = [P, i32, i32, i32, i32]
+        L.kvqo_group_qnorm.restype = f32
+        L.kvqo_key_bound.argtypes = [f32, f32, f32]
+        L.kvqo_key_bound.restype = f32
+        L.kvqo_quant_k_row.argtypes = [P, P, P, P]
+        L.kvqo_quant_k_row.restype = None
+        L.kvqo_quant_v_row.argtypes = [P, P, P, P]
+        L.kvqo_quant_v_row.restype = None
+        L.kvqo_quantize_cache.argtypes = [i32, i32, i64, i64, P, P, P, P, P, P, P, P]
+        L.kvqo_quantize_cache.restype = None
+        L.kvqo_bounds.argtypes = [i32, i32, i32, i64, i64, P, f32, f32, f32, P, P, P, P, P]
+        L.kvqo_bounds.restype = None
+        L.kvqo_attention.argtypes = [i32, i32, i32, i64, i64, P, f32, f32, f32,
+                                     P, P, P, P, P, P, P, P, P, P]
+        L.kvqo_attention.restype = None
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    return ctypes.c_void_p(a.ctypes.data) if a is not None else None
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+# ----------------------------------------------------------------- scalars
+
+def f16_bits_to_f64(bits: int) -> float:
+    return lib().kvqo_f16_to_f64(int(bits) & 0xFFFF)
+
+
+def f32_to_f16_bits(x: float) -> int:
+    return int(lib().kvqo_f32_to_f16(float(np.float32(x))))
+
+
+def f32_to_f16_array(x):
+    """float32 array -> uint16 fp16 bit patterns (RNE)."""
+    x = _c(x, np.float32)
+    out = np.zeros(x.shape, np.uint16)
+    lib().kvqo_f32_to_f16_array(_p(x), _p(out), x.size)
+    return out
+
+
+def tree128(v) -> float:
+    v = _c(v, np.float64)
+    assert v.shape == (D,)
+    return lib().kvqo_tree128(_p(v))
+
+
+def qnorm(q) -> float:
+    q = _c(q, np.float16)
+    assert q.shape == (D,)
+    return float(np.float32(lib().kvqo_qnorm(_p(q))))
+
+
+def key_bound(sm: float, qn: float, kerr: float) -> float:
+    return float(np.float32(lib().kvqo_key_bound(sm, qn, kerr)))
+
+
+def quant_k_row(x):
+    """Returns (codes int8[128], scale float16, err float32)."""
+    x = _c(x, np.float16)
+    codes = np.zeros(D, np.int8)
+    scale = np.zeros(1, np.float16)
+    err = np.zeros(1, np.float32)
+    lib().kvqo_quant_k_row(_p(x), _p(codes), _p(scale), _p(err))
+    return codes, scale[0], err[0]
+
+
+def quant_v_row(x):
+    """Returns (codes int8[128] in [-7,7], scales float16[4], err float32)."""
+    x = _c(x, np.float16)
+    codes = np.zeros(D, np.int8)
+    scales = np.zeros(4, np.float16)
+    err = np.zeros(1, np.float32)
+    lib().kvqo_quant_v_row(_p(x), _p(codes), _p(scales), _p(err))
+    return codes, scales, err[0]
+
+
+# ----------------------------------------------------------------- cache
+
+class Cache:
+    """The oracle's own quantized cache (tier 1) for fp16 tier-2 arrays."""
+
+    def __init__(self, k16, v16, length):
+        k16 = _c(k16, np.float16)
+        v16 = _c(v16, np.float16)
+        B, Hkv, cap, d = k16.shape
+        assert d == D and cap % BLK == 0 and v16.shape == k16.shape and 0 <= length <= cap
+        self.B, self.Hkv, self.cap, self.length = B, Hkv, cap, int(length)
+        self.k16, self.v16 = k16, v16
+        nb = cap // BLK
+        self.k_codes = np.zeros((B, Hkv, cap, D), np.int8)
+        self.k_scales = np.zeros((B, Hkv, cap), np.float16)
+        self.v_codes = np.zeros((B, Hkv, nb, D, BLK // 2), np.uint8)
+        self.v_scales = np.zeros((B, Hkv, cap, D // VG), np.float16)
+        self.k_err = np.zeros((B, Hkv, nb), np.float32)
+        self.v_err = np.zeros((B, Hkv, nb), np.float32)
+        lib().kvqo_quantize_cache(B, Hkv, cap, self.length, _p(k16), _p(v16), _p(self.k_codes),
+                                  _p(self.k_scales), _p(self.v_codes), _p(self.v_scales),
+                                  _p(self.k_err), _p(self.v_err))
+
+    @property
+    def nblocks(self):
+        return (self.length + BLK - 1) // BLK
+
+    def v_codes_unpacked(self):
+        """int8 [B][Hkv][cap][128] in [-8, 7] read back from the packed layout."""
+        vc = self.v_codes  # [B][Hkv][nb][D][32]
+        lo = (vc & 0x0F).astype(np.int16)
+        hi = (vc >> 4).astype(np.int16)
+        tok = np.stack([lo, hi], axis=-1).reshape(self.B, self.Hkv, -1, D, BLK)  # [..nb, D, 64]
+        tok = np.where(tok >= 8, tok - 16, tok).astype(np.int8)
+        return tok.transpose(0, 1, 2, 4, 3).reshape(self.B, self.Hkv, -1, D)
+
+    def bounds(self, q, sm, tau_k, tau_v):
+        """kb, vb float32 and mask uint8, each [B][Hkv][nblocks]."""
+        q = _c(q, np.float16)
+        B, Hq, d = q.shape
+        assert B == self.B and d == D and Hq % self.Hkv == 0
+        nb = self.nblocks
+        kb = np.zeros((B, self.Hkv, nb), np.float32)
+        vb = np.zeros((B, self.Hkv, nb), np.float32)
+        mask = np.zeros((B, self.Hkv, nb), np.uint8)
+        lib().kvqo_bounds(B, Hq, self.Hkv, self.cap, self.length, _p(q), sm, tau_k, tau_v,
+                          _p(self.k_err), _p(self.v_err), _p(kb), _p(vb), _p(mask))
+        return kb, vb, mask
+
+    def attention(self, q, sm, tau_k, tau_v):
+        """fp64 output [B][Hq][128] and mask uint8 [B][Hkv][nblocks]."""
+        q = _c(q, np.float16)
+        B, Hq, d = q.shape
+        assert B == self.B and d == D and Hq % self.Hkv == 0
+        out = np.zeros((B, Hq, D), np.float64)
+        mask = np.zeros((B, self.Hkv, max(self.nblocks, 1)), np.uint8)
+        lib().kvqo_attention(B, Hq, self.Hkv, self.cap, self.length, _p(q), sm, tau_k, tau_v,
+                             _p(self.k16), _p(self.v16), _p(self.k_codes), _p(self.k_scales),
+                             _p(self.v_codes), _p(self.v_scales), _p(self.k_err), _p(self.v_err),
+                             _p(out), _p(mask))
+        return out, mask[:, :, : self.nblocks]
+
+
+def tau_for_fraction(values, frac):
+    """Tolerance that makes about `frac` of `values` exceed it: the midpoint
+    between the sorted values around rank N - max(1, round(frac*N)).
+    Non-finite values always exceed any finite tolerance and are ignored."""
+    v = np.sort(np.asarray(values, np.float64).ravel())
+    v = v[np.isfinite(v)]
+    n = v.size
+    if n == 0:
+        return float("inf")
+    k = max(1, int(round(frac * n)))
+    if k >= n:
+        return 0.0
+    lo, hi = v[n - k - 1], v[n - k]
+    return float(np.float32((lo + hi) / 2.0))

@@ -1,0 +1,415 @@
+/*
+ * kvq_oracle.c -- plain CPU oracle for certified quantized-KV decode attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * CPU-baseline leg of the benchmark may load this library.  The product path
+ * (the HIP library and its Python binding) never calls it and shares no code,
+ * header, table or helper with it.
+ *
+ * Source of the method: "Runtime-Certified Bounded-Error Quantized Attention"
+ * (gist.science explainer of arXiv 2605.20868), technical summary:
+ *   - Methodology 1, "Tiered Storage with Deterministic Fallback": tier 1 holds
+ *     INT8 keys and INT4 values with scales and per-block error annotations;
+ *     tier 2 holds the FP16 originals used as ground truth for fallback.
+ *   - Methodology 2, "Two-Term Error Decomposition": a key term driven by the
+ *     per-token score perturbation and a value term driven by per-block value
+ *     reconstruction errors, both computed online from scales and query norms.
+ *   - Key Contributions, "Deterministic Recovery": when a bound cannot be met
+ *     the exact dense FP16 result is recovered.
+ * The page prints no formulas or constants for these steps.  The readings this
+ * oracle implements (each listed in the design notes) are:
+ *   K codec  : int8 per token and KV head, fp16 scale s = f16(f32(absmax)/127),
+ *              c = clamp(RNE(x/s), -127, 127); s == 0 gives c == 0.
+ *   V codec  : int4 per token and 32-channel group, fp16 scale
+ *              s = f16(f32(absmax)/7), c = clamp(RNE(x/s), -7, 7).
+ *   non-finite rows/groups: codes 0, scale 0, error +Inf (forces fallback).
+ *   key error  k_err(token) = f32(sqrt(T128(e_j^2))), e = x - s*c (exact);
+ *   value error v_err(token) = max_j |x_j - s*c_j| (exact);
+ *   block statistics = max over the block's valid tokens.
+ *   query norm qn_h = f32(sqrt(T128(q_j^2))); qn(b,kvh) = max over its group.
+ *   key bound  KB = ((sm*qn)*k_err)*(1+2^-16) in fp32 (Cauchy-Schwarz on the
+ *              logit perturbation, inflated past fp32 rounding);
+ *   value bound VB = v_err;
+ *   fallback   fb_k = !(KB finite and KB <= tau_k), likewise fb_v with VB
+ *              and tau_v, per (batch, kv head, 64-token block).
+ *   attention  fp64 softmax attention over k~ = fb_k ? K16 : s*c and
+ *              v~ = fb_v ? V16 : s*c, tokens t < length.
+ * T128 is a pinned fp64 summation tree over 128 terms: within each run of 8
+ * contiguous terms, pairwise with strides 1, 2, 4; then across the 16 run sums
+ * with strides 64, 32, 16, 8 (in terms).  Every element pair it adds is fixed,
+ * so the result is a fixed function of the inputs.
+ *
+ * Physical layouts (per batch b and KV head h; cap = capacity, a multiple of 64):
+ *   k16, v16  : uint16 fp16 bits [B][Hkv][cap][128]
+ *   k_codes   : int8  [B][Hkv][cap][128]
+ *   k_scales  : fp16  [B][Hkv][cap]
+ *   v_codes   : uint8 [B][Hkv][cap/64][128][32]  per 64-token block, channel-
+ *               major: byte (j, i) holds token 2i of channel j in its low
+ *               nibble and token 2i+1 in its high nibble, two's complement.
+ *               Nibbles of tokens >= length inside a written block are 0.
+ *   v_scales  : fp16  [B][Hkv][cap][4]
+ *   k_err, v_err : float [B][Hkv][cap/64]
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define D 128
+#define BLK 64
+#define VG 32
+
+/* ---------------------------------------------------------------- fp16 */
+
+/* Exact value of an IEEE binary16 bit pattern. */
+double kvqo_f16_to_f64(uint16_t h)
+{
+    int sign = h >> 15;
+    int e = (h >> 10) & 31;
+    int m = h & 1023;
+    double v;
+    if (e == 31)
+        v = m ? NAN : INFINITY;
+    else if (e == 0)
+        v = ldexp((double)m, -24);
+    else
+        v = ldexp((double)(m + 1024), e - 25);
+    return sign ? -v : v;
+}
+
+/* binary32 -> binary16, round to nearest, ties to even (IEEE 754). */
+uint16_t kvqo_f32_to_f16(float f)
+{
+    uint16_t sign = signbit(f) ? 0x8000 : 0;
+    if (isnan(f))
+        return sign | 0x7E00;
+    double x = fabs((double)f);
+    if (x == 0.0)
+        return sign;
+    if (isinf(f))
+        return sign | 0x7C00;
+    int E;
+    frexp(x, &E);
+    E -= 1; /* x in [2^E, 2^(E+1)) */
+    if (E < -14) {
+        /* subnormal range: multiples of 2^-24; r == 1024 is the least normal */
+        double r = nearbyint(ldexp(x, 24));
+        return sign | (uint16_t)r;
+    }
+    double r = nearbyint(ldexp(x, 10 - E)); /* 11-bit significand, RNE */
+    if (r == 2048.0) {
+        r = 1024.0;
+        E += 1;
+    }
+    if (E > 15)
+        return sign | 0x7C00;
+    return sign | (uint16_t)(((E + 15) << 10) | ((int)r - 1024));
+}
+
+/* Element-wise kvqo_f32_to_f16 over n values. */
+void kvqo_f32_to_f16_array(const float *in, uint16_t *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = kvqo_f32_to_f16(in[i]);
+}
+
+/* ---------------------------------------------------------------- T128 */
+
+/* The pinned fp64 summation tree over 128 terms (see header). */
+double kvqo_tree128(const double *in)
+{
+    double v[D];
+    memcpy(v, in, sizeof v);
+    for (int st = 1; st <= 4; st *= 2)
+        for (int i = 0; i < D; i += 2 * st)
+            v[i] += v[i + st];
+    for (int st = 64; st >= 8; st /= 2)
+        for (int i = 0; i < st; i += 8)
+            v[i] += v[i + st];
+    return v[0];
+}
+
+/* ||q||_2 of one 128-channel fp16 query row: f32(sqrt(T128(q_j^2))). */
+float kvqo_qnorm(const uint16_t *q)
+{
+    double sq[D];
+    for (int j = 0; j < D; ++j) {
+        double x = kvqo_f16_to_f64(q[j]);
+        sq[j] = x * x; /* exact: 22 significant bits */
+    }
+    return (float)sqrt(kvqo_tree128(sq));
+}
+
+/* ---------------------------------------------------------------- codec */
+
+/* RNE(x / s) for fp16-valued x and s != 0: IEEE binary32 division then rint.
+ * The division's rounding cannot move the quotient across a half-integer
+ * (the quotient of two 11-bit significands is at least 2^-12 away from any
+ * half-integer it does not equal), so this is RNE of the exact quotient. */
+static int rne_div(double x, float s)
+{
+    float q = (float)x / s;
+    return (int)rintf(q);
+}
+
+static int clampi(int c, int lo, int hi) { return c < lo ? lo : (c > hi ? hi : c); }
+
+/* Quantize one key row of 128 fp16 values. */
+void kvqo_quant_k_row(const uint16_t *x16, int8_t *codes, uint16_t *scale, float *err)
+{
+    double x[D];
+    double a = 0.0;
+    int finite = 1;
+    for (int j = 0; j < D; ++j) {
+        x[j] = kvqo_f16_to_f64(x16[j]);
+        if (!isfinite(x[j]))
+            finite = 0;
+        else if (fabs(x[j]) > a)
+            a = fabs(x[j]);
+    }
+    if (!finite) {
+        memset(codes, 0, D);
+        *scale = 0;
+        *err = INFINITY;
+        return;
+    }
+    uint16_t sh = kvqo_f32_to_f16((float)a / 127.0f);
+    double s = kvqo_f16_to_f64(sh);
+    double sq[D];
+    for (int j = 0; j < D; ++j) {
+        int c = (s == 0.0) ? 0 : clampi(rne_div(x[j], (float)s), -127, 127);
+        double e = x[j] - s * (double)c; /* exact in fp64 (and in fp32) */
+        codes[j] = (int8_t)c;
+        sq[j] = e * e;                   /* exact: at most 48 significant bits */
+    }
+    *scale = sh;
+    *err = (float)sqrt(kvqo_tree128(sq));
+}
+
+/* Quantize one value row: 4 groups of 32 channels.  Writes 128 int4 codes as
+ * ints in [-7, 7], 4 scales, and returns the row's max |v - v^|. */
+void kvqo_quant_v_row(const uint16_t *x16, int8_t *codes, uint16_t *scales, float *err)
+{
+    double row_err = 0.0;
+    for (int g = 0; g < D / VG; ++g) {
+        double x[VG];
+        double a = 0.0;
+        int finite = 1;
+        for (int j = 0; j < VG; ++j) {
+            x[j] = kvqo_f16_to_f64(x16[g * VG + j]);
+            if (!isfinite(x[j]))
+                finite = 0;
+            else if (fabs(x[j]) > a)
+                a = fabs(x[j]);
+        }
+        if (!finite) {
+            for (int j = 0; j < VG; ++j)
+                codes[g * VG + j] = 0;
+            scales[g] = 0;
+            row_err = INFINITY;
+            continue;
+        }
+        uint16_t sh = kvqo_f32_to_f16((float)a / 7.0f);
+        double s = kvqo_f16_to_f64(sh);
+        scales[g] = sh;
+        for (int j = 0; j < VG; ++j) {
+            int c = (s == 0.0) ? 0 : clampi(rne_div(x[j], (float)s), -7, 7);
+            double e = fabs(x[j] - s * (double)c); /* exact */
+            codes[g * VG + j] = (int8_t)c;
+            if (e > row_err)
+                row_err = e;
+        }
+    }
+    *err = (float)row_err;
+}
+
+/* ---------------------------------------------------------------- cache */
+
+static size_t row_index(int b, int h, int64_t t, int Hkv, int64_t cap)
+{
+    return ((size_t)b * Hkv + h) * (size_t)cap + (size_t)t;
+}
+
+static size_t blk_index(int b, int h, int64_t blk, int Hkv, int64_t cap)
+{
+    return ((size_t)b * Hkv + h) * (size_t)(cap / BLK) + (size_t)blk;
+}
+
+/* Byte offset of (token t, channel j) in v_codes, and whether it is the high
+ * nibble. */
+static size_t v_byte(int b, int h, int64_t t, int j, int Hkv, int64_t cap, int *high)
+{
+    *high = (int)(t & 1);
+    return blk_index(b, h, t / BLK, Hkv, cap) * (size_t)(D * BLK / 2) + (size_t)j * (BLK / 2) +
+           (size_t)((t % BLK) / 2);
+}
+
+/* Quantize tokens [0, length) of every (b, kv head) from scratch.  Blocks that
+ * hold at least one valid token get their statistics and v_codes bytes fully
+ * defined; other blocks are left untouched. */
+void kvqo_quantize_cache(int B, int Hkv, int64_t cap, int64_t length, const uint16_t *k16,
+                         const uint16_t *v16, int8_t *k_codes, uint16_t *k_scales, uint8_t *v_codes,
+                         uint16_t *v_scales, float *k_err, float *v_err)
+{
+    int64_t nblk = (length + BLK - 1) / BLK;
+#pragma omp parallel for collapse(3) schedule(dynamic)
+    for (int b = 0; b < B; ++b)
+        for (int h = 0; h < Hkv; ++h)
+            for (int64_t blk = 0; blk < nblk; ++blk) {
+                float kmax = 0.0f, vmax = 0.0f;
+                int high;
+                size_t byte0 = v_byte(b, h, blk * BLK, 0, Hkv, cap, &high);
+                memset(v_codes + byte0, 0, D * BLK / 2);
+                for (int64_t t = blk * BLK; t < length && t < (blk + 1) * BLK; ++t) {
+                    size_t r = row_index(b, h, t, Hkv, cap);
+                    float ke, ve;
+                    kvqo_quant_k_row(k16 + r * D, k_codes + r * D, k_scales + r, &ke);
+                    int8_t vc[D];
+                    kvqo_quant_v_row(v16 + r * D, vc, v_scales + r * (D / VG), &ve);
+                    for (int j = 0; j < D; ++j) {
+                        size_t o = v_byte(b, h, t, j, Hkv, cap, &high);
+                        uint8_t nib = (uint8_t)vc[j] & 0x0F;
+                        v_codes[o] |= high ? (uint8_t)(nib << 4) : nib;
+                    }
+                    if (ke > kmax)
+                        kmax = ke;
+                    if (ve > vmax)
+                        vmax = ve;
+                }
+                size_t s = blk_index(b, h, blk, Hkv, cap);
+                k_err[s] = kmax;
+                v_err[s] = vmax;
+            }
+}
+
+/* ---------------------------------------------------------------- bounds */
+
+/* Per-(b, kv head) group query norm: max over the G heads of the group
+ * (heads h*G .. h*G+G-1); NaN if any head's norm is NaN. */
+float kvqo_group_qnorm(const uint16_t *q, int b, int h, int Hq, int G)
+{
+    float qn = 0.0f;
+    int any_nan = 0;
+    for (int g = 0; g < G; ++g) {
+        float n = kvqo_qnorm(q + ((size_t)b * Hq + (size_t)h * G + g) * D);
+        if (isnan(n))
+            any_nan = 1;
+        else if (n > qn)
+            qn = n;
+    }
+    return any_nan ? NAN : qn;
+}
+
+/* Key bound of one block: ((sm*qn)*k_err)*(1+2^-16), fp32, left to right.
+ * volatile stores force each product to be rounded to binary32. */
+float kvqo_key_bound(float sm, float qn, float kerr)
+{
+    volatile float p1 = sm * qn;
+    volatile float p2 = p1 * kerr;
+    volatile float p3 = p2 * (1.0f + 0x1p-16f);
+    return p3;
+}
+
+/* A block keeps its quantized tile only when its bound is certified: finite
+ * and not above the tolerance.  NaN or +Inf bounds (non-finite inputs) always
+ * fall back, whatever the tolerance. */
+static int falls_back(float bound, float tau)
+{
+    return !(isfinite(bound) && bound <= tau);
+}
+
+void kvqo_bounds(int B, int Hq, int Hkv, int64_t cap, int64_t length, const uint16_t *q, float sm,
+                 float tau_k, float tau_v, const float *k_err, const float *v_err, float *kb,
+                 float *vb, uint8_t *mask)
+{
+    int G = Hq / Hkv;
+    int64_t nblk = (length + BLK - 1) / BLK;
+    for (int b = 0; b < B; ++b)
+        for (int h = 0; h < Hkv; ++h) {
+            float qn = kvqo_group_qnorm(q, b, h, Hq, G);
+            for (int64_t blk = 0; blk < nblk; ++blk) {
+                size_t s = blk_index(b, h, blk, Hkv, cap);
+                size_t o = ((size_t)b * Hkv + h) * (size_t)nblk + (size_t)blk;
+                float kbv = kvqo_key_bound(sm, qn, k_err[s]);
+                float vbv = v_err[s];
+                uint8_t m = (uint8_t)(falls_back(kbv, tau_k) | (falls_back(vbv, tau_v) << 1));
+                if (kb)
+                    kb[o] = kbv;
+                if (vb)
+                    vb[o] = vbv;
+                if (mask)
+                    mask[o] = m;
+            }
+        }
+}
+
+/* ---------------------------------------------------------------- attention */
+
+/* fp64 attention for every (b, query head).  out: double [B][Hq][128];
+ * mask: uint8 [B][Hkv][ceil(length/64)] (bit0 key fallback, bit1 value
+ * fallback).  length == 0 gives a zero output. */
+void kvqo_attention(int B, int Hq, int Hkv, int64_t cap, int64_t length, const uint16_t *q, float sm,
+                    float tau_k, float tau_v, const uint16_t *k16, const uint16_t *v16,
+                    const int8_t *k_codes, const uint16_t *k_scales, const uint8_t *v_codes,
+                    const uint16_t *v_scales, const float *k_err, const float *v_err, double *out,
+                    uint8_t *mask)
+{
+    int G = Hq / Hkv;
+    int64_t nblk = (length + BLK - 1) / BLK;
+    uint8_t *m = mask ? mask : (uint8_t *)malloc((size_t)B * Hkv * (size_t)(nblk ? nblk : 1));
+    kvqo_bounds(B, Hq, Hkv, cap, length, q, sm, tau_k, tau_v, k_err, v_err, NULL, NULL, m);
+
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int b = 0; b < B; ++b)
+        for (int hq = 0; hq < Hq; ++hq) {
+            int h = hq / G;
+            double qv[D];
+            for (int j = 0; j < D; ++j)
+                qv[j] = kvqo_f16_to_f64(q[((size_t)b * Hq + hq) * D + j]);
+            double *o = out + ((size_t)b * Hq + hq) * D;
+            for (int j = 0; j < D; ++j)
+                o[j] = 0.0;
+            if (length == 0)
+                continue;
+            double *logit = (double *)malloc(sizeof(double) * (size_t)length);
+            double mx = -INFINITY;
+            for (int64_t t = 0; t < length; ++t) {
+                size_t r = row_index(b, h, t, Hkv, cap);
+                int fbk = m[((size_t)b * Hkv + h) * (size_t)nblk + (size_t)(t / BLK)] & 1;
+                double s = kvqo_f16_to_f64(k_scales[r]);
+                double acc = 0.0;
+                for (int j = 0; j < D; ++j) {
+                    double k = fbk ? kvqo_f16_to_f64(k16[r * D + j]) : s * (double)k_codes[r * D + j];
+                    acc += qv[j] * k;
+                }
+                logit[t] = (double)sm * acc;
+                if (logit[t] > mx)
+                    mx = logit[t];
+            }
+            double wsum = 0.0;
+            for (int64_t t = 0; t < length; ++t) {
+                size_t r = row_index(b, h, t, Hkv, cap);
+                int fbv = (m[((size_t)b * Hkv + h) * (size_t)nblk + (size_t)(t / BLK)] >> 1) & 1;
+                double w = exp(logit[t] - mx);
+                wsum += w;
+                for (int j = 0; j < D; ++j) {
+                    double v;
+                    if (fbv) {
+                        v = kvqo_f16_to_f64(v16[r * D + j]);
+                    } else {
+                        int high;
+                        size_t ob = v_byte(b, h, t, j, Hkv, cap, &high);
+                        int nib = high ? (v_codes[ob] >> 4) : (v_codes[ob] & 0x0F);
+                        int c = nib >= 8 ? nib - 16 : nib;
+                        v = kvqo_f16_to_f64(v_scales[r * (D / VG) + j / VG]) * (double)c;
+                    }
+                    o[j] += w * v;
+                }
+            }
+            for (int j = 0; j < D; ++j)
+                o[j] /= wsum;
+            free(logit);
+        }
+    if (!mask)
+        free(m);
+}
