@@ -1,0 +1,179 @@
+/*
+ * kvq.h -- C ABI of libkvq: certified quantized-KV decode attention on AMD
+ * MI355X (gfx950).
+ *
+ * Method: "Runtime-Certified Bounded-Error Quantized Attention" (Dean Calver;
+ * gist.science explainer of arXiv 2605.20868), technical summary:
+ *   Methodology 1 "Tiered Storage with Deterministic Fallback" -- a compressed
+ *     tier of INT8 keys and INT4 values with scales and per-block error
+ *     annotations, and a tier of FP16 originals used for fallback;
+ *   Methodology 2 "Two-Term Error Decomposition" -- a key term bounded through
+ *     the per-token score perturbation and a value term from per-block
+ *     reconstruction errors, both computed online from scales and query norms,
+ *     giving per-head, per-step precision decisions;
+ *   Key Contributions "Deterministic Recovery" -- blocks whose bound is not
+ *     certified are served from the FP16 originals.
+ *
+ * Codec and bounds implemented here (this library's reading of the page,
+ * which names INT8 keys, INT4 values, scales and per-block annotations but
+ * prints no formulas):
+ *   key codes   int8 per (token, KV head); fp16 scale s = f16(f32(max|x|)/127);
+ *               c = clamp(round_half_even(x/s), -127, 127); s = 0 -> c = 0.
+ *   value codes int4 per (token, KV head, 32-channel group); fp16 scale
+ *               s = f16(f32(max|x|)/7); c = clamp(round_half_even(x/s), -7, 7).
+ *   a key row or value group holding Inf/NaN gets codes 0, scale 0 and an
+ *   error of +Inf, so its block always falls back.
+ *   per-token key error  ||k - k^||_2 = f32(sqrt(T128(e_j^2))) in fp64, with
+ *   T128 the fixed pairwise tree (within 8 contiguous channels: strides 1, 2,
+ *   4; then across the 16 partial sums: channel strides 64, 32, 16, 8);
+ *   per-token value error max_j |v_j - v^_j| (exact).
+ *   block statistics k_err, v_err = max over the block's valid tokens.
+ *   query norm of head h: f32(sqrt(T128(q_j^2))); per (batch, KV head) the max
+ *   over its G = q_heads/kv_heads query heads (heads kvh*G .. kvh*G+G-1).
+ *   key bound   KB = ((sm*qn)*k_err)*(1+2^-16), fp32 products left to right:
+ *               an upper bound (Cauchy-Schwarz) on |sm * q.(k - k^)| for every
+ *               head of the group and token of the block, in logit units.
+ *   value bound VB = v_err.
+ *   fallback    mask bit 0 (key) = !(KB finite && KB <= tau_k);
+ *               mask bit 1 (value) = !(VB finite && VB <= tau_v).
+ *   attention   softmax(sm * q.k~) v~ over tokens t < length with, per block,
+ *               k~ = bit0 ? fp16 original : s*c and v~ = bit1 ? fp16 original
+ *               : s*c.  Output fp16.  length 0 gives a zero output.
+ *
+ * Memory layout (all device memory, caller-allocated, head-major so that each
+ * 64-token block of one (batch, KV head) is contiguous).  cap = capacity in
+ * tokens, a multiple of 64; NBc = cap/64.
+ *   k16, v16   uint16 (fp16 bits) [B][Hkv][cap][128]  FP16 originals (tier 2)
+ *   k_codes    int8               [B][Hkv][cap][128]
+ *   k_scales   uint16 (fp16)      [B][Hkv][cap]
+ *   v_codes    uint8              [B][Hkv][NBc][128][32]  per block, channel-
+ *              major: byte (j, i) holds token 2i of channel j in its low
+ *              nibble and token 2i+1 in its high nibble (two's complement).
+ *              Nibbles of tokens >= length inside a written block are 0.
+ *   v_scales   uint16 (fp16)      [B][Hkv][cap][4]
+ *   k_err, v_err float            [B][Hkv][NBc]
+ *   q          uint16 (fp16)      [B][Hq][128]
+ *   out        uint16 (fp16)      [B][Hq][128]
+ *   kb, vb     float, mask uint8  [B][Hkv][NB], NB = ceil(length/64)
+ *
+ * Streams: every entry point that touches the GPU takes a hipStream_t passed
+ * as void* (NULL = the null stream) and only enqueues work on it; nothing
+ * blocks the host.  Calls on one cache must be ordered by the caller (same
+ * stream or explicit events).  Argument errors are reported synchronously and
+ * enqueue nothing.  A failed launch returns KVQ_ERR_HIP; kvq_last_hip_error()
+ * then holds the hipError_t code (thread-local).  Faults during execution
+ * surface at the caller's next synchronisation.
+ *
+ * Preconditions checked by every entry point: head_dim == 128,
+ * block_tokens == 64, v_group == 32, batch >= 1, kv_heads >= 1,
+ * capacity % 64 == 0, 0 <= length <= capacity, q_heads % kv_heads == 0 with
+ * 1 <= q_heads/kv_heads <= 16, tolerances not NaN and >= 0, every device
+ * pointer 16-byte aligned (fp16/int8 arrays) or 4-byte aligned (float).
+ * The library never allocates memory and keeps no state besides the
+ * thread-local error code.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KVQ_OK = 0,
+    KVQ_ERR_INVALID_ARG = -1, /* null pointer, bad shape, NaN/negative tolerance */
+    KVQ_ERR_UNSUPPORTED = -2, /* head_dim/block/group other than 128/64/32, G > 16 */
+    KVQ_ERR_CAPACITY = -3,    /* length + n_new > capacity */
+    KVQ_ERR_ALIGNMENT = -4,   /* a device pointer is misaligned */
+    KVQ_ERR_WORKSPACE = -5,   /* workspace null or smaller than kvq_decode_workspace_bytes */
+    KVQ_ERR_HIP = -6          /* a HIP call failed; see kvq_last_hip_error() */
+} kvq_status;
+
+/* A quantized KV cache for one attention layer.  The struct is host memory;
+ * every pointer in it is device memory owned by the caller. */
+typedef struct kvq_cache {
+    int32_t batch;        /* B */
+    int32_t kv_heads;     /* Hkv */
+    int32_t head_dim;     /* must be 128 */
+    int32_t block_tokens; /* must be 64 */
+    int32_t v_group;      /* must be 32 */
+    int32_t reserved;     /* set to 0 */
+    int64_t capacity;     /* tokens per sequence, multiple of 64 */
+    int64_t length;       /* valid tokens per sequence (host-side) */
+    const uint16_t *k16;  /* FP16 originals, written by the caller */
+    const uint16_t *v16;
+    int8_t *k_codes;
+    uint16_t *k_scales;
+    uint8_t *v_codes;
+    uint16_t *v_scales;
+    float *k_err;
+    float *v_err;
+} kvq_cache;
+
+/* Byte sizes of the six tier-1 buffers, in the order k_codes, k_scales,
+ * v_codes, v_scales, k_err, v_err, for the shape fields of *c (pointers and
+ * length are ignored).  Host only. */
+kvq_status kvq_cache_bytes(const kvq_cache *c, size_t bytes_out[6]);
+
+/* Quantize-on-append (Methodology 1: tier-1 codes, scales and per-block error
+ * annotations derived from the FP16 originals).  Quantizes tokens
+ * [length, length + n_new) of every (batch, KV head) from k16/v16 into the
+ * tier-1 buffers, updates the statistics of every block those tokens touch
+ * (max with the block's earlier tokens), and on success advances c->length by
+ * n_new.  Blocks are written whole by one workgroup, so appends of any size
+ * and alignment give bit-identical buffers to one bulk append of the same
+ * tokens.  n_new == 0 is a no-op.  Errors: INVALID_ARG, UNSUPPORTED,
+ * CAPACITY, ALIGNMENT, HIP. */
+kvq_status kvq_quantize_append(kvq_cache *c, int64_t n_new, void *stream);
+
+/* Per-block bounds and fallback masks (Methodology 2: key and value terms
+ * from the block statistics and the query norms, no FP16 access).  For
+ * q [B][q_heads][128] writes, for every (batch, KV head, block < NB), the key
+ * bound KB, the value bound VB and the 2-bit fallback mask.  Each of kb, vb,
+ * mask may be NULL.  Errors: INVALID_ARG, UNSUPPORTED, ALIGNMENT, HIP. */
+kvq_status kvq_bounds(const kvq_cache *c, const uint16_t *q, int32_t q_heads, float sm_scale,
+                      float tau_k, float tau_v, float *kb, float *vb, uint8_t *mask, void *stream);
+
+/* Workspace size in bytes needed by kvq_decode_attn for this cache shape and
+ * query-head count (independent of length).  0 on invalid arguments. */
+size_t kvq_decode_workspace_bytes(const kvq_cache *c, int32_t q_heads);
+
+/* Certified decode attention (Methodology 1-3 on the decode step): one query
+ * token per sequence, q [B][q_heads][128] fp16 -> out [B][q_heads][128] fp16.
+ * Bounds and masks are evaluated inside the kernel from the block statistics
+ * (same arithmetic as kvq_bounds); fallback blocks read k16/v16, the others
+ * read the int8/int4 codes.  mask_out [B][Hkv][NB] receives the masks used
+ * (may be NULL).  workspace: device memory of at least
+ * kvq_decode_workspace_bytes() bytes, zero-filled before its first use; the
+ * library leaves it in a reusable state after every call, so it can be
+ * reused by later calls on the same stream.  Errors: INVALID_ARG,
+ * UNSUPPORTED, ALIGNMENT, WORKSPACE, HIP. */
+kvq_status kvq_decode_attn(const kvq_cache *c, const uint16_t *q, int32_t q_heads, float sm_scale,
+                           float tau_k, float tau_v, uint16_t *out, uint8_t *mask_out,
+                           void *workspace, size_t ws_bytes, void *stream);
+
+/* Decode kernel selection, for measurement.  kvq_decode_attn uses
+ * KVQ_KERNEL_AUTO; kvq_decode_attn_ex lets a benchmark force a variant and a
+ * split count (0 = automatic).  Same semantics and errors as
+ * kvq_decode_attn; a variant that does not support the group size returns
+ * KVQ_ERR_UNSUPPORTED. */
+typedef enum { KVQ_KERNEL_AUTO = 0, KVQ_KERNEL_VALU = 1, KVQ_KERNEL_MFMA = 2 } kvq_kernel;
+kvq_status kvq_decode_attn_ex(const kvq_cache *c, const uint16_t *q, int32_t q_heads,
+                              float sm_scale, float tau_k, float tau_v, uint16_t *out,
+                              uint8_t *mask_out, void *workspace, size_t ws_bytes, void *stream,
+                              int32_t kernel, int32_t splits);
+
+/* Human-readable name of a status code (static string). */
+const char *kvq_status_str(kvq_status s);
+
+/* hipError_t of the last failed HIP call on this thread (0 if none). */
+int kvq_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

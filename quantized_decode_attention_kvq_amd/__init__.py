@@ -1,0 +1,209 @@
+"""Python binding of libkvq (include/kvq.h): certified quantized-KV decode
+attention for AMD MI355X.
+
+Argument marshalling only: every step runs in the HIP kernels of libkvq.so.
+PyTorch provides device memory (tensors) and streams; nothing here computes
+on the data, and there is no CPU fallback: without the built library every
+call raises.
+
+Method: "Runtime-Certified Bounded-Error Quantized Attention", Methodology 1
+(INT8 keys / INT4 values with scales and per-block error annotations, FP16
+originals for fallback) and Methodology 2 (key and value error terms
+evaluated online per block from the statistics and the query norm).
+"""
+import ctypes
+import math
+import os
+
+import torch
+
+from . import build as _build
+
+D = 128
+BLK = 64
+VG = 32
+
+KVQ_OK = 0
+KERNEL_AUTO, KERNEL_VALU, KERNEL_MFMA = 0, 1, 2
+DEFAULT_SM_SCALE = float(torch.tensor(1.0 / math.sqrt(D), dtype=torch.float32))
+
+
+class KvqError(RuntimeError):
+    def __init__(self, fn, status, hip):
+        msg = f"{fn} failed: {lib().kvq_status_str(status).decode()} (status {status}"
+        if hip:
+            msg += f", hipError {hip}"
+        super().__init__(msg + ")")
+        self.status = status
+
+
+class _Cache(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("block_tokens", ctypes.c_int32), ("v_group", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("capacity", ctypes.c_int64), ("length", ctypes.c_int64),
+        ("k16", ctypes.c_void_p), ("v16", ctypes.c_void_p),
+        ("k_codes", ctypes.c_void_p), ("k_scales", ctypes.c_void_p),
+        ("v_codes", ctypes.c_void_p), ("v_scales", ctypes.c_void_p),
+        ("k_err", ctypes.c_void_p), ("v_err", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+EXPORTS = ("kvq_cache_bytes", "kvq_quantize_append", "kvq_bounds", "kvq_decode_workspace_bytes",
+           "kvq_decode_attn", "kvq_decode_attn_ex", "kvq_status_str", "kvq_last_hip_error")
+
+
+def lib_path():
+    return _build.LIB
+
+
+def lib():
+    """Load libkvq.so (building it in-tree first if it is absent)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        L = ctypes.CDLL(_build.LIB)
+        P, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+        CP = ctypes.POINTER(_Cache)
+        L.kvq_cache_bytes.argtypes = [CP, ctypes.POINTER(sz)]
+        L.kvq_cache_bytes.restype = ctypes.c_int
+        L.kvq_quantize_append.argtypes = [CP, i64, P]
+        L.kvq_quantize_append.restype = ctypes.c_int
+        L.kvq_bounds.argtypes = [CP, P, i32, f32, f32, f32, P, P, P, P]
+        L.kvq_bounds.restype = ctypes.c_int
+        L.kvq_decode_workspace_bytes.argtypes = [CP, i32]
+        L.kvq_decode_workspace_bytes.restype = sz
+        L.kvq_decode_attn.argtypes = [CP, P, i32, f32, f32, f32, P, P, P, sz, P]
+        L.kvq_decode_attn.restype = ctypes.c_int
+        L.kvq_decode_attn_ex.argtypes = [CP, P, i32, f32, f32, f32, P, P, P, sz, P, i32, i32]
+        L.kvq_decode_attn_ex.restype = ctypes.c_int
+        L.kvq_status_str.argtypes = [ctypes.c_int]
+        L.kvq_status_str.restype = ctypes.c_char_p
+        L.kvq_last_hip_error.argtypes = []
+        L.kvq_last_hip_error.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(fn, status):
+    if status != KVQ_OK:
+        raise KvqError(fn, status, lib().kvq_last_hip_error())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+class KVCache:
+    """One layer's KV cache: FP16 originals (tier 2) and the quantized tier 1,
+    as torch tensors on one device.  Shapes (head-major, per include/kvq.h):
+        k16, v16   fp16  [B][Hkv][cap][128]
+        k_codes    int8  [B][Hkv][cap][128]
+        k_scales   fp16  [B][Hkv][cap]
+        v_codes    uint8 [B][Hkv][cap/64][128][32]
+        v_scales   fp16  [B][Hkv][cap][4]
+        k_err, v_err float32 [B][Hkv][cap/64]
+    `length` is host-side and advanced by kvq_quantize_append."""
+
+    def __init__(self, batch, kv_heads, capacity, device="cuda", k16=None, v16=None):
+        if capacity % BLK:
+            raise ValueError("capacity must be a multiple of 64")
+        dev = torch.device(device)
+        if dev.type == "cuda" and dev.index is None:
+            dev = torch.device("cuda", torch.cuda.current_device())
+        shape = (batch, kv_heads, capacity, D)
+        self.batch, self.kv_heads, self.capacity, self.length = batch, kv_heads, capacity, 0
+        self.k16 = k16 if k16 is not None else torch.zeros(shape, dtype=torch.float16, device=dev)
+        self.v16 = v16 if v16 is not None else torch.zeros(shape, dtype=torch.float16, device=dev)
+        for t in (self.k16, self.v16):
+            if t.shape != shape or t.dtype != torch.float16 or not t.is_contiguous() or t.device != dev:
+                raise ValueError(f"tier-2 tensors must be contiguous fp16 {shape} on {dev}")
+        nbc = capacity // BLK
+        self.k_codes = torch.empty(shape, dtype=torch.int8, device=dev)
+        self.k_scales = torch.empty((batch, kv_heads, capacity), dtype=torch.float16, device=dev)
+        self.v_codes = torch.empty((batch, kv_heads, nbc, D, BLK // 2), dtype=torch.uint8, device=dev)
+        self.v_scales = torch.empty((batch, kv_heads, capacity, D // VG), dtype=torch.float16, device=dev)
+        self.k_err = torch.zeros((batch, kv_heads, nbc), dtype=torch.float32, device=dev)
+        self.v_err = torch.zeros((batch, kv_heads, nbc), dtype=torch.float32, device=dev)
+
+    @property
+    def nblocks(self):
+        return (self.length + BLK - 1) // BLK
+
+    def c_struct(self):
+        return _Cache(self.batch, self.kv_heads, D, BLK, VG, 0, self.capacity, self.length,
+                      self.k16.data_ptr(), self.v16.data_ptr(), self.k_codes.data_ptr(),
+                      self.k_scales.data_ptr(), self.v_codes.data_ptr(), self.v_scales.data_ptr(),
+                      self.k_err.data_ptr(), self.v_err.data_ptr())
+
+    def tier1_bytes(self):
+        out = (ctypes.c_size_t * 6)()
+        _check("kvq_cache_bytes", lib().kvq_cache_bytes(ctypes.byref(self.c_struct()), out))
+        return list(out)
+
+
+def kvq_quantize_append(cache: KVCache, n_new: int, stream=None):
+    """Quantize tokens [length, length+n_new) of cache.k16/v16 into tier 1 and
+    advance cache.length (asynchronous on `stream`)."""
+    c = cache.c_struct()
+    _check("kvq_quantize_append", lib().kvq_quantize_append(ctypes.byref(c), int(n_new), _stream(stream)))
+    cache.length = int(c.length)
+
+
+def _check_q(cache, q):
+    if q.dtype != torch.float16 or not q.is_contiguous() or q.dim() != 3 or q.shape[0] != cache.batch \
+            or q.shape[2] != D:
+        raise ValueError("q must be a contiguous fp16 tensor [B][Hq][128]")
+
+
+def kvq_bounds(cache: KVCache, q, sm_scale=DEFAULT_SM_SCALE, tau_k=0.0, tau_v=0.0, want=("kb", "vb", "mask"),
+               stream=None):
+    """Per-block key bound, value bound and fallback mask, each
+    [B][Hkv][nblocks] (float32, float32, uint8); entries not in `want` are None."""
+    _check_q(cache, q)
+    nb = cache.nblocks
+    dev = q.device
+    kb = torch.empty((cache.batch, cache.kv_heads, nb), dtype=torch.float32, device=dev) if "kb" in want else None
+    vb = torch.empty((cache.batch, cache.kv_heads, nb), dtype=torch.float32, device=dev) if "vb" in want else None
+    mask = torch.empty((cache.batch, cache.kv_heads, nb), dtype=torch.uint8, device=dev) if "mask" in want else None
+    c = cache.c_struct()
+    _check("kvq_bounds", lib().kvq_bounds(ctypes.byref(c), _ptr(q), q.shape[1], sm_scale, tau_k, tau_v,
+                                          _ptr(kb), _ptr(vb), _ptr(mask), _stream(stream)))
+    return kb, vb, mask
+
+
+def kvq_decode_workspace_bytes(cache: KVCache, q_heads: int) -> int:
+    return int(lib().kvq_decode_workspace_bytes(ctypes.byref(cache.c_struct()), int(q_heads)))
+
+
+def make_workspace(cache: KVCache, q_heads: int, device=None):
+    """A zero-filled workspace for kvq_decode_attn (reusable across calls)."""
+    n = kvq_decode_workspace_bytes(cache, q_heads)
+    if n == 0:
+        raise ValueError("invalid cache shape or q_heads")
+    return torch.zeros(n, dtype=torch.uint8, device=device or cache.k16.device)
+
+
+def kvq_decode_attn(cache: KVCache, q, sm_scale=DEFAULT_SM_SCALE, tau_k=0.0, tau_v=0.0, out=None,
+                    mask_out=None, workspace=None, stream=None, kernel=KERNEL_AUTO, splits=0):
+    """Certified decode attention: q [B][Hq][128] fp16 -> out [B][Hq][128] fp16.
+    mask_out (optional uint8 [B][Hkv][nblocks]) receives the fallback masks."""
+    _check_q(cache, q)
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        workspace = make_workspace(cache, q.shape[1], q.device)
+    c = cache.c_struct()
+    st = lib().kvq_decode_attn_ex(ctypes.byref(c), _ptr(q), q.shape[1], sm_scale, tau_k, tau_v, _ptr(out),
+                                  _ptr(mask_out), _ptr(workspace), workspace.numel(), _stream(stream),
+                                  int(kernel), int(splits))
+    _check("kvq_decode_attn", st)
+    return out

@@ -1,0 +1,271 @@
+// kvq_api.hip -- the C ABI of libkvq (see include/kvq.h): argument checks,
+// workspace sizing, split selection and kernel dispatch.  Host code only; no
+// allocation, no synchronisation.
+#include <math.h>
+#include <stdlib.h>
+
+#include "kvq.h"
+#include "kvq_internal.hpp"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+kvq_status hip_fail(hipError_t e) {
+    g_last_hip_error = (int)e;
+    return KVQ_ERR_HIP;
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+kvq_status check_shape(const kvq_cache *c) {
+    if (!c) return KVQ_ERR_INVALID_ARG;
+    if (c->head_dim != kvq::D || c->block_tokens != kvq::BLK || c->v_group != kvq::VG)
+        return KVQ_ERR_UNSUPPORTED;
+    if (c->batch < 1 || c->kv_heads < 1 || c->capacity < 0 || c->capacity % kvq::BLK != 0)
+        return KVQ_ERR_INVALID_ARG;
+    if (c->length < 0 || c->length > c->capacity) return KVQ_ERR_INVALID_ARG;
+    if (c->batch > 65535 || c->kv_heads > 65535) return KVQ_ERR_UNSUPPORTED;
+    return KVQ_OK;
+}
+
+kvq_status check_buffers(const kvq_cache *c, bool need_fp16) {
+    if (!c->k_codes || !c->k_scales || !c->v_codes || !c->v_scales || !c->k_err || !c->v_err)
+        return KVQ_ERR_INVALID_ARG;
+    if (need_fp16 && (!c->k16 || !c->v16)) return KVQ_ERR_INVALID_ARG;
+    if (!aligned(c->k_codes, 16) || !aligned(c->k_scales, 16) || !aligned(c->v_codes, 16) ||
+        !aligned(c->v_scales, 16) || !aligned(c->k_err, 4) || !aligned(c->v_err, 4) ||
+        !aligned(c->k16, 16) || !aligned(c->v16, 16))
+        return KVQ_ERR_ALIGNMENT;
+    return KVQ_OK;
+}
+
+kvq_status check_query(const kvq_cache *c, const uint16_t *q, int32_t q_heads, float sm,
+                       float tau_k, float tau_v) {
+    if (!q || q_heads < 1 || q_heads % c->kv_heads != 0) return KVQ_ERR_INVALID_ARG;
+    if (q_heads / c->kv_heads > 16) return KVQ_ERR_UNSUPPORTED;
+    if (!isfinite(sm) || isnan(tau_k) || isnan(tau_v) || tau_k < 0.0f || tau_v < 0.0f)
+        return KVQ_ERR_INVALID_ARG;
+    if (!aligned(q, 16)) return KVQ_ERR_ALIGNMENT;
+    return KVQ_OK;
+}
+
+kvq::CachePtrs ptrs(const kvq_cache *c) {
+    return kvq::CachePtrs{c->k16, c->v16, c->k_codes, c->k_scales, c->v_codes, c->v_scales, c->k_err,
+                          c->v_err};
+}
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Workspace layout: [counters u32 x B*Hkv, padded to 256 B]
+//                   [part_ml float2 x B*Hkv*S*G] [part_acc float x B*Hkv*S*G*128]
+struct WsLayout {
+    size_t counters, ml, acc, total;
+};
+
+WsLayout ws_layout(const kvq_cache *c, int32_t g, int64_t splits) {
+    const size_t bh = (size_t)c->batch * (size_t)c->kv_heads;
+    WsLayout w;
+    w.counters = 0;
+    w.ml = round_up(bh * sizeof(uint32_t), 256);
+    w.acc = w.ml + round_up(bh * (size_t)splits * (size_t)g * sizeof(float2), 256);
+    w.total = w.acc + bh * (size_t)splits * (size_t)g * kvq::D * sizeof(float);
+    return w;
+}
+
+int64_t max_splits(const kvq_cache *c) {
+    const int64_t nbc = c->capacity / kvq::BLK;
+    int64_t s = nbc < kvq::MAX_SPLITS ? nbc : kvq::MAX_SPLITS;
+    return s < 1 ? 1 : s;
+}
+
+int device_cus() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cached[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+// Splits: enough workgroups to give every CU several waves in flight, never
+// more splits than blocks, never more blocks per split than the LDS mask
+// table holds.
+int64_t choose_splits(const kvq_cache *c, int64_t nb, int32_t requested) {
+    const int64_t bh = (int64_t)c->batch * c->kv_heads;
+    const int64_t smax = max_splits(c);
+    int64_t s;
+    if (requested > 0) {
+        s = requested;
+    } else if (const char *env = getenv("KVQ_SPLITS")) {
+        s = atoll(env);
+    } else {
+        const int64_t target_wgs = 4LL * device_cus();
+        s = (target_wgs + bh - 1) / bh;
+    }
+    if (s > nb) s = nb;
+    const int64_t need = (nb + kvq::MAX_BPS - 1) / kvq::MAX_BPS;
+    if (s < need) s = need;
+    if (s > smax) s = smax;
+    if (s < 1) s = 1;
+    return s;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *kvq_status_str(kvq_status s) {
+    switch (s) {
+        case KVQ_OK: return "ok";
+        case KVQ_ERR_INVALID_ARG: return "invalid argument";
+        case KVQ_ERR_UNSUPPORTED: return "unsupported shape";
+        case KVQ_ERR_CAPACITY: return "capacity exceeded";
+        case KVQ_ERR_ALIGNMENT: return "misaligned pointer";
+        case KVQ_ERR_WORKSPACE: return "workspace missing or too small";
+        case KVQ_ERR_HIP: return "HIP error";
+    }
+    return "unknown status";
+}
+
+int kvq_last_hip_error(void) { return g_last_hip_error; }
+
+kvq_status kvq_cache_bytes(const kvq_cache *c, size_t bytes_out[6]) {
+    kvq_status st = check_shape(c);
+    if (st != KVQ_OK) return st;
+    if (!bytes_out) return KVQ_ERR_INVALID_ARG;
+    const size_t rows = (size_t)c->batch * c->kv_heads * (size_t)c->capacity;
+    const size_t blocks = rows / kvq::BLK;
+    bytes_out[0] = rows * kvq::D;                // k_codes
+    bytes_out[1] = rows * sizeof(uint16_t);      // k_scales
+    bytes_out[2] = rows * kvq::D / 2;            // v_codes
+    bytes_out[3] = rows * 4 * sizeof(uint16_t);  // v_scales
+    bytes_out[4] = blocks * sizeof(float);       // k_err
+    bytes_out[5] = blocks * sizeof(float);       // v_err
+    return KVQ_OK;
+}
+
+kvq_status kvq_quantize_append(kvq_cache *c, int64_t n_new, void *stream) {
+    kvq_status st = check_shape(c);
+    if (st != KVQ_OK) return st;
+    if (n_new < 0) return KVQ_ERR_INVALID_ARG;
+    if (n_new > c->capacity - c->length) return KVQ_ERR_CAPACITY;
+    if ((st = check_buffers(c, true)) != KVQ_OK) return st;
+    if (n_new == 0) return KVQ_OK;
+    kvq::AppendArgs a;
+    a.c = ptrs(c);
+    a.cap = c->capacity;
+    a.len0 = c->length;
+    a.len1 = c->length + n_new;
+    a.blk_lo = a.len0 / kvq::BLK;
+    a.hkv = c->kv_heads;
+    const int64_t nblk = (a.len1 - 1) / kvq::BLK - a.blk_lo + 1;
+    if (nblk > 0x7FFFFFFF) return KVQ_ERR_UNSUPPORTED;
+    hipError_t e = kvq::launch_append(a, c->batch, nblk, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e);
+    c->length = a.len1;
+    return KVQ_OK;
+}
+
+kvq_status kvq_bounds(const kvq_cache *c, const uint16_t *q, int32_t q_heads, float sm_scale,
+                      float tau_k, float tau_v, float *kb, float *vb, uint8_t *mask, void *stream) {
+    kvq_status st = check_shape(c);
+    if (st != KVQ_OK) return st;
+    if ((st = check_query(c, q, q_heads, sm_scale, tau_k, tau_v)) != KVQ_OK) return st;
+    if (!c->k_err || !c->v_err) return KVQ_ERR_INVALID_ARG;
+    if (!aligned(c->k_err, 4) || !aligned(c->v_err, 4) || !aligned(kb, 4) || !aligned(vb, 4))
+        return KVQ_ERR_ALIGNMENT;
+    const int64_t nb = (c->length + kvq::BLK - 1) / kvq::BLK;
+    if (nb == 0) return KVQ_OK;
+    kvq::BoundsArgs a;
+    a.k_err = c->k_err;
+    a.v_err = c->v_err;
+    a.q = q;
+    a.kb = kb;
+    a.vb = vb;
+    a.mask = mask;
+    a.nbc = c->capacity / kvq::BLK;
+    a.nb = nb;
+    a.hkv = c->kv_heads;
+    a.hq = q_heads;
+    a.g = q_heads / c->kv_heads;
+    a.sm = sm_scale;
+    a.tau_k = tau_k;
+    a.tau_v = tau_v;
+    hipError_t e = kvq::launch_bounds(a, c->batch, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e);
+    return KVQ_OK;
+}
+
+size_t kvq_decode_workspace_bytes(const kvq_cache *c, int32_t q_heads) {
+    if (check_shape(c) != KVQ_OK || q_heads < 1 || q_heads % c->kv_heads != 0 ||
+        q_heads / c->kv_heads > 16)
+        return 0;
+    return ws_layout(c, q_heads / c->kv_heads, max_splits(c)).total;
+}
+
+kvq_status kvq_decode_attn_ex(const kvq_cache *c, const uint16_t *q, int32_t q_heads,
+                              float sm_scale, float tau_k, float tau_v, uint16_t *out,
+                              uint8_t *mask_out, void *workspace, size_t ws_bytes, void *stream,
+                              int32_t kernel, int32_t splits) {
+    kvq_status st = check_shape(c);
+    if (st != KVQ_OK) return st;
+    if ((st = check_query(c, q, q_heads, sm_scale, tau_k, tau_v)) != KVQ_OK) return st;
+    if ((st = check_buffers(c, true)) != KVQ_OK) return st;
+    if (!out) return KVQ_ERR_INVALID_ARG;
+    if (!aligned(out, 16)) return KVQ_ERR_ALIGNMENT;
+    if (kernel < KVQ_KERNEL_AUTO || kernel > KVQ_KERNEL_MFMA || splits < 0) return KVQ_ERR_INVALID_ARG;
+    const int32_t g = q_heads / c->kv_heads;
+    if (!workspace || ws_bytes < kvq_decode_workspace_bytes(c, q_heads)) return KVQ_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return KVQ_ERR_ALIGNMENT;
+
+    const int64_t nb = (c->length + kvq::BLK - 1) / kvq::BLK;
+    const int64_t nbc = c->capacity / kvq::BLK;
+    if (nb > (int64_t)kvq::MAX_BPS * kvq::MAX_SPLITS) return KVQ_ERR_UNSUPPORTED;
+    const int64_t s = nb > 0 ? choose_splits(c, nb, splits) : 1;
+    const int64_t bps = nb > 0 ? (nb + s - 1) / s : 1;
+    const int64_t s_eff = nb > 0 ? (nb + bps - 1) / bps : 1;
+
+    const WsLayout w = ws_layout(c, g, s_eff);
+    kvq::DecodeArgs a;
+    a.c = ptrs(c);
+    a.q = q;
+    a.out = out;
+    a.mask_out = mask_out;
+    a.counters = reinterpret_cast<uint32_t *>((char *)workspace + w.counters);
+    a.part_ml = reinterpret_cast<float2 *>((char *)workspace + w.ml);
+    a.part_acc = reinterpret_cast<float *>((char *)workspace + w.acc);
+    a.cap = c->capacity;
+    a.length = c->length;
+    a.nbc = nbc;
+    a.nb = nb;
+    a.hkv = c->kv_heads;
+    a.hq = q_heads;
+    a.g = g;
+    a.splits = (int32_t)s_eff;
+    a.bps = (int32_t)bps;
+    a.sm = sm_scale;
+    a.tau_k = tau_k;
+    a.tau_v = tau_v;
+
+    int32_t k = kernel;
+    if (k == KVQ_KERNEL_AUTO) k = kvq::mfma_supports(g) ? KVQ_KERNEL_MFMA : KVQ_KERNEL_VALU;
+    if (k == KVQ_KERNEL_MFMA && !kvq::mfma_supports(g)) return KVQ_ERR_UNSUPPORTED;
+    hipError_t e = (k == KVQ_KERNEL_MFMA) ? kvq::launch_decode_mfma(a, c->batch, (hipStream_t)stream)
+                                          : kvq::launch_decode_valu(a, c->batch, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e);
+    return KVQ_OK;
+}
+
+kvq_status kvq_decode_attn(const kvq_cache *c, const uint16_t *q, int32_t q_heads, float sm_scale,
+                           float tau_k, float tau_v, uint16_t *out, uint8_t *mask_out,
+                           void *workspace, size_t ws_bytes, void *stream) {
+    return kvq_decode_attn_ex(c, q, q_heads, sm_scale, tau_k, tau_v, out, mask_out, workspace,
+                              ws_bytes, stream, KVQ_KERNEL_AUTO, 0);
+}
+
+}  // extern "C"

@@ -1,0 +1,67 @@
+// kvq_internal.hpp -- launch arguments and launcher declarations shared by the
+// libkvq host code and its kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvq {
+
+constexpr int D = 128;   // head dim
+constexpr int BLK = 64;  // tokens per block
+constexpr int VG = 32;   // channels per value group
+
+struct CachePtrs {
+    const uint16_t *k16, *v16;
+    int8_t *k_codes;
+    uint16_t *k_scales;
+    uint8_t *v_codes;
+    uint16_t *v_scales;
+    float *k_err, *v_err;
+};
+
+struct AppendArgs {
+    CachePtrs c;
+    int64_t cap;     // tokens per sequence
+    int64_t len0;    // first new token
+    int64_t len1;    // one past the last new token
+    int64_t blk_lo;  // first block touched (len0 / 64)
+    int32_t hkv;
+};
+
+struct BoundsArgs {
+    const float *k_err, *v_err;
+    const uint16_t *q;
+    float *kb, *vb;
+    uint8_t *mask;
+    int64_t nbc;  // blocks of capacity (stride of k_err/v_err)
+    int64_t nb;   // blocks holding valid tokens (stride of kb/vb/mask)
+    int32_t hkv, hq, g;
+    float sm, tau_k, tau_v;
+};
+
+struct DecodeArgs {
+    CachePtrs c;
+    const uint16_t *q;
+    uint16_t *out;
+    uint8_t *mask_out;
+    uint32_t *counters;  // [B*Hkv], zero between calls
+    float2 *part_ml;     // [B*Hkv][S][G] (running max, running sum)
+    float *part_acc;     // [B*Hkv][S][G][128] unnormalised
+    int64_t cap, length, nbc, nb;
+    int32_t hkv, hq, g;
+    int32_t splits, bps;  // number of splits and blocks per split
+    float sm, tau_k, tau_v;
+};
+
+// Upper limits that size the workspace and LDS tables.
+constexpr int MAX_SPLITS = 128;
+constexpr int MAX_BPS = 4096;  // blocks per split (mask table in LDS)
+
+hipError_t launch_append(const AppendArgs &a, int batch, int64_t nblk, hipStream_t s);
+hipError_t launch_bounds(const BoundsArgs &a, int batch, hipStream_t s);
+hipError_t launch_decode_valu(const DecodeArgs &a, int batch, hipStream_t s);
+hipError_t launch_decode_mfma(const DecodeArgs &a, int batch, hipStream_t s);
+bool mfma_supports(int g);
+
+}  // namespace kvq

@@ -1,0 +1,186 @@
+// kvq_quantize.hip -- quantize-on-append for the tier-1 cache (gfx950).
+//
+// "Runtime-Certified Bounded-Error Quantized Attention", Methodology 1: the
+// compressed tier holds INT8 keys and INT4 values with their scales and
+// per-block error annotations, derived from the FP16 originals kept in tier 2.
+//
+// One workgroup (256 threads = 4 waves) owns one 64-token block of one
+// (batch, KV head), so a block's codes and statistics have a single writer and
+// appends of any size compose bit-exactly.  Each token row (128 fp16 = 256 B)
+// is handled by 16 lanes that each load 16 B (8 channels); a wave covers 4
+// rows per pass, the workgroup 16.  Reductions inside a row are xor-shuffles
+// within the 16-lane group: absmax over 16 lanes for the key scale, over 4
+// lanes for a 32-channel value group, and the fixed fp64 tree for ||k - k^||.
+// Value nibbles are staged as bytes in LDS and packed channel-major on the way
+// out; key codes go straight from registers to HBM (128 B per row, coalesced).
+#include "kvq_device.hpp"
+#include "kvq_internal.hpp"
+
+namespace kvq {
+
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+
+// Max of |x| over the 8 fp16 values of a lane, as a bit pattern (for
+// non-negative fp16 the bit pattern orders like the value; Inf and NaN sort
+// above every finite value).
+__device__ __forceinline__ uint32_t absmax_bits(const uint32_t w[4]) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m = umax(m, umax(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
+    return m;
+}
+
+__device__ __forceinline__ float elem(const uint32_t w[4], int k) {
+    return h2f((k & 1) ? (w[k >> 1] >> 16) : (w[k >> 1] & 0xFFFFu));
+}
+
+// round_half_even(x / s) clamped to [-lim, lim]; s > 0.  IEEE binary32
+// division (correctly rounded) followed by rint: the quotient of two fp16
+// values cannot be moved across a half-integer by that rounding.
+__device__ __forceinline__ int quant_code(float x, float s, int lim) {
+    int c = (int)__builtin_rintf(__fdiv_rn(x, s));
+    return c < -lim ? -lim : (c > lim ? lim : c);
+}
+
+__global__ __launch_bounds__(256) void quantize_append_kernel(AppendArgs a) {
+    __shared__ __attribute__((aligned(16))) uint8_t vtile[BLK][D];  // new value codes (low nibble), [token][channel]
+    __shared__ float red[2][4];
+
+    const int tid = threadIdx.x;
+    const int lane16 = tid & 15;
+    const int row0 = tid >> 4;  // 0..15
+    const int64_t blk = a.blk_lo + blockIdx.x;
+    const int64_t head = (int64_t)blockIdx.z * a.hkv + blockIdx.y;
+    const int64_t t_first = blk * BLK;
+    const int64_t t_begin = a.len0 > t_first ? a.len0 : t_first;
+    const int64_t t_end = a.len1 < t_first + BLK ? a.len1 : t_first + BLK;
+    const int64_t row_base = head * a.cap;
+
+    float kmax = 0.0f, vmax = 0.0f;
+
+    for (int r = row0; r < BLK; r += 16) {
+        const int64_t t = t_first + r;
+        const bool valid = t >= t_begin && t < t_end;  // uniform in the 16-lane group
+        const int64_t roff = (row_base + t) * D + 8 * lane16;
+
+        // ---------------- key row: int8 per token, scale absmax/127
+        const uint4 kr = *reinterpret_cast<const uint4 *>(a.c.k16 + roff);
+        const uint32_t kw[4] = {kr.x, kr.y, kr.z, kr.w};
+        uint32_t am = absmax_bits(kw);
+        am = umax(am, __shfl_xor(am, 1));
+        am = umax(am, __shfl_xor(am, 2));
+        am = umax(am, __shfl_xor(am, 4));
+        am = umax(am, __shfl_xor(am, 8));
+        const bool knonfin = am >= 0x7C00u;
+        const uint32_t ksb = knonfin ? 0u : f2h_rn(__fdiv_rn(h2f(am), 127.0f));
+        const float ks = h2f(ksb);
+        uint32_t kc[2] = {0u, 0u};
+        double sq[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const float x = elem(kw, k);
+            const int c = (ks != 0.0f) ? quant_code(x, ks, 127) : 0;
+            const float e = __fsub_rn(x, __fmul_rn(ks, (float)c));  // exact
+            sq[k] = sq64(e);
+            kc[k >> 2] |= ((uint32_t)c & 0xFFu) << (8 * (k & 3));
+        }
+        const double ss = tree128(sq);
+        const float kerr = knonfin ? __builtin_huge_valf() : (float)__dsqrt_rn(ss);
+
+        // ---------------- value row: int4 per 32-channel group, scale absmax/7
+        const uint4 vr = *reinterpret_cast<const uint4 *>(a.c.v16 + roff);
+        const uint32_t vw[4] = {vr.x, vr.y, vr.z, vr.w};
+        uint32_t vm = absmax_bits(vw);
+        vm = umax(vm, __shfl_xor(vm, 1));
+        vm = umax(vm, __shfl_xor(vm, 2));
+        const bool vnonfin = vm >= 0x7C00u;
+        const uint32_t vsb = vnonfin ? 0u : f2h_rn(__fdiv_rn(h2f(vm), 7.0f));
+        const float vs = h2f(vsb);
+        uint32_t vc[2] = {0u, 0u};
+        float verr = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const float x = elem(vw, k);
+            const int c = (vs != 0.0f) ? quant_code(x, vs, 7) : 0;
+            const float e = __builtin_fabsf(__fsub_rn(x, __fmul_rn(vs, (float)c)));  // exact
+            verr = verr > e ? verr : e;
+            vc[k >> 2] |= ((uint32_t)c & 0x0Fu) << (8 * (k & 3));
+        }
+        verr = vnonfin ? __builtin_huge_valf() : verr;
+        verr = fmaxf(verr, __shfl_xor(verr, 1));
+        verr = fmaxf(verr, __shfl_xor(verr, 2));
+        verr = fmaxf(verr, __shfl_xor(verr, 4));  // row: max over the 4 groups
+        verr = fmaxf(verr, __shfl_xor(verr, 8));
+
+        if (valid) {
+            *reinterpret_cast<uint2 *>(a.c.k_codes + roff) = make_uint2(kc[0], kc[1]);
+            if (lane16 == 0) a.c.k_scales[row_base + t] = (uint16_t)ksb;
+            if ((lane16 & 3) == 0) a.c.v_scales[(row_base + t) * 4 + (lane16 >> 2)] = (uint16_t)vsb;
+            *reinterpret_cast<uint2 *>(&vtile[r][8 * lane16]) = make_uint2(vc[0], vc[1]);
+            kmax = fmaxf(kmax, kerr);
+            vmax = fmaxf(vmax, verr);
+        }
+    }
+
+    // block statistics: max over this workgroup's rows, then over old rows
+    kmax = fmaxf(kmax, __shfl_xor(kmax, 16));
+    kmax = fmaxf(kmax, __shfl_xor(kmax, 32));
+    vmax = fmaxf(vmax, __shfl_xor(vmax, 16));
+    vmax = fmaxf(vmax, __shfl_xor(vmax, 32));
+    if ((tid & 63) == 0) {
+        red[0][tid >> 6] = kmax;
+        red[1][tid >> 6] = vmax;
+    }
+    __syncthreads();
+
+    const bool has_old = t_first < a.len0;
+    if (tid == 0) {
+        float km = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
+        float vm2 = fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3]));
+        const int64_t si = head * (a.cap / BLK) + blk;
+        if (has_old) {
+            km = fmaxf(km, a.c.k_err[si]);
+            vm2 = fmaxf(vm2, a.c.v_err[si]);
+        }
+        a.c.k_err[si] = km;
+        a.c.v_err[si] = vm2;
+    }
+
+    // value codes: channel-major nibble pairs, 16 bytes per thread
+    {
+        const int j = tid >> 1;         // channel
+        const int i0 = (tid & 1) * 16;  // first byte (token pair) of this thread
+        uint8_t *dst = a.c.v_codes + (head * (a.cap / BLK) + blk) * (D * BLK / 2) + j * (BLK / 2) + i0;
+        uint4 old = make_uint4(0, 0, 0, 0);
+        if (has_old) old = *reinterpret_cast<const uint4 *>(dst);
+        const uint32_t ow[4] = {old.x, old.y, old.z, old.w};
+        uint32_t nw[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            uint32_t byte = 0;
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int tk = 2 * (i0 + i) + half;
+                const int64_t t = t_first + tk;
+                uint32_t nib;
+                if (t < a.len0)
+                    nib = (ow[i >> 2] >> (8 * (i & 3) + 4 * half)) & 0x0Fu;
+                else if (t < a.len1)
+                    nib = vtile[tk][j] & 0x0Fu;
+                else
+                    nib = 0u;
+                byte |= nib << (4 * half);
+            }
+            nw[i >> 2] |= byte << (8 * (i & 3));
+        }
+        *reinterpret_cast<uint4 *>(dst) = make_uint4(nw[0], nw[1], nw[2], nw[3]);
+    }
+}
+
+hipError_t launch_append(const AppendArgs &a, int batch, int64_t nblk, hipStream_t s) {
+    dim3 grid((unsigned)nblk, (unsigned)a.hkv, (unsigned)batch);
+    hipLaunchKernelGGL(quantize_append_kernel, grid, dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace kvq
