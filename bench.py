@@ -1,0 +1,267 @@
+"""Benchmark of the certified quantized-KV decode step on one MI355X.
+
+One step = one decode step of one attention layer for the whole batch:
+kvq_quantize_append of the new token of every sequence (quantize-on-append),
+then kvq_decode_attn (bounds, fallback masks, split-K streaming attention and
+the cross-split merge, fused in one kernel).  Inputs are resident in HBM when
+the timed region starts.  Several layers' caches ("replicas") are cycled so
+that consecutive steps never find their KV stream in the 256 MB Infinity
+Cache, as in a real multi-layer decode.
+
+Prints one JSON line:
+  value      effective KV bandwidth of the step: algorithmic bytes / step time
+             (GB/s, 1e9 B/s); tokens_per_s and pct_of_hbm_peak beside it.
+  roofline   for the dominant kernel (the decode kernel): its algorithmic
+             bytes per launch / its mean launch time from HIP events on its
+             stream, against the 8 TB/s HBM3E peak.
+  cpu_baseline  the CPU oracle (fp64, OpenMP) timed on a bounded sample of
+             the same workload, same byte accounting.
+
+Algorithmic bytes per decode, per (batch, KV head, 64-token block):
+  8 (k_err, v_err) + key tile (8192 codes + 128 scale bytes, or 16384 fp16
+  bytes on key fallback) + value tile (4096 nibble bytes + 512 scale bytes,
+  or 16384 fp16 bytes on value fallback); plus q and out (256 B per head
+  each).  Per append: the new token's fp16 K and V rows (512 B) read, its
+  codes, scales and block statistics (210 B) written, per (batch, KV head).
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "decode_counters.json")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="llama3_8b_32k")
+    p.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma"])
+    p.add_argument("--splits", type=int, default=0)
+    p.add_argument("--replicas", type=int, default=0, help="layer caches cycled (0: enough for >= 2 GB)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU work of the oracle sample")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="also run one 1 GiB device copy (reference kernel for HBM counters)")
+    return p.parse_args()
+
+
+def kernel_source_hash():
+    import quantized_decode_attention_kvq_amd.build as b
+    h = hashlib.sha256()
+    for f in sorted(b.sources()):
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def decode_bytes(mask, B, Hq):
+    """Algorithmic bytes of one decode over blocks with fallback mask `mask`."""
+    import numpy as np
+    m = np.asarray(mask)
+    fk = (m & 1).astype(np.int64)
+    fv = ((m >> 1) & 1).astype(np.int64)
+    per_unit = 8 + np.where(fk, 16384, 8320) + np.where(fv, 16384, 4608)
+    return int(per_unit.sum()) + 2 * B * Hq * 256
+
+
+def append_bytes(B, Hkv, n=1):
+    return B * Hkv * n * (512 + 128 + 2 + 64 + 8 + 8)
+
+
+def traffic_from_counters(launches_per_step_kernel):
+    """HBM bytes per decode launch from committed rocprofv3 counter runs, or
+    None when they are absent or were taken on different kernel sources."""
+    if not os.path.exists(PROFILE_COUNTERS):
+        return None
+    try:
+        c = json.load(open(PROFILE_COUNTERS))
+        if c.get("kernel_source_hash") != kernel_source_hash():
+            return None
+        return float(c["hbm_bytes_per_launch"])
+    except Exception:
+        return None
+
+
+def cpu_baseline(w, d, tau_k, tau_v, sm, target_s):
+    """The oracle (as it stands) on a bounded sample: whole-context decode for
+    a subset of (batch, KV head) groups, timed on the host cores."""
+    import numpy as np
+
+    import oracle
+
+    k16 = d["k16"].cpu().numpy()
+    v16 = d["v16"].cpu().numpy()
+    q = d["q"].cpu().numpy()
+    groups = [(b, h) for b in range(w.B) for h in range(w.Hkv)]
+
+    def sample(n):
+        idx = groups[:n]
+        ks = np.stack([k16[b, h] for b, h in idx])[:, None]
+        vs = np.stack([v16[b, h] for b, h in idx])[:, None]
+        qs = np.stack([q[b, h * w.G:(h + 1) * w.G] for b, h in idx])
+        oc = oracle.Cache(ks, vs, w.T)  # the quantized cache (setup, untimed)
+        t0 = time.perf_counter()
+        _, mask = oc.attention(qs, sm, tau_k, tau_v)
+        dt = time.perf_counter() - t0
+        return dt, mask
+
+    dt1, _ = sample(1)
+    n = int(max(1, min(len(groups), target_s / max(dt1, 1e-3))))
+    dt, mask = sample(n)
+    nbytes = decode_bytes(mask, n, w.G)
+    return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": f"fp64 decode of {n} of {len(groups)} (batch, KV head) groups at T={w.T} "
+                      f"({n * w.G} query heads), {dt:.2f} s; same byte accounting as the GPU line",
+            "tokens_per_s_equiv": round(n / len(groups) * w.B / dt, 3)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "multi-GPU runs are not part of it (the decode path would shard over "
+              "(batch, KV head) groups with no communication)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import quantized_decode_attention_kvq_amd as kvq
+    import workloads
+
+    torch.cuda.set_device(0)
+    w = workloads.WORKLOADS[args.workload]
+    if w.name == "bulk_quantize":
+        sys.exit("bench.py: use --workload with a decode workload (bulk_quantize is a parity case)")
+    dev = "cuda"
+    sm = kvq.DEFAULT_SM_SCALE
+    kernel = {"auto": kvq.KERNEL_AUTO, "valu": kvq.KERNEL_VALU, "mfma": kvq.KERNEL_MFMA}[args.kernel]
+
+    d = workloads.make(w, dev)
+    # layer caches: same data, distinct HBM allocations
+    tier2 = 2 * d["k16"].numel() * 2
+    tier1 = tier2 * 0.395
+    R = args.replicas or int(max(2, np.ceil(2e9 / tier1)))
+    caches = []
+    for r in range(R):
+        k16 = d["k16"] if r == 0 else d["k16"].clone()
+        v16 = d["v16"] if r == 0 else d["v16"].clone()
+        c = kvq.KVCache(w.B, w.Hkv, w.cap, device=dev, k16=k16, v16=v16)
+        kvq.kvq_quantize_append(c, w.T - 1)  # prefill; the step appends token T-1
+        caches.append(c)
+    q = d["q"].contiguous()
+
+    # tolerances: ~fallback_frac of the blocks per bound, from the library's own bounds
+    c0 = caches[0]
+    kvq.kvq_quantize_append(c0, 1)
+    kb, vb, _ = kvq.kvq_bounds(c0, q, sm, 0.0, 0.0, want=("kb", "vb"))
+    kbn, vbn = kb.flatten().float().cpu().numpy(), vb.flatten().float().cpu().numpy()
+
+    def tau(vals, frac):
+        v = np.sort(vals[np.isfinite(vals)])
+        k = max(1, int(round(frac * v.size)))
+        return float(np.float32((v[v.size - k - 1] + v[v.size - k]) / 2))
+
+    tau_k, tau_v = tau(kbn, w.fallback_frac), tau(vbn, w.fallback_frac)
+    c0.length = w.T - 1
+
+    out = torch.empty_like(q)
+    mask = torch.empty((w.B, w.Hkv, (w.T + 63) // 64), dtype=torch.uint8, device=dev)
+    ws = [kvq.make_workspace(c, w.Hq) for c in caches]
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        c = caches[i % R]
+        c.length = w.T - 1
+        kvq.kvq_quantize_append(c, 1, stream)
+        if ev is not None:
+            ev[0].record(stream)
+        kvq.kvq_decode_attn(c, q, sm, tau_k, tau_v, out=out, mask_out=mask if i == 0 else None,
+                            workspace=ws[i % R], stream=stream, kernel=kernel, splits=args.splits)
+        if ev is not None:
+            ev[1].record(stream)
+
+    step(0)
+    torch.cuda.synchronize()
+    m = mask.cpu().numpy()
+    dec_bytes = decode_bytes(m, w.B, w.Hq)
+    step_bytes = dec_bytes + append_bytes(w.B, w.Hkv)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    ms_step = dt / args.steps * 1e3
+    dec_ms = [a.elapsed_time(b) for a, b in evs]
+    dec_ms_mean = float(np.mean(dec_ms))
+
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    gbs = step_bytes / (ms_step * 1e-3) / 1e9
+    dec_gbs = dec_bytes / (dec_ms_mean * 1e-3) / 1e9
+    traffic = traffic_from_counters(1)
+    line = {
+        "metric": "quantized-KV decode attention: effective KV GB/s (% of HBM peak), tokens/s",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "tokens_per_s": round(w.B / (ms_step * 1e-3), 1),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8 K / int4 V codes, fp16 q and fallback tiles, fp32 accumulate",
+        "data": "synthetic (seeded normal fp16 K/V/q with per-head K outlier channels)",
+        "config": {
+            "workload": f"{w.name}: B{w.B} Hq{w.Hq} Hkv{w.Hkv} D128 T{w.T}, one decode step "
+                        "(append 1 token + certified attention) of one layer",
+            "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "context": w.T,
+            "fallback_blocks_key": round(float((m & 1).mean()), 5),
+            "fallback_blocks_value": round(float(((m >> 1) & 1).mean()), 5),
+            "tau_k": tau_k, "tau_v": tau_v, "layers_cycled": R,
+            "kernel": args.kernel, "splits": args.splits,
+            "bytes_per_step": step_bytes,
+        },
+        "roofline": {
+            "kernel": "kvq decode (split-K, fused bounds + merge)",
+            "bound": "hbm",
+            "achieved": round(dec_gbs, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": dec_bytes,
+            "mean_launch_ms": round(dec_ms_mean, 5),
+        },
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, d, tau_k, tau_v, sm, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

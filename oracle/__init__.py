@@ -33,6 +33,8 @@ def lib():
         L = ctypes.CDLL(_build.LIB)
         P = ctypes.c_void_p
         i32, i64, f32 = ctypes.c_int, ctypes.c_int64, ctypes.c_float
+        L.kvqo_max_threads.argtypes = []
+        L.kvqo_max_threads.restype = ctypes.c_int
         L.kvqo_f16_to_f64.argtypes = [ctypes.c_uint16]
         L.kvqo_f16_to_f64.restype = ctypes.c_double
         L.kvqo_f32_to_f16.argtypes = [f32]
@@ -71,6 +73,10 @@ def _c(a, dtype):
 
 
 # ----------------------------------------------------------------- scalars
+
+def max_threads() -> int:
+    return int(lib().kvqo_max_threads())
+
 
 def f16_bits_to_f64(bits: int) -> float:
     return lib().kvqo_f16_to_f64(int(bits) & 0xFFFF)

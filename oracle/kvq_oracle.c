@@ -51,6 +51,9 @@
  *   k_err, v_err : float [B][Hkv][cap/64]
  */
 #include <math.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -58,6 +61,16 @@
 #define D 128
 #define BLK 64
 #define VG 32
+
+/* Number of threads the OpenMP loops below use (1 without OpenMP). */
+int kvqo_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
 
 /* ---------------------------------------------------------------- fp16 */
 

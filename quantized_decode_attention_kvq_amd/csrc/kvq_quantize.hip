@@ -60,7 +60,10 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(AppendArgs a) {
 
     for (int r = row0; r < BLK; r += 16) {
         const int64_t t = t_first + r;
-        const bool valid = t >= t_begin && t < t_end;  // uniform in the 16-lane group
+        // rows outside the appended range are neither read nor written; the
+        // test is uniform in the 16-lane group, so the group's shuffles below
+        // only ever involve active lanes
+        if (t < t_begin || t >= t_end) continue;
         const int64_t roff = (row_base + t) * D + 8 * lane16;
 
         // ---------------- key row: int8 per token, scale absmax/127
@@ -112,14 +115,12 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(AppendArgs a) {
         verr = fmaxf(verr, __shfl_xor(verr, 4));  // row: max over the 4 groups
         verr = fmaxf(verr, __shfl_xor(verr, 8));
 
-        if (valid) {
-            *reinterpret_cast<uint2 *>(a.c.k_codes + roff) = make_uint2(kc[0], kc[1]);
-            if (lane16 == 0) a.c.k_scales[row_base + t] = (uint16_t)ksb;
-            if ((lane16 & 3) == 0) a.c.v_scales[(row_base + t) * 4 + (lane16 >> 2)] = (uint16_t)vsb;
-            *reinterpret_cast<uint2 *>(&vtile[r][8 * lane16]) = make_uint2(vc[0], vc[1]);
-            kmax = fmaxf(kmax, kerr);
-            vmax = fmaxf(vmax, verr);
-        }
+        *reinterpret_cast<uint2 *>(a.c.k_codes + roff) = make_uint2(kc[0], kc[1]);
+        if (lane16 == 0) a.c.k_scales[row_base + t] = (uint16_t)ksb;
+        if ((lane16 & 3) == 0) a.c.v_scales[(row_base + t) * 4 + (lane16 >> 2)] = (uint16_t)vsb;
+        *reinterpret_cast<uint2 *>(&vtile[r][8 * lane16]) = make_uint2(vc[0], vc[1]);
+        kmax = fmaxf(kmax, kerr);
+        vmax = fmaxf(vmax, verr);
     }
 
     // block statistics: max over this workgroup's rows, then over old rows
