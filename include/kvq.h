@@ -147,10 +147,11 @@ size_t kvq_decode_workspace_bytes(const kvq_cache *c, int32_t q_heads);
  * (same arithmetic as kvq_bounds); fallback blocks read k16/v16, the others
  * read the int8/int4 codes.  mask_out [B][Hkv][NB] receives the masks used
  * (may be NULL).  workspace: device memory of at least
- * kvq_decode_workspace_bytes() bytes, zero-filled before its first use; the
- * library leaves it in a reusable state after every call, so it can be
- * reused by later calls on the same stream.  Errors: INVALID_ARG,
- * UNSUPPORTED, ALIGNMENT, WORKSPACE, HIP. */
+ * kvq_decode_workspace_bytes() bytes, 256-byte aligned, with no required
+ * contents; it holds the per-split partial results between the split-K
+ * kernel and the merge kernel that this call enqueues, so concurrent calls
+ * need distinct workspaces.  Errors: INVALID_ARG, UNSUPPORTED, ALIGNMENT,
+ * WORKSPACE, HIP. */
 kvq_status kvq_decode_attn(const kvq_cache *c, const uint16_t *q, int32_t q_heads, float sm_scale,
                            float tau_k, float tau_v, uint16_t *out, uint8_t *mask_out,
                            void *workspace, size_t ws_bytes, void *stream);

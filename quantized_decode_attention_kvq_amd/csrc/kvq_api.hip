@@ -57,18 +57,17 @@ kvq::CachePtrs ptrs(const kvq_cache *c) {
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Workspace layout: [counters u32 x B*Hkv, padded to 256 B]
-//                   [part_ml float2 x B*Hkv*S*G] [part_acc float x B*Hkv*S*G*128]
+// Workspace layout: [part_ml float2 x B*Hkv*S*G, padded to 256 B]
+//                   [part_acc float x B*Hkv*S*G*128]
 struct WsLayout {
-    size_t counters, ml, acc, total;
+    size_t ml, acc, total;
 };
 
 WsLayout ws_layout(const kvq_cache *c, int32_t g, int64_t splits) {
     const size_t bh = (size_t)c->batch * (size_t)c->kv_heads;
     WsLayout w;
-    w.counters = 0;
-    w.ml = round_up(bh * sizeof(uint32_t), 256);
-    w.acc = w.ml + round_up(bh * (size_t)splits * (size_t)g * sizeof(float2), 256);
+    w.ml = 0;
+    w.acc = round_up(bh * (size_t)splits * (size_t)g * sizeof(float2), 256);
     w.total = w.acc + bh * (size_t)splits * (size_t)g * kvq::D * sizeof(float);
     return w;
 }
@@ -236,7 +235,6 @@ kvq_status kvq_decode_attn_ex(const kvq_cache *c, const uint16_t *q, int32_t q_h
     a.q = q;
     a.out = out;
     a.mask_out = mask_out;
-    a.counters = reinterpret_cast<uint32_t *>((char *)workspace + w.counters);
     a.part_ml = reinterpret_cast<float2 *>((char *)workspace + w.ml);
     a.part_acc = reinterpret_cast<float *>((char *)workspace + w.acc);
     a.cap = c->capacity;

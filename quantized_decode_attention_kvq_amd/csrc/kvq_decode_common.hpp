@@ -62,20 +62,16 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
-// Writes this workgroup's partial (m, l, acc) for split `split`, then the
-// last workgroup of (b, kvh) to arrive merges all splits into fp16 out and
-// resets the arrival counter.  wm/wl: [nw][16] per-wave running max/sum,
-// wacc: [nw][gp][128] per-wave unnormalised accumulators, all in LDS and
-// complete (a barrier has been passed) on entry.
-__device__ __forceinline__ void merge_and_finish(const DecodeArgs &a, int64_t bh, int split,
-                                                 int nw, int gp, const float (*wm)[16],
-                                                 const float (*wl)[16], const float *wacc) {
-    const int tid = threadIdx.x;
+// Writes this workgroup's partial (running max, running sum, unnormalised
+// accumulator) of split `split` for the G heads of (b, kvh).  Running maxima
+// are in log2 units (scores scaled by sm * log2(e)).  wm/wl: [nw][16]
+// per-wave running max/sum, wacc: [nw][gp][128] per-wave accumulators, all in
+// LDS and complete (a barrier has been passed) on entry.
+__device__ __forceinline__ void write_partial(const DecodeArgs &a, int64_t bh, int split, int nw,
+                                              int gp, const float (*wm)[16], const float (*wl)[16],
+                                              const float *wacc) {
     const int g = a.g;
-    __shared__ int is_last;
-
-    // 1. merge the waves of this workgroup into one partial
-    for (int idx = tid; idx < g * D; idx += blockDim.x) {
+    for (int idx = threadIdx.x; idx < g * D; idx += blockDim.x) {
         const int h = idx / D, j = idx % D;
         float M = -__builtin_huge_valf();
         for (int w = 0; w < nw; ++w) M = fmaxf(M, wm[w][h]);
@@ -83,7 +79,7 @@ __device__ __forceinline__ void merge_and_finish(const DecodeArgs &a, int64_t bh
         if (M != -__builtin_huge_valf()) {
             for (int w = 0; w < nw; ++w) {
                 if (wm[w][h] == -__builtin_huge_valf()) continue;
-                const float f = __expf(wm[w][h] - M);
+                const float f = __builtin_amdgcn_exp2f(wm[w][h] - M);
                 L += wl[w][h] * f;
                 A += wacc[(w * gp + h) * D + j] * f;
             }
@@ -92,37 +88,6 @@ __device__ __forceinline__ void merge_and_finish(const DecodeArgs &a, int64_t bh
         a.part_acc[p * D + j] = A;
         if (j == 0) a.part_ml[p] = make_float2(M, L);
     }
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-        const uint32_t prev = atomicAdd(&a.counters[bh], 1u);
-        is_last = (prev == (uint32_t)(a.splits - 1));
-    }
-    __syncthreads();
-    if (!is_last) return;
-    __threadfence();
-
-    // 2. last arriver: merge the splits, normalise, write fp16
-    const int64_t b = bh / a.hkv, kvh = bh % a.hkv;
-    for (int idx = tid; idx < g * D; idx += blockDim.x) {
-        const int h = idx / D, j = idx % D;
-        float M = -__builtin_huge_valf();
-        for (int s = 0; s < a.splits; ++s) M = fmaxf(M, a.part_ml[(bh * a.splits + s) * g + h].x);
-        float L = 0.0f, A = 0.0f;
-        if (M != -__builtin_huge_valf()) {
-            for (int s = 0; s < a.splits; ++s) {
-                const int64_t p = (bh * a.splits + s) * g + h;
-                const float2 ml = a.part_ml[p];
-                if (ml.x == -__builtin_huge_valf()) continue;
-                const float f = __expf(ml.x - M);
-                L += ml.y * f;
-                A += a.part_acc[p * D + j] * f;
-            }
-        }
-        const float o = (L > 0.0f) ? A / L : 0.0f;
-        a.out[((b * a.hq) + kvh * g + h) * D + j] = (uint16_t)f2h_rn(o);
-    }
-    if (tid == 0) a.counters[bh] = 0u;
 }
 
 }  // namespace kvq

@@ -12,7 +12,8 @@
 // 64-token blocks of one (b, kvh); its four waves take every fourth block.
 // Per block a wave maps lane t to token t for Q.K (int8 codes are widened to
 // fp16 pairs with a byte permute and dotted against q with v_dot2_f32_f16),
-// updates its online softmax, stages the weights p*s_v in LDS and then maps
+// updates its online softmax (scores in log2 units, exp2), stages the
+// weights p*s_v in LDS and then maps
 // lane l to channels (2l, 2l+1) for P.V over the block's channel-major int4
 // codes.  Waves and splits are merged by log-sum-exp; the last workgroup of a
 // (b, kvh) to finish writes the fp16 output.
@@ -78,7 +79,8 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
     __shared__ __attribute__((aligned(16))) float w_lds[NW][GP][4][BLK];
     __shared__ float wm[NW][16], wl[NW][16];
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept scalar
     const int split = blockIdx.x;
     const int64_t kvh = blockIdx.y, b = blockIdx.z;
     const int64_t bh = b * a.hkv + kvh;
@@ -99,9 +101,10 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
 
     const int64_t row_base = bh * a.cap;
     const int vg = lane >> 4;  // value group of channels (2*lane, 2*lane+1)
+    const float sml2 = a.sm * 1.4426950408889634f;  // scores in log2 units
 
     for (int64_t blk = blk0 + wave; blk < blk1; blk += NW) {
-        const uint32_t mk = mask_lds[blk - blk0];
+        const uint32_t mk = __builtin_amdgcn_readfirstlane(mask_lds[blk - blk0]);
         const int64_t t = blk * BLK + lane;
         const bool valid = t < a.length;
 
@@ -136,7 +139,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
                     sc[h] = s;
                 }
             }
-            const float f = ks * a.sm;
+            const float f = ks * sml2;
 #pragma unroll
             for (int h = 0; h < GP; ++h) sc[h] *= f;
         } else {
@@ -156,7 +159,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
                 }
             }
 #pragma unroll
-            for (int h = 0; h < GP; ++h) sc[h] *= a.sm;
+            for (int h = 0; h < GP; ++h) sc[h] *= sml2;
         }
 
         // ---------------- online softmax over the block (per head)
@@ -177,8 +180,8 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
             const float m_new = fmaxf(m_run[h], wave_max(s));
             float p = 0.0f, alpha = 1.0f;
             if (m_new != -__builtin_huge_valf()) {
-                p = valid ? __expf(s - m_new) : 0.0f;
-                alpha = (m_run[h] == -__builtin_huge_valf()) ? 0.0f : __expf(m_run[h] - m_new);
+                p = valid ? __builtin_amdgcn_exp2f(s - m_new) : 0.0f;
+                alpha = (m_run[h] == -__builtin_huge_valf()) ? 0.0f : __builtin_amdgcn_exp2f(m_run[h] - m_new);
             }
             l_run[h] = l_run[h] * alpha + wave_sum(p);
             acc[h][0] *= alpha;
@@ -251,7 +254,56 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
         }
     }
     __syncthreads();
-    merge_and_finish(a, bh, split, NW, GP, wm, wl, wacc);
+    write_partial(a, bh, split, NW, GP, wm, wl, wacc);
+}
+
+// ------------------------------------------------------------ split merge
+
+// Log-sum-exp merge of the splits of one (b, kvh), in log2 units: M = max m_s,
+// L = sum l_s 2^(m_s - M), out = sum acc_s 2^(m_s - M) / L, written as fp16.
+// The per-(split, head) weights 2^(m_s - M) / L are formed once in LDS; the
+// accumulators are then summed with coalesced loads, several splits in
+// flight per thread.  No split holding a valid token (length 0) gives 0.
+__global__ __launch_bounds__(256) void merge_splits_kernel(DecodeArgs a) {
+    __shared__ float wgt[MAX_SPLITS][16];
+    __shared__ float2 ml[MAX_SPLITS][16];
+    const int64_t kvh = blockIdx.x, b = blockIdx.y;
+    const int64_t bh = b * a.hkv + kvh;
+    const int g = a.g, S = a.splits;
+    const float2 *pml = a.part_ml + bh * S * g;
+    for (int i = threadIdx.x; i < S * g; i += blockDim.x) ml[i / g][i % g] = pml[i];
+    __syncthreads();
+    for (int i = threadIdx.x; i < S * g; i += blockDim.x) {
+        const int s = i / g, h = i % g;
+        float M = -__builtin_huge_valf();
+        for (int r = 0; r < S; ++r) M = fmaxf(M, ml[r][h].x);
+        float L = 0.0f;
+        for (int r = 0; r < S; ++r)
+            if (ml[r][h].x != -__builtin_huge_valf()) L += ml[r][h].y * __builtin_amdgcn_exp2f(ml[r][h].x - M);
+        const float m_s = ml[s][h].x;
+        wgt[s][h] = (L > 0.0f && m_s != -__builtin_huge_valf()) ? __builtin_amdgcn_exp2f(m_s - M) / L : 0.0f;
+    }
+    __syncthreads();
+    const float *pacc = a.part_acc + bh * S * g * D;
+    for (int idx = threadIdx.x; idx < g * D; idx += blockDim.x) {
+        const int h = idx / D;
+        float o = 0.0f;
+        int s = 0;
+        for (; s + 8 <= S; s += 8) {
+            float v[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) v[k] = pacc[(int64_t)(s + k) * g * D + idx];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) o += wgt[s + k][h] * v[k];
+        }
+        for (; s < S; ++s) o += wgt[s][h] * pacc[(int64_t)s * g * D + idx];
+        a.out[((b * a.hq) + kvh * g) * D + idx] = (uint16_t)f2h_rn(o);
+    }
+}
+
+hipError_t launch_merge(const DecodeArgs &a, int batch, hipStream_t s) {
+    hipLaunchKernelGGL(merge_splits_kernel, dim3((unsigned)a.hkv, (unsigned)batch), dim3(256), 0, s, a);
+    return hipGetLastError();
 }
 
 hipError_t launch_decode_valu(const DecodeArgs &a, int batch, hipStream_t s) {
@@ -267,7 +319,8 @@ hipError_t launch_decode_valu(const DecodeArgs &a, int batch, hipStream_t s) {
         hipLaunchKernelGGL(decode_valu_kernel<8>, grid, dim3(256), 0, s, a);
     else
         hipLaunchKernelGGL(decode_valu_kernel<16>, grid, dim3(256), 0, s, a);
-    return hipGetLastError();
+    hipError_t e = hipGetLastError();
+    return e != hipSuccess ? e : launch_merge(a, batch, s);
 }
 
 }  // namespace kvq

@@ -45,7 +45,6 @@ struct DecodeArgs {
     const uint16_t *q;
     uint16_t *out;
     uint8_t *mask_out;
-    uint32_t *counters;  // [B*Hkv], zero between calls
     float2 *part_ml;     // [B*Hkv][S][G] (running max, running sum)
     float *part_acc;     // [B*Hkv][S][G][128] unnormalised
     int64_t cap, length, nbc, nb;
@@ -62,6 +61,7 @@ hipError_t launch_append(const AppendArgs &a, int batch, int64_t nblk, hipStream
 hipError_t launch_bounds(const BoundsArgs &a, int batch, hipStream_t s);
 hipError_t launch_decode_valu(const DecodeArgs &a, int batch, hipStream_t s);
 hipError_t launch_decode_mfma(const DecodeArgs &a, int batch, hipStream_t s);
+hipError_t launch_merge(const DecodeArgs &a, int batch, hipStream_t s);
 bool mfma_supports(int g);
 
 }  // namespace kvq
