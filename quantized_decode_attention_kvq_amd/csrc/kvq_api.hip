@@ -91,10 +91,11 @@ int device_cus() {
     return cached[dev];
 }
 
-// Splits: enough workgroups to give every CU several waves in flight, never
-// more splits than blocks, never more blocks per split than the LDS mask
-// table holds.
-int64_t choose_splits(const kvq_cache *c, int64_t nb, int32_t requested) {
+// Splits: enough workgroups to occupy every CU (`per_cu` resident
+// workgroups each: the MFMA kernel's LDS ring takes a whole CU, the VALU
+// kernel fits four), never more splits than blocks, never more blocks per
+// split than the LDS mask table holds.
+int64_t choose_splits(const kvq_cache *c, int64_t nb, int32_t requested, int per_cu) {
     const int64_t bh = (int64_t)c->batch * c->kv_heads;
     const int64_t smax = max_splits(c);
     int64_t s;
@@ -103,7 +104,7 @@ int64_t choose_splits(const kvq_cache *c, int64_t nb, int32_t requested) {
     } else if (const char *env = getenv("KVQ_SPLITS")) {
         s = atoll(env);
     } else {
-        const int64_t target_wgs = 4LL * device_cus();
+        const int64_t target_wgs = (int64_t)per_cu * device_cus();
         s = (target_wgs + bh - 1) / bh;
     }
     if (s > nb) s = nb;
@@ -225,7 +226,10 @@ kvq_status kvq_decode_attn_ex(const kvq_cache *c, const uint16_t *q, int32_t q_h
     const int64_t nb = (c->length + kvq::BLK - 1) / kvq::BLK;
     const int64_t nbc = c->capacity / kvq::BLK;
     if (nb > (int64_t)kvq::MAX_BPS * kvq::MAX_SPLITS) return KVQ_ERR_UNSUPPORTED;
-    const int64_t s = nb > 0 ? choose_splits(c, nb, splits) : 1;
+    int32_t k = kernel;
+    if (k == KVQ_KERNEL_AUTO) k = kvq::mfma_supports(g) ? KVQ_KERNEL_MFMA : KVQ_KERNEL_VALU;
+    if (k == KVQ_KERNEL_MFMA && !kvq::mfma_supports(g)) return KVQ_ERR_UNSUPPORTED;
+    const int64_t s = nb > 0 ? choose_splits(c, nb, splits, k == KVQ_KERNEL_MFMA ? 1 : 4) : 1;
     const int64_t bps = nb > 0 ? (nb + s - 1) / s : 1;
     const int64_t s_eff = nb > 0 ? (nb + bps - 1) / bps : 1;
 
@@ -250,9 +254,6 @@ kvq_status kvq_decode_attn_ex(const kvq_cache *c, const uint16_t *q, int32_t q_h
     a.tau_k = tau_k;
     a.tau_v = tau_v;
 
-    int32_t k = kernel;
-    if (k == KVQ_KERNEL_AUTO) k = kvq::mfma_supports(g) ? KVQ_KERNEL_MFMA : KVQ_KERNEL_VALU;
-    if (k == KVQ_KERNEL_MFMA && !kvq::mfma_supports(g)) return KVQ_ERR_UNSUPPORTED;
     hipError_t e = (k == KVQ_KERNEL_MFMA) ? kvq::launch_decode_mfma(a, c->batch, (hipStream_t)stream)
                                           : kvq::launch_decode_valu(a, c->batch, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e);

@@ -15,16 +15,17 @@ namespace kvq {
 
 // Loads the G query rows of (b, kvh) into q_lds (fp16 bits, [16][128], rows
 // >= G zeroed) and returns the group query norm (max over the G heads).  Must
-// be called by all 256 threads of the workgroup.  qn_lds: 16 floats.
+// be called by all threads of the workgroup (at least 256); 16-lane group h
+// handles head h.  qn_lds: 16 floats.
 __device__ __forceinline__ float load_q_and_norm(const uint16_t *__restrict__ q, int64_t qrow0,
                                                  int g, uint16_t (*q_lds)[D], float *qn_lds) {
     const int tid = threadIdx.x;
     const int h = tid >> 4, lane16 = tid & 15;
     uint4 raw = make_uint4(0, 0, 0, 0);
     if (h < g) raw = *reinterpret_cast<const uint4 *>(q + (qrow0 + h) * D + 8 * lane16);
-    *reinterpret_cast<uint4 *>(&q_lds[h][8 * lane16]) = raw;
+    if (h < 16) *reinterpret_cast<uint4 *>(&q_lds[h][8 * lane16]) = raw;
     const float n = qnorm16(raw);  // all 16 lanes of the group participate
-    if (lane16 == 0) qn_lds[h] = n;
+    if (lane16 == 0 && h < 16) qn_lds[h] = n;
     __syncthreads();
     float qn = 0.0f;
     for (int i = 0; i < g; ++i) qn = max_keep_nan(qn, qn_lds[i]);

@@ -6,37 +6,39 @@
 // statistics and the query norm, before any tile is fetched), Key
 // Contributions "Deterministic Recovery" (uncertified blocks read FP16).
 //
-// The G query heads of a KV group share every K/V tile, so per 64-token
-// block Q.K^T is a (64 tokens x 128) x (128 x G) contraction and P.V a
-// (128 x 64 tokens) x (64 x G) one.  Both run on v_mfma_f32_16x16x32_f16 with
-// the heads on the N side (padded to 16); int8/int4 codes are widened to
-// exact fp16 integers in registers and their scales are applied to the fp32
-// scores (keys) and folded into the fp16 P operand per 32-channel group
-// (values).  Only the widening, the online softmax and the operand packing
-// run on the VALU, which keeps a G >= 2 group from being ALU-bound.
+// The G query heads of a KV group share every K/V tile, so Q.K^T over a tile
+// is a (tokens x 128) x (128 x G) contraction and P.V a (128 x tokens) x
+// (tokens x G) one.  Both run on v_mfma_f32_16x16x32_f16 with the heads on the
+// N side (padded to 16); int8/int4 codes are widened to exact fp16 integers in
+// registers and their scales are applied to the fp32 scores (keys) and folded
+// into the fp16 P operand per 32-channel group (values).  Only the widening,
+// the online softmax and the operand packing run on the VALU.
 //
 // Operand layout (A lane l: row l%16, k-slots [8*(l/16), +8); B lane l: column
 // l%16, same k-slots; C lane l: column l%16, rows 4*(l/16) .. +3).  The
 // contraction order inside one instruction is free, so the slots are chosen
 // to make loads contiguous and to let the P operand of P.V come straight out
-// of the Q.K^T accumulators without any cross-lane traffic:
-//   Q.K^T subtile st = 2u+e (u, e in {0,1}) holds tokens
-//       sigma(st, m) = 16*(m/4) + 8u + 4e + (m%4),  m = 0..15,
-//   and its A lane (m, dg) holds key channels [32dg + 8s, +8) at step s, so
-//   one lane reads 32 contiguous code bytes of one token row.
-//   P.V step u of m-tile mt (channels 16mt..16mt+15) has A lane (m, kg)
-//   holding the 8 tokens 16kg + 8u + [0, 8) of channel 16mt + m -- four bytes
-//   of the channel-major nibble layout -- in the slot order (0,4),(1,5),(2,6),
-//   (3,7) that the C registers of subtiles 2u and 2u+1 provide.
+// of the Q.K^T accumulators without any cross-lane traffic.  A 64-token block
+// is streamed as two 32-token halves u; in half u,
+//   Q.K^T subtile e (e in {0,1}) holds tokens
+//       32u + 8*(m/4) + 4e + (m%4),  m = 0..15,
+//   and its A lane (m, dg) holds key channels [32dg + 8s, +8) at step s (32
+//   contiguous code bytes of one token row);
+//   P.V m-tile mt (channels 16mt..16mt+15) has A lane (m, kg) holding the 8
+//   tokens 32u + 8kg + [0, 8) of channel 16mt + m -- four bytes of the
+//   channel-major nibble layout -- in the slot order (0,4),(1,5),(2,6),(3,7)
+//   that the C registers of subtiles 0 and 1 provide.
 //
-// Grid (splits, Hkv, B), 256 threads; each wave streams every fourth block of
-// its workgroup's range with its own online softmax, prefetching the next
-// block's quantized tiles into registers while it computes the current one;
-// two such waves share each SIMD.
-// Blocks with a fallback bit take a slower path that loads the FP16 tile
-// (keys: contiguous 64 B per lane; values: per-token gathers).  Waves and
-// splits are merged by log-sum-exp; the last workgroup of a (b, kvh) writes
-// the fp16 output.
+// Grid (splits, Hkv, B), 512 threads = 8 waves (two per SIMD, so one wave's
+// VALU and matrix work hides the other's latencies), one workgroup per CU.
+// Each wave streams the halves of every eighth block of its workgroup's range
+// through its own 3-stage LDS ring: the quantized data of a half (4 KB key
+// codes, 2 KB value codes, key and value scales) is copied HBM -> LDS by
+// global_load_lds (no registers held while in flight), so two halves are in
+// flight while the wave computes a third.  The copy places every chunk where
+// the MFMA lane that consumes it reads it back with a lane-linear ds_read.
+// Halves of blocks with a fallback bit read their FP16 rows straight from HBM.
+// Waves and splits are merged by log-sum-exp in a second kernel.
 #include "kvq_decode_common.hpp"
 
 namespace kvq {
@@ -47,7 +49,7 @@ typedef float float2_t __attribute__((ext_vector_type(2)));
 
 namespace {
 
-constexpr int NW = 4;  // waves per workgroup
+constexpr int NW = 8;  // waves per workgroup
 constexpr float NEG_INF = -__builtin_huge_valf();
 
 __device__ __forceinline__ float4_t mfma(uint4 a, uint4 b, float4_t c) {
@@ -102,130 +104,156 @@ __device__ __forceinline__ void wave_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Registers of one block's quantized tiles for one lane.
-struct QTile {
-    uint4 k[4][2];  // [subtile][half]: 16 code bytes of row sigma(st, m), channels 32dg + 16h ..
-    uint2 v[8];     // [m-tile]: 8 nibble bytes, channel 16mt + m, tokens 16kg .. 16kg+15
-    uint32_t ks;    // k_scale of token `lane` (fp16 bits)
-    uint2 vs;       // 4 v_scales of token `lane`
-};
+// Row (token) of the half held by MFMA row m of Q.K^T subtile e.
+__device__ __forceinline__ int half_row(int e, int m) { return 8 * (m >> 2) + 4 * e + (m & 3); }
 
-__device__ __forceinline__ int sigma(int st, int m) {
-    return 16 * (m >> 2) + 8 * (st >> 1) + 4 * (st & 1) + (m & 3);
+// One stage of a wave's LDS ring: the quantized data of one 32-token half u
+// of a block.
+//   [0, 4096)     key codes, 4 chunks of 1 KB; chunk 2e+h, lane l (m, dg):
+//                 row half_row(e, m), code bytes [32dg + 16h, +16)
+//   [4096, 6144)  value codes, 2 chunks of 1 KB; chunk j, lane l: channel
+//                 64j + l, bytes [16u, +16) (tokens 32u .. 32u+31)
+//   [6144, 6400)  key scales, one dword per token of the half (fp16 in the
+//                 low half; lanes 32..63 repeat tokens 0..31)
+//   [6400, 6656)  value scales: dword t < 32 = groups (0,1) of token t,
+//                 dword 32 + t = groups (2,3)
+constexpr int ST_K = 0, ST_V = 4096, ST_KS = 6144, ST_VS = 6400, ST_BYTES = 6656;
+constexpr int NSTAGE = 3;
+constexpr int DMA_PER_HALF = 8;  // 4 key + 2 value + 1 key-scale + 1 value-scale copies
+
+// Copies of global memory into LDS that bypass the registers.  M0 holds the
+// wave-uniform LDS destination; lane l writes its bytes at M0 + l*size (16 B
+// per lane for dwordx4; a zero-extended dword per lane for dword and ushort).
+// The copy is issued in inline assembly so that its completion is tracked
+// here, with s_waitcnt vmcnt, rather than by the compiler's conservative wait
+// before every LDS read.  The preceding lgkmcnt(0) retires any LDS read of
+// the stage being refilled.
+__device__ __forceinline__ void dma16(uint32_t lds, const void *src) {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :: "s"(lds), "v"(src) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(uint32_t lds, const void *src) {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+                 :: "s"(lds), "v"(src) : "memory", "m0");
+}
+__device__ __forceinline__ void dma2(uint32_t lds, const void *src) {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_ushort %1, off"
+                 :: "s"(lds), "v"(src) : "memory", "m0");
 }
 
-// Per-lane byte offsets of the quantized tiles inside one block, computed once:
-// keys: row sigma(0, m), channels 32dg (the other subtiles and halves add
-// constants); values: channel m, tokens 16kg (m-tiles add 512 B).
-struct LaneOffsets {
-    uint32_t k, v;
-};
-
-__device__ __forceinline__ LaneOffsets lane_offsets(int lane) {
-    const int m = lane & 15, g4 = lane >> 4;
-    return LaneOffsets{(uint32_t)(sigma(0, m) * D + 32 * g4), (uint32_t)(m * (BLK / 2) + 8 * g4)};
+// Waits until at most N of this wave's memory loads are outstanding (loads
+// complete in issue order).  The "memory" clobber keeps LDS reads of the
+// stage below the wait.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
 }
 
-// Loads block `blk` of (b, kvh) into `t`: wave-uniform block bases plus the
-// lane offsets plus compile-time constants (sigma(st, m) - sigma(0, m) =
-// 8*(st/2) + 4*(st%2) rows).
-__device__ __forceinline__ void load_qtile(QTile &t, const DecodeArgs &a, int64_t bh, int64_t blk,
-                                           LaneOffsets lo, int lane) {
+// Issues the copies of half u of block `blk` of (b, kvh) into the stage at
+// LDS byte address `stage` (wave-uniform).  Every source address lies inside
+// the block.
+__device__ __forceinline__ void issue_half(const DecodeArgs &a, int64_t bh, int64_t blk, int u,
+                                           uint32_t stage, int lane) {
+    const int m = lane & 15, dg = lane >> 4, l32 = lane & 31;
     const int64_t row0 = bh * a.cap + blk * BLK;
-    const int8_t *kc = a.c.k_codes + row0 * D + lo.k;
-    const uint8_t *vc = a.c.v_codes + (bh * a.nbc + blk) * (D * BLK / 2) + lo.v;
+    const int8_t *kc = a.c.k_codes + (row0 + 32 * u) * D + 32 * dg;
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-        const int rows = 8 * (st >> 1) + 4 * (st & 1);
-        t.k[st][0] = *reinterpret_cast<const uint4 *>(kc + rows * D);
-        t.k[st][1] = *reinterpret_cast<const uint4 *>(kc + rows * D + 16);
-    }
+    for (int e = 0; e < 2; ++e)
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) t.v[mt] = *reinterpret_cast<const uint2 *>(vc + mt * 16 * (BLK / 2));
-    t.ks = a.c.k_scales[row0 + lane];
-    t.vs = *reinterpret_cast<const uint2 *>(a.c.v_scales + (row0 + lane) * 4);
+        for (int h = 0; h < 2; ++h) dma16(stage + ST_K + (2 * e + h) * 1024, kc + half_row(e, m) * D + 16 * h);
+    const uint8_t *vc = a.c.v_codes + (bh * a.nbc + blk) * (D * BLK / 2) + lane * (BLK / 2) + 16 * u;
+    dma16(stage + ST_V, vc);
+    dma16(stage + ST_V + 1024, vc + 64 * (BLK / 2));
+    dma2(stage + ST_KS, a.c.k_scales + row0 + 32 * u + l32);
+    dma4(stage + ST_VS, a.c.v_scales + (row0 + 32 * u + l32) * 4 + 2 * (lane >> 5));
 }
 
-}  // namespace
-
-// Scores, online softmax and P.V of one block for one wave, from the block's
-// quantized tiles in `t` (already in registers) or, for fallback parts, from
-// the FP16 originals.  Scores are kept in log2 units (sm * log2(e) folded into
-// the per-token key factor) so the softmax uses exp2.  State: m_run / l_run of
-// head m (this lane's column; l as this lane's share of the 16-token groups)
-// and the P.V accumulators.
+// Scores, online softmax and P.V of half u of one block for one wave, from the
+// stage in LDS or, for fallback parts, from the FP16 originals.  Scores are
+// kept in log2 units (sm * log2(e) folded into the per-token key factor) so
+// the softmax uses exp2.  State: m_run / l_run of head m (this lane's column;
+// l as this lane's share of the 8-token groups) and the P.V accumulators.
 struct WaveState {
     float m_run, l_run;
     float4_t acc[8];
 };
 
-__device__ __forceinline__ void process_block(const DecodeArgs &a, const QTile &t, int64_t bh,
-                                              int64_t blk, uint32_t mk, const uint4 (&qb)[4],
-                                              float sml2, float *ks_w, uint16_t (*vs_w)[BLK],
-                                              WaveState &w, int lane) {
+__device__ __forceinline__ void process_half(const DecodeArgs &a, const uint8_t *stage, int64_t bh,
+                                             int64_t blk, int u, uint32_t mk, const uint4 (&qb)[4],
+                                             float sml2, WaveState &w, int lane) {
     const int m = lane & 15, g4 = lane >> 4;
-    const int64_t row0 = bh * a.cap + blk * BLK;
-    const int nvalid = (int)(a.length - blk * BLK < BLK ? a.length - blk * BLK : BLK);
-    const bool lane_valid = lane < nvalid;  // token `lane` of the block
+    const int64_t row0 = bh * a.cap + blk * BLK + 32 * u;  // first token of the half
+    const int64_t left = a.length - (blk * BLK + 32 * u);
+    const int nvalid = (int)(left < 32 ? (left > 0 ? left : 0) : 32);  // valid tokens of the half
 
-    // ---------------- Q.K^T: S^T[token][head] for the 4 subtiles
-    float4_t sc[4];
+    // ---------------- Q.K^T: S^T[token][head] for the 2 subtiles
+    float4_t sc[2];
     if (!(mk & 1u)) {
-        ks_w[lane] = h2f(t.ks) * sml2;  // per-token factor k_scale * sm * log2(e)
+        uint4 kt[4];
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
+        for (int j = 0; j < 4; ++j) kt[j] = *reinterpret_cast<const uint4 *>(stage + ST_K + j * 1024 + 16 * lane);
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
             float4_t c = {0.f, 0.f, 0.f, 0.f};
-            c = mfma(i8x8_to_h8(t.k[st][0].x, t.k[st][0].y), qb[0], c);
-            c = mfma(i8x8_to_h8(t.k[st][0].z, t.k[st][0].w), qb[1], c);
-            c = mfma(i8x8_to_h8(t.k[st][1].x, t.k[st][1].y), qb[2], c);
-            c = mfma(i8x8_to_h8(t.k[st][1].z, t.k[st][1].w), qb[3], c);
-            sc[st] = c;
+            c = mfma(i8x8_to_h8(kt[2 * e].x, kt[2 * e].y), qb[0], c);
+            c = mfma(i8x8_to_h8(kt[2 * e].z, kt[2 * e].w), qb[1], c);
+            c = mfma(i8x8_to_h8(kt[2 * e + 1].x, kt[2 * e + 1].y), qb[2], c);
+            c = mfma(i8x8_to_h8(kt[2 * e + 1].z, kt[2 * e + 1].w), qb[3], c);
+            sc[e] = c;
         }
-        wave_sync();
+        // key scales of tokens 8*g4 + 4e + i of the half (one dword per token)
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            const float4 f = *reinterpret_cast<const float4 *>(&ks_w[16 * g4 + 4 * st]);
-            sc[st][0] *= f.x;
-            sc[st][1] *= f.y;
-            sc[st][2] *= f.z;
-            sc[st][3] *= f.w;
+        for (int e = 0; e < 2; ++e) {
+            const uint4 f = *reinterpret_cast<const uint4 *>(stage + ST_KS + 4 * (8 * g4 + 4 * e));
+            sc[e][0] *= h2f(f.x & 0xFFFFu) * sml2;
+            sc[e][1] *= h2f(f.y & 0xFFFFu) * sml2;
+            sc[e][2] *= h2f(f.z & 0xFFFFu) * sml2;
+            sc[e][3] *= h2f(f.w & 0xFFFFu) * sml2;
         }
     } else {
+        // FP16 key rows straight from HBM: all 8 loads first, then the
+        // contractions, so the loads share one wait
         const uint16_t *kr = a.c.k16 + row0 * D + 32 * g4;  // channels [32dg, 32dg+32)
+        uint4 kf[2][4];
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            const uint4 *p = reinterpret_cast<const uint4 *>(kr + sigma(st, m) * D);
+        for (int e = 0; e < 2; ++e) {
+            const uint4 *p = reinterpret_cast<const uint4 *>(kr + half_row(e, m) * D);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) kf[e][k] = p[k];
+        }
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
             float4_t c = {0.f, 0.f, 0.f, 0.f};
-            c = mfma(p[0], qb[0], c);
-            c = mfma(p[1], qb[1], c);
-            c = mfma(p[2], qb[2], c);
-            c = mfma(p[3], qb[3], c);
-            sc[st] = c * sml2;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) c = mfma(kf[e][k], qb[k], c);
+            sc[e] = c * sml2;
         }
     }
 
-    // ---------------- online softmax of head m over this block
-    const int tk0 = 16 * g4;  // this lane's 16 tokens: tk0 + 4st + i of the block
+    // ---------------- online softmax of head m over this half
+    const int tk0 = 8 * g4;  // this lane's 8 tokens of the half: tk0 + 4e + i
     float bmax = NEG_INF;
 #pragma unroll
-    for (int st = 0; st < 4; ++st)
+    for (int e = 0; e < 2; ++e)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            if (tk0 + 4 * st + i >= nvalid) sc[st][i] = NEG_INF;
-            bmax = fmaxf(bmax, sc[st][i]);
+            if (tk0 + 4 * e + i >= nvalid) sc[e][i] = NEG_INF;
+            bmax = fmaxf(bmax, sc[e][i]);
         }
     bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
     bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
-    const float m_new = fmaxf(w.m_run, bmax);  // finite: the block holds a valid token
-    const float alpha = __builtin_amdgcn_exp2f(w.m_run - m_new);  // 0 on the first block
-    float pv[4][4];
+    const float m_new = fmaxf(w.m_run, bmax);
+    // a half with no valid token (the tail of the last block) leaves the
+    // state unchanged: m_new may then still be -inf
+    const float alpha = (m_new == NEG_INF) ? 1.0f : __builtin_amdgcn_exp2f(w.m_run - m_new);
+    float pv[2][4];
     float psum = 0.0f;
 #pragma unroll
-    for (int st = 0; st < 4; ++st)
+    for (int e = 0; e < 2; ++e)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            pv[st][i] = __builtin_amdgcn_exp2f(sc[st][i] - m_new);  // exp2(-inf) = 0
-            psum += pv[st][i];
+            pv[e][i] = (sc[e][i] == NEG_INF) ? 0.0f : __builtin_amdgcn_exp2f(sc[e][i] - m_new);
+            psum += pv[e][i];
         }
     w.m_run = m_new;
     w.l_run = w.l_run * alpha + psum;
@@ -235,88 +263,116 @@ __device__ __forceinline__ void process_block(const DecodeArgs &a, const QTile &
     }
 
     // ---------------- P.V
-    // B operand (k-slot pairs): p of tokens (8u + q, 8u + 4 + q) of this lane's 16
-    half2_t pp[2][4];
+    // B operand (k-slot pairs): p of tokens (8kg + q, 8kg + 4 + q) of the half
+    half2_t pp[4];
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-            pp[u][q] = __builtin_bit_cast(half2_t, pack_h2(pv[2 * u][q], pv[2 * u + 1][q]));
+    for (int q = 0; q < 4; ++q) pp[q] = __builtin_bit_cast(half2_t, pack_h2(pv[0][q], pv[1][q]));
     if (!(mk & 2u)) {
-        // value scales staged as [group][token], the tokens of each 8-run in
-        // the slot order 0,4,1,5,2,6,3,7, so one 16-byte read yields the
-        // (token q, token q+4) scale pairs; scales of tokens past `length`
-        // are zeroed (their p is 0, and a stale scale must not make it NaN)
-        {
-            const uint2 sv = lane_valid ? t.vs : make_uint2(0u, 0u);
-            const int r = lane & 7, slot = (lane & ~7) + ((r & 3) << 1) + (r >> 2);
-            vs_w[0][slot] = (uint16_t)(sv.x & 0xFFFFu);
-            vs_w[1][slot] = (uint16_t)(sv.x >> 16);
-            vs_w[2][slot] = (uint16_t)(sv.y & 0xFFFFu);
-            vs_w[3][slot] = (uint16_t)(sv.y >> 16);
-        }
-        wave_sync();
+        // value codes of channel 16mt + m, tokens 8kg .. 8kg+7 of the half
+        uint32_t vt[8];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
+        for (int mt = 0; mt < 8; ++mt)
+            vt[mt] = *reinterpret_cast<const uint32_t *>(stage + ST_V + (mt >> 2) * 1024 +
+                                                         16 * (16 * (mt & 3) + m) + 4 * g4);
+        // scales of tokens 8kg + [0, 8): dwords of groups (0,1) and (2,3)
+        const int t0 = 8 * g4;
+        const uint4 a01 = *reinterpret_cast<const uint4 *>(stage + ST_VS + 4 * t0);
+        const uint4 b01 = *reinterpret_cast<const uint4 *>(stage + ST_VS + 4 * (t0 + 4));
+        const uint4 a23 = *reinterpret_cast<const uint4 *>(stage + ST_VS + 128 + 4 * t0);
+        const uint4 b23 = *reinterpret_cast<const uint4 *>(stage + ST_VS + 128 + 4 * (t0 + 4));
+        uint32_t lo_a[4] = {a01.x, a01.y, a01.z, a01.w}, lo_b[4] = {b01.x, b01.y, b01.z, b01.w};
+        uint32_t hi_a[4] = {a23.x, a23.y, a23.z, a23.w}, hi_b[4] = {b23.x, b23.y, b23.z, b23.w};
+        if (nvalid < 32) {
+            // tokens past `length` carry stale scales: zero them (their p is
+            // 0, and 0 * NaN would reach the accumulator)
 #pragma unroll
-            for (int gg = 0; gg < 4; ++gg) {
-                const uint4 sp = *reinterpret_cast<const uint4 *>(&vs_w[gg][16 * g4 + 8 * u]);
-                uint4 bop;  // p * s_v in fp16: one rounding of p, one of the product
-                bop.x = __builtin_bit_cast(uint32_t, pp[u][0] * __builtin_bit_cast(half2_t, sp.x));
-                bop.y = __builtin_bit_cast(uint32_t, pp[u][1] * __builtin_bit_cast(half2_t, sp.y));
-                bop.z = __builtin_bit_cast(uint32_t, pp[u][2] * __builtin_bit_cast(half2_t, sp.z));
-                bop.w = __builtin_bit_cast(uint32_t, pp[u][3] * __builtin_bit_cast(half2_t, sp.w));
-                w.acc[2 * gg] = mfma(i4x8_to_h8(u ? t.v[2 * gg].y : t.v[2 * gg].x), bop, w.acc[2 * gg]);
-                w.acc[2 * gg + 1] =
-                    mfma(i4x8_to_h8(u ? t.v[2 * gg + 1].y : t.v[2 * gg + 1].x), bop, w.acc[2 * gg + 1]);
+            for (int q = 0; q < 4; ++q) {
+                if (t0 + q >= nvalid) lo_a[q] = hi_a[q] = 0u;
+                if (t0 + 4 + q >= nvalid) lo_b[q] = hi_b[q] = 0u;
             }
+        }
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+            uint32_t r[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t wa = (gg < 2) ? lo_a[q] : hi_a[q], wb = (gg < 2) ? lo_b[q] : hi_b[q];
+                // (scale of token q, scale of token q+4) for group gg
+                const uint32_t sp = (gg & 1) ? __builtin_amdgcn_perm(wb, wa, 0x07060302u)
+                                             : __builtin_amdgcn_perm(wb, wa, 0x05040100u);
+                // p * s_v in fp16: one rounding of p, one of the product
+                r[q] = __builtin_bit_cast(uint32_t, pp[q] * __builtin_bit_cast(half2_t, sp));
+            }
+            const uint4 bop = make_uint4(r[0], r[1], r[2], r[3]);
+            w.acc[2 * gg] = mfma(i4x8_to_h8(vt[2 * gg]), bop, w.acc[2 * gg]);
+            w.acc[2 * gg + 1] = mfma(i4x8_to_h8(vt[2 * gg + 1]), bop, w.acc[2 * gg + 1]);
         }
     } else {
+        const uint4 bop = make_uint4(__builtin_bit_cast(uint32_t, pp[0]), __builtin_bit_cast(uint32_t, pp[1]),
+                                     __builtin_bit_cast(uint32_t, pp[2]), __builtin_bit_cast(uint32_t, pp[3]));
+        const int tb = 8 * g4;  // tokens tb + q and tb + 4 + q of the half
+        // gather all 64 values first (one shared wait), then the 8
+        // contractions; rows past `length` are still inside the block's
+        // storage: load them, then zero them (a stale value could be NaN, and
+        // 0 * NaN would reach the accumulator)
+        uint32_t lo[8][4], hi[8][4];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const uint4 bop = make_uint4(__builtin_bit_cast(uint32_t, pp[u][0]), __builtin_bit_cast(uint32_t, pp[u][1]),
-                                         __builtin_bit_cast(uint32_t, pp[u][2]), __builtin_bit_cast(uint32_t, pp[u][3]));
-            const int tb = 16 * g4 + 8 * u;  // tokens tb + q and tb + 4 + q
+        for (int mt = 0; mt < 8; ++mt) {
+            const uint16_t *vcol = a.c.v16 + row0 * D + 16 * mt + m;
 #pragma unroll
-            for (int mt = 0; mt < 8; ++mt) {
-                const uint16_t *vcol = a.c.v16 + row0 * D + 16 * mt + m;
-                uint32_t r[4];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    // rows past `length` are still inside the block's storage:
-                    // load them unconditionally, then zero them (a stale value
-                    // could be NaN, and 0 * NaN would reach the accumulator)
-                    const int ta = tb + q, tb2 = tb + 4 + q;
-                    const uint32_t lo = vcol[ta * D], hi = vcol[tb2 * D];
-                    r[q] = ((ta < nvalid) ? lo : 0u) | (((tb2 < nvalid) ? hi : 0u) << 16);
-                }
-                w.acc[mt] = mfma(make_uint4(r[0], r[1], r[2], r[3]), bop, w.acc[mt]);
+            for (int q = 0; q < 4; ++q) {
+                lo[mt][q] = vcol[(tb + q) * D];
+                hi[mt][q] = vcol[(tb + 4 + q) * D];
             }
+        }
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) {
+            uint32_t r[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                r[q] = ((tb + q < nvalid) ? lo[mt][q] : 0u) | (((tb + 4 + q < nvalid) ? hi[mt][q] : 0u) << 16);
+            w.acc[mt] = mfma(make_uint4(r[0], r[1], r[2], r[3]), bop, w.acc[mt]);
         }
     }
 }
 
-// Two waves per SIMD (at most 256 registers each): one wave's VALU and matrix
-// work overlaps the other's memory latency.
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_mfma_kernel(
-    DecodeArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t q_lds[16][D];
+}  // namespace
+
+// Largest per-split block count the mask table of this kernel holds.
+constexpr int MFMA_MAX_BPS = 1024;
+
+__global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
+    // 8 waves x 3 stages x 6656 B = 159,744 B of ring.  Before the stream
+    // starts, wave 0's stage 2 holds the query rows; after it ends, the ring
+    // holds the wave merge.
+    __shared__ __attribute__((aligned(16))) uint8_t ring[NW][NSTAGE][ST_BYTES];
     __shared__ float qn_lds[16];
-    __shared__ uint8_t mask_lds[MAX_BPS];
-    __shared__ __attribute__((aligned(16))) float ks_lds[NW][BLK];
-    __shared__ __attribute__((aligned(16))) uint16_t vs_lds[NW][4][BLK];
-    __shared__ __attribute__((aligned(16))) float wacc[NW * 16 * D];
+    __shared__ uint8_t mask_lds[MFMA_MAX_BPS];
     __shared__ float wm[NW][16], wl[NW][16];
+    uint16_t(*q_lds)[D] = reinterpret_cast<uint16_t(*)[D]>(&ring[0][2][0]);
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept scalar
-    const int m = lane & 15, g4 = lane >> 4;  // MFMA row/column index and k-group
+    const int m = lane & 15, g4 = lane >> 4;                    // MFMA row/column index and k-group
     const int split = blockIdx.x;
     const int64_t kvh = blockIdx.y, b = blockIdx.z;
     const int64_t bh = b * a.hkv + kvh;
     const int g = a.g;
     const int64_t blk0 = (int64_t)split * a.bps;
     const int64_t blk1 = blk0 + a.bps < a.nb ? blk0 + a.bps : a.nb;
+
+    // this wave's blocks: first, first + NW, ..., streamed as halves
+    // k = 0 .. 2*nblk-1 (block k/2, half k%2); half k lives in stage k % 3
+    const int64_t first = blk0 + wave;
+    const int64_t nblk = first < blk1 ? (blk1 - 1 - first) / NW + 1 : 0;
+    const int64_t nhalf = 2 * nblk;
+    const uint32_t ring0 = (uint32_t)(uintptr_t)&ring[wave][0][0];
+    auto stage_addr = [&](int64_t k) { return ring0 + (uint32_t)((k % NSTAGE) * ST_BYTES); };
+    auto issue = [&](int64_t k) { issue_half(a, bh, first + (k >> 1) * NW, (int)(k & 1), stage_addr(k), lane); };
+    // start streaming before the query and mask set-up so it overlaps them
+    // (stages 0 and 1 only: stage 2 of wave 0 holds the query rows for now)
+    if (nhalf > 0) issue(0);
+    if (nhalf > 1) issue(1);
 
     const float qn = load_q_and_norm(a.q, b * a.hq + kvh * g, g, q_lds, qn_lds);
     compute_masks(a, bh, blk0, blk1, qn, mask_lds);
@@ -325,6 +381,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     uint4 qb[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) qb[s] = *reinterpret_cast<const uint4 *>(&q_lds[m][32 * g4 + 8 * s]);
+    __syncthreads();  // every wave holds its q operands: stage 2 of wave 0 is free
 
     const float sml2 = a.sm * 1.4426950408889634f;  // scores in log2 units
     WaveState ws;
@@ -333,29 +390,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) ws.acc[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-    // Two register tiles in ping-pong: while one block is processed from one
-    // tile, the loads of the wave's next block land in the other.  The next
-    // block index is clamped to a valid block at the end of the range so the
-    // load sequence stays uniform and the compiler can count it exactly.
-    QTile t0, t1;
-    const LaneOffsets lo = lane_offsets(lane);
-    int64_t blk = blk0 + wave;
-    if (blk < blk1) {
-        load_qtile(t0, a, bh, blk, lo, lane);
-        for (;;) {
-            int64_t nb = blk + NW < blk1 ? blk + NW : blk;
-            load_qtile(t1, a, bh, nb, lo, lane);
-            process_block(a, t0, bh, blk, __builtin_amdgcn_readfirstlane(mask_lds[blk - blk0]), qb, sml2,
-                          ks_lds[wave], vs_lds[wave], ws, lane);
-            blk += NW;
-            if (blk >= blk1) break;
-            nb = blk + NW < blk1 ? blk + NW : blk;
-            load_qtile(t0, a, bh, nb, lo, lane);
-            process_block(a, t1, bh, blk, __builtin_amdgcn_readfirstlane(mask_lds[blk - blk0]), qb, sml2,
-                          ks_lds[wave], vs_lds[wave], ws, lane);
-            blk += NW;
-            if (blk >= blk1) break;
-        }
+    // Before computing half k the copies of half k+2 are issued; waiting until
+    // at most the copies issued after half k's (0, 1 or 2 halves' worth) are
+    // outstanding makes half k resident.  Any other load issued in between
+    // only makes the wait stronger.
+    auto step = [&](int64_t k, int s) {
+        if (k + 2 < nhalf) issue(k + 2);
+        const int64_t after = (nhalf - 1 - k) < 2 ? (nhalf - 1 - k) : 2;
+        if (after == 2)
+            wait_vmcnt<2 * DMA_PER_HALF>();
+        else if (after == 1)
+            wait_vmcnt<DMA_PER_HALF>();
+        else
+            wait_vmcnt<0>();
+        const int64_t blk = first + (k >> 1) * NW;
+        process_half(a, &ring[wave][s][0], bh, blk, (int)(k & 1),
+                     __builtin_amdgcn_readfirstlane(mask_lds[blk - blk0]), qb, sml2, ws, lane);
+    };
+    for (int64_t k = 0; k < nhalf; k += NSTAGE) {
+        step(k, 0);
+        if (k + 1 < nhalf) step(k + 1, 1);
+        if (k + 2 < nhalf) step(k + 2, 2);
     }
 
     // ---------------- merge waves, then splits
@@ -363,6 +418,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     float l_run = ws.l_run;
     l_run += __shfl_xor(l_run, 16);
     l_run += __shfl_xor(l_run, 32);
+    __syncthreads();  // every wave is done with the ring: reuse it for the wave merge
+    float *wacc = reinterpret_cast<float *>(&ring[0][0][0]);
     if (m < g) {
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt)
@@ -381,7 +438,7 @@ bool mfma_supports(int g) { return g >= 1 && g <= 16; }
 
 hipError_t launch_decode_mfma(const DecodeArgs &a, int batch, hipStream_t s) {
     dim3 grid((unsigned)a.splits, (unsigned)a.hkv, (unsigned)batch);
-    hipLaunchKernelGGL(decode_mfma_kernel, grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(decode_mfma_kernel, grid, dim3(512), 0, s, a);
     hipError_t e = hipGetLastError();
     return e != hipSuccess ? e : launch_merge(a, batch, s);
 }
