@@ -98,10 +98,14 @@ __device__ __forceinline__ uint32_t pack_h2(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, half2_t));
 }
 
-__device__ __forceinline__ void wave_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+// Max over the four 16-lane rows (lanes l, l^16, l^32, l^48), with the
+// row-swap permutes (no LDS round trip): after a swap of a value with itself
+// the two results hold, in every lane, the lane's value and its partner's.
+__device__ __forceinline__ float max_across_rows(float v) {
+    const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+    const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
 }
 
 // Row (token) of the half held by MFMA row m of Q.K^T subtile e.
@@ -240,8 +244,7 @@ __device__ __forceinline__ void process_half(const DecodeArgs &a, const uint8_t 
             if (tk0 + 4 * e + i >= nvalid) sc[e][i] = NEG_INF;
             bmax = fmaxf(bmax, sc[e][i]);
         }
-    bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
-    bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
+    bmax = max_across_rows(bmax);
     const float m_new = fmaxf(w.m_run, bmax);
     // a half with no valid token (the tail of the last block) leaves the
     // state unchanged: m_new may then still be -inf
