@@ -47,6 +47,8 @@ def parse():
     p.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma"])
     p.add_argument("--splits", type=int, default=0)
     p.add_argument("--replicas", type=int, default=0, help="layer caches cycled (0: enough for >= 2 GB)")
+    p.add_argument("--fallback-frac", type=float, default=None,
+                   help="fraction of blocks per bound that fall back (default: the workload's; 0: none)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU work of the oracle sample")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -167,11 +169,14 @@ def main():
     kbn, vbn = kb.flatten().float().cpu().numpy(), vb.flatten().float().cpu().numpy()
 
     def tau(vals, frac):
+        if frac <= 0:
+            return float("inf")
         v = np.sort(vals[np.isfinite(vals)])
         k = max(1, int(round(frac * v.size)))
         return float(np.float32((v[v.size - k - 1] + v[v.size - k]) / 2))
 
-    tau_k, tau_v = tau(kbn, w.fallback_frac), tau(vbn, w.fallback_frac)
+    frac = w.fallback_frac if args.fallback_frac is None else args.fallback_frac
+    tau_k, tau_v = tau(kbn, frac), tau(vbn, frac)
     c0.length = w.T - 1
 
     out = torch.empty_like(q)
@@ -242,7 +247,8 @@ def main():
             "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "context": w.T,
             "fallback_blocks_key": round(float((m & 1).mean()), 5),
             "fallback_blocks_value": round(float(((m >> 1) & 1).mean()), 5),
-            "tau_k": tau_k, "tau_v": tau_v, "layers_cycled": R,
+            "tau_k": tau_k if np.isfinite(tau_k) else "inf", "tau_v": tau_v if np.isfinite(tau_v) else "inf",
+            "layers_cycled": R,
             "kernel": args.kernel, "splits": args.splits,
             "bytes_per_step": step_bytes,
         },

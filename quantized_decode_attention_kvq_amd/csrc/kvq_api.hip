@@ -91,11 +91,11 @@ int device_cus() {
     return cached[dev];
 }
 
-// Splits: enough workgroups to occupy every CU (`per_cu` resident
-// workgroups each: the MFMA kernel's LDS ring takes a whole CU, the VALU
-// kernel fits four), never more splits than blocks, never more blocks per
-// split than the LDS mask table holds.
-int64_t choose_splits(const kvq_cache *c, int64_t nb, int32_t requested, int per_cu) {
+// Splits: about `per_cu` workgroups per CU over the launch (the matrix-core
+// kernel keeps two resident per CU, so later ones fill CUs that finish
+// early; the VALU kernel keeps four), never more splits than blocks, never
+// more blocks per split than the kernel's LDS table holds (max_bps).
+int64_t choose_splits(const kvq_cache *c, int64_t nb, int32_t requested, int per_cu, int64_t max_bps) {
     const int64_t bh = (int64_t)c->batch * c->kv_heads;
     const int64_t smax = max_splits(c);
     int64_t s;
@@ -108,7 +108,7 @@ int64_t choose_splits(const kvq_cache *c, int64_t nb, int32_t requested, int per
         s = (target_wgs + bh - 1) / bh;
     }
     if (s > nb) s = nb;
-    const int64_t need = (nb + kvq::MAX_BPS - 1) / kvq::MAX_BPS;
+    const int64_t need = (nb + max_bps - 1) / max_bps;
     if (s < need) s = need;
     if (s > smax) s = smax;
     if (s < 1) s = 1;
@@ -226,10 +226,13 @@ kvq_status kvq_decode_attn_ex(const kvq_cache *c, const uint16_t *q, int32_t q_h
     const int64_t nb = (c->length + kvq::BLK - 1) / kvq::BLK;
     const int64_t nbc = c->capacity / kvq::BLK;
     if (nb > (int64_t)kvq::MAX_BPS * kvq::MAX_SPLITS) return KVQ_ERR_UNSUPPORTED;
+    // the matrix-core kernel lists at most MFMA_MAX_BPS blocks per split
+    const bool mfma_fits = kvq::mfma_supports(g) && nb <= (int64_t)kvq::MFMA_MAX_BPS * max_splits(c);
     int32_t k = kernel;
-    if (k == KVQ_KERNEL_AUTO) k = kvq::mfma_supports(g) ? KVQ_KERNEL_MFMA : KVQ_KERNEL_VALU;
-    if (k == KVQ_KERNEL_MFMA && !kvq::mfma_supports(g)) return KVQ_ERR_UNSUPPORTED;
-    const int64_t s = nb > 0 ? choose_splits(c, nb, splits, k == KVQ_KERNEL_MFMA ? 1 : 4) : 1;
+    if (k == KVQ_KERNEL_AUTO) k = mfma_fits ? KVQ_KERNEL_MFMA : KVQ_KERNEL_VALU;
+    if (k == KVQ_KERNEL_MFMA && !mfma_fits) return KVQ_ERR_UNSUPPORTED;
+    const bool mf = k == KVQ_KERNEL_MFMA;
+    const int64_t s = nb > 0 ? choose_splits(c, nb, splits, mf ? 1 : 4, mf ? kvq::MFMA_MAX_BPS : kvq::MAX_BPS) : 1;
     const int64_t bps = nb > 0 ? (nb + s - 1) / s : 1;
     const int64_t s_eff = nb > 0 ? (nb + bps - 1) / bps : 1;
 

@@ -29,15 +29,27 @@
 //   channel-major nibble layout -- in the slot order (0,4),(1,5),(2,6),(3,7)
 //   that the C registers of subtiles 0 and 1 provide.
 //
-// Grid (splits, Hkv, B), 512 threads = 8 waves (two per SIMD, so one wave's
-// VALU and matrix work hides the other's latencies), one workgroup per CU.
-// Each wave streams the halves of every eighth block of its workgroup's range
+// Grid (splits, Hkv, B), 256 threads = 4 waves, two workgroups per CU (so two
+// waves per SIMD: one wave's VALU and matrix work hides the other's
+// latencies), several workgroups per CU over the launch so that the hardware
+// dispatcher evens out the finishing times.  After the fallback masks of its
+// block range are known, a workgroup lists its blocks (certified ones first)
+// and its waves share them out: wave w takes every fourth certified block and
+// two of the eight fallback steps of every fallback block, so the waves of a
+// workgroup carry equal work however the fallback blocks fall.  Each wave
+// streams its steps
 // through its own 3-stage LDS ring: the quantized data of a half (4 KB key
 // codes, 2 KB value codes, key and value scales) is copied HBM -> LDS by
 // global_load_lds (no registers held while in flight), so two halves are in
 // flight while the wave computes a third.  The copy places every chunk where
 // the MFMA lane that consumes it reads it back with a lane-linear ds_read.
-// Halves of blocks with a fallback bit read their FP16 rows straight from HBM.
+// A block with a fallback bit is streamed through the same ring as eight
+// 8-token steps (an 8-token slice of FP16 rows is 2 KB per tensor, so a step
+// with both tensors in FP16 still fits a stage); its tokens sit in the rows
+// of the MFMA tiles that a 32-token half gives to its first 8 tokens, and the
+// other rows are masked.  Every step, of either kind, issues exactly 8 copy
+// instructions, so the waits stay compile-time constants, and no global load
+// is ever waited on while later steps are in flight.
 // Waves and splits are merged by log-sum-exp in a second kernel.
 #include "kvq_decode_common.hpp"
 
@@ -49,7 +61,8 @@ typedef float float2_t __attribute__((ext_vector_type(2)));
 
 namespace {
 
-constexpr int NW = 8;  // waves per workgroup
+constexpr int NW = 8;         // waves per workgroup (one workgroup per CU)
+constexpr int FBS = 8 / NW;   // fallback steps of one fallback block per wave
 constexpr float NEG_INF = -__builtin_huge_valf();
 
 __device__ __forceinline__ float4_t mfma(uint4 a, uint4 b, float4_t c) {
@@ -122,8 +135,18 @@ __device__ __forceinline__ int half_row(int e, int m) { return 8 * (m >> 2) + 4 
 //   [6400, 6656)  value scales: dword t < 32 = groups (0,1) of token t,
 //                 dword 32 + t = groups (2,3)
 constexpr int ST_K = 0, ST_V = 4096, ST_KS = 6144, ST_VS = 6400, ST_BYTES = 6656;
+// A fallback step (tokens 8j .. 8j+7 of a block) in the same stage:
+//   [0, 2048)     FP16 key rows: chunk e (1 KB), lane (s, dg, r) = lane
+//                 16s + 4dg + r: token 4e + r, channels [32dg + 8s, +8);
+//                 or the 8 key code rows, row-major [8][128] (1 KB)
+//   [2048, 4096)  FP16 value rows, row-major [8][128];
+//                 or value codes [128 channels][4 bytes] (tokens 8j .. 8j+7)
+//   [4096, 5120)  sink of the padding copies
+//   [6144, 6400)  key scales, dword 4t = token t (t < 8)
+//   [6400, 6656)  value scales, dword t = groups (0,1), 32 + t = (2,3)
+constexpr int FB_K = 0, FB_V = 2048, FB_SINK = 4096;
 constexpr int NSTAGE = 3;
-constexpr int DMA_PER_HALF = 8;  // 4 key + 2 value + 1 key-scale + 1 value-scale copies
+constexpr int DMA_PER_STEP = 8;  // copy instructions of every step (half or fallback step)
 
 // Copies of global memory into LDS that bypass the registers.  M0 holds the
 // wave-uniform LDS destination; lane l writes its bytes at M0 + l*size (16 B
@@ -172,30 +195,79 @@ __device__ __forceinline__ void issue_half(const DecodeArgs &a, int64_t bh, int6
     dma4(stage + ST_VS, a.c.v_scales + (row0 + 32 * u + l32) * 4 + 2 * (lane >> 5));
 }
 
-// Scores, online softmax and P.V of half u of one block for one wave, from the
-// stage in LDS or, for fallback parts, from the FP16 originals.  Scores are
-// kept in log2 units (sm * log2(e) folded into the per-token key factor) so
-// the softmax uses exp2.  State: m_run / l_run of head m (this lane's column;
-// l as this lane's share of the 8-token groups) and the P.V accumulators.
+// Issues the copies of fallback step j (tokens 8j .. 8j+7) of block `blk`
+// with fallback mask mk: FP16 rows for the parts whose bit is set, codes and
+// scales for the others, then padding copies up to DMA_PER_STEP (a dword of
+// the block's statistics into the sink).  Every source address lies inside the
+// block.
+__device__ __forceinline__ void issue_fb(const DecodeArgs &a, int64_t bh, int64_t blk, int j,
+                                         uint32_t mk, uint32_t stage, int lane) {
+    const int64_t row0 = bh * a.cap + blk * BLK + 8 * j;
+    const int t8 = lane & 7;
+    int n = 0;
+    if (mk & 1u) {
+        const int r = lane & 3, dg = (lane >> 2) & 3, st = lane >> 4;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) dma16(stage + FB_K + 1024 * e, a.c.k16 + (row0 + 4 * e + r) * D + 32 * dg + 8 * st);
+        n += 2;
+    } else {
+        dma16(stage + FB_K, a.c.k_codes + (row0 + (lane >> 3)) * D + 16 * t8);
+        dma2(stage + ST_KS, a.c.k_scales + row0 + t8);
+        n += 2;
+    }
+    if (mk & 2u) {
+#pragma unroll
+        for (int d = 0; d < 2; ++d) dma16(stage + FB_V + 1024 * d, a.c.v16 + (row0 + 4 * d + (lane >> 4)) * D + 8 * (lane & 15));
+        n += 2;
+    } else {
+        const uint8_t *vc = a.c.v_codes + (bh * a.nbc + blk) * (D * BLK / 2) + 4 * j;
+#pragma unroll
+        for (int d = 0; d < 2; ++d) dma4(stage + FB_V + 256 * d, vc + (64 * d + lane) * (BLK / 2));
+        dma4(stage + ST_VS, a.c.v_scales + (row0 + t8) * 4 + 2 * (lane >> 5));
+        n += 3;
+    }
+    const float *sink_src = a.c.k_err + bh * a.nbc + blk;
+    for (int i = 0; n < DMA_PER_STEP; ++i, ++n) dma4(stage + FB_SINK + 256 * i, sink_src);
+}
+
+// Scores, online softmax and P.V of one step for one wave, from its stage in
+// LDS.  A half (FB = false) covers 32 tokens of codes; a fallback step (FB =
+// true) covers 8 tokens, each tensor as FP16 rows (its bit in mk set) or as
+// codes, and its tokens take the positions 0..7 of a half.  nvalid: tokens of
+// the step before `length` (positions >= nvalid are masked).  Scores are kept
+// in log2 units (sm * log2(e) folded into the per-token key factor) so the
+// softmax uses exp2.  State: m_run / l_run of head m (this lane's column; l as
+// this lane's share of the 8-token groups) and the P.V accumulators.
 struct WaveState {
     float m_run, l_run;
     float4_t acc[8];
 };
 
-__device__ __forceinline__ void process_half(const DecodeArgs &a, const uint8_t *stage, int64_t bh,
-                                             int64_t blk, int u, uint32_t mk, const uint4 (&qb)[4],
-                                             float sml2, WaveState &w, int lane) {
+template <bool FB>
+__device__ __forceinline__ void process_step(const uint8_t *stage, uint32_t mk, int nvalid,
+                                             const uint4 (&qb)[4], float sml2, WaveState &w, int lane) {
     const int m = lane & 15, g4 = lane >> 4;
-    const int64_t row0 = bh * a.cap + blk * BLK + 32 * u;  // first token of the half
-    const int64_t left = a.length - (blk * BLK + 32 * u);
-    const int nvalid = (int)(left < 32 ? (left > 0 ? left : 0) : 32);  // valid tokens of the half
 
     // ---------------- Q.K^T: S^T[token][head] for the 2 subtiles
     float4_t sc[2];
-    if (!(mk & 1u)) {
+    if (FB && (mk & 1u)) {
+        // FP16 key rows: subtile e row r holds token 4e + (r & 3)
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            float4_t c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int st = 0; st < 4; ++st)
+                c = mfma(*reinterpret_cast<const uint4 *>(stage + FB_K + 1024 * e + 16 * (16 * st + 4 * g4 + (m & 3))),
+                         qb[st], c);
+            sc[e] = c * sml2;
+        }
+    } else {
         uint4 kt[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) kt[j] = *reinterpret_cast<const uint4 *>(stage + ST_K + j * 1024 + 16 * lane);
+        for (int j = 0; j < 4; ++j)
+            kt[j] = FB ? *reinterpret_cast<const uint4 *>(stage + FB_K + (4 * (j >> 1) + (m & 3)) * D + 32 * g4 +
+                                                           16 * (j & 1))
+                       : *reinterpret_cast<const uint4 *>(stage + ST_K + j * 1024 + 16 * lane);
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
             float4_t c = {0.f, 0.f, 0.f, 0.f};
@@ -214,28 +286,10 @@ __device__ __forceinline__ void process_half(const DecodeArgs &a, const uint8_t 
             sc[e][2] *= h2f(f.z & 0xFFFFu) * sml2;
             sc[e][3] *= h2f(f.w & 0xFFFFu) * sml2;
         }
-    } else {
-        // FP16 key rows straight from HBM: all 8 loads first, then the
-        // contractions, so the loads share one wait
-        const uint16_t *kr = a.c.k16 + row0 * D + 32 * g4;  // channels [32dg, 32dg+32)
-        uint4 kf[2][4];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            const uint4 *p = reinterpret_cast<const uint4 *>(kr + half_row(e, m) * D);
-#pragma unroll
-            for (int k = 0; k < 4; ++k) kf[e][k] = p[k];
-        }
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            float4_t c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int k = 0; k < 4; ++k) c = mfma(kf[e][k], qb[k], c);
-            sc[e] = c * sml2;
-        }
     }
 
-    // ---------------- online softmax of head m over this half
-    const int tk0 = 8 * g4;  // this lane's 8 tokens of the half: tk0 + 4e + i
+    // ---------------- online softmax of head m over this step
+    const int tk0 = 8 * g4;  // this lane's 8 positions of the half: tk0 + 4e + i
     float bmax = NEG_INF;
 #pragma unroll
     for (int e = 0; e < 2; ++e)
@@ -246,8 +300,8 @@ __device__ __forceinline__ void process_half(const DecodeArgs &a, const uint8_t 
         }
     bmax = max_across_rows(bmax);
     const float m_new = fmaxf(w.m_run, bmax);
-    // a half with no valid token (the tail of the last block) leaves the
-    // state unchanged: m_new may then still be -inf
+    // a step with no valid token leaves the state unchanged: m_new may then
+    // still be -inf
     const float alpha = (m_new == NEG_INF) ? 1.0f : __builtin_amdgcn_exp2f(w.m_run - m_new);
     float pv[2][4];
     float psum = 0.0f;
@@ -266,18 +320,45 @@ __device__ __forceinline__ void process_half(const DecodeArgs &a, const uint8_t 
     }
 
     // ---------------- P.V
-    // B operand (k-slot pairs): p of tokens (8kg + q, 8kg + 4 + q) of the half
+    // B operand (k-slot pairs): p of positions (8kg + q, 8kg + 4 + q)
     half2_t pp[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) pp[q] = __builtin_bit_cast(half2_t, pack_h2(pv[0][q], pv[1][q]));
-    if (!(mk & 2u)) {
-        // value codes of channel 16mt + m, tokens 8kg .. 8kg+7 of the half
+    if (FB && (mk & 2u)) {
+        // FP16 value rows: lane (m, kg = 0) gathers channel 16mt + m of the 8
+        // tokens; other lanes and positions >= nvalid give 0 (a stale row could
+        // hold NaN, and 0 * NaN would reach the accumulator)
+        const uint4 bop = make_uint4(__builtin_bit_cast(uint32_t, pp[0]), __builtin_bit_cast(uint32_t, pp[1]),
+                                     __builtin_bit_cast(uint32_t, pp[2]), __builtin_bit_cast(uint32_t, pp[3]));
+        // all 64 reads first (unconditional, inside the stage), then the
+        // selects, so that the reads share one wait
+        uint32_t v[8][8];
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) {
+            const uint16_t *col = reinterpret_cast<const uint16_t *>(stage + FB_V) + 16 * mt + m;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) v[mt][t] = col[t * D];
+        }
+        uint32_t keep = 0;  // bit t: position t holds a valid token for this lane
+#pragma unroll
+        for (int t = 0; t < 8; ++t) keep |= (g4 == 0 && t < nvalid) ? (1u << t) : 0u;
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) {
+            uint32_t r[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                r[q] = ((keep >> q) & 1u ? v[mt][q] : 0u) | (((keep >> (q + 4)) & 1u ? v[mt][q + 4] : 0u) << 16);
+            w.acc[mt] = mfma(make_uint4(r[0], r[1], r[2], r[3]), bop, w.acc[mt]);
+        }
+    } else {
+        // value codes of channel 16mt + m, positions 8kg .. 8kg+7
         uint32_t vt[8];
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt)
-            vt[mt] = *reinterpret_cast<const uint32_t *>(stage + ST_V + (mt >> 2) * 1024 +
-                                                         16 * (16 * (mt & 3) + m) + 4 * g4);
-        // scales of tokens 8kg + [0, 8): dwords of groups (0,1) and (2,3)
+            vt[mt] = FB ? *reinterpret_cast<const uint32_t *>(stage + FB_V + 4 * (16 * mt + m))
+                        : *reinterpret_cast<const uint32_t *>(stage + ST_V + (mt >> 2) * 1024 +
+                                                              16 * (16 * (mt & 3) + m) + 4 * g4);
+        // scales of positions 8kg + [0, 8): dwords of groups (0,1) and (2,3)
         const int t0 = 8 * g4;
         const uint4 a01 = *reinterpret_cast<const uint4 *>(stage + ST_VS + 4 * t0);
         const uint4 b01 = *reinterpret_cast<const uint4 *>(stage + ST_VS + 4 * (t0 + 4));
@@ -286,8 +367,9 @@ __device__ __forceinline__ void process_half(const DecodeArgs &a, const uint8_t 
         uint32_t lo_a[4] = {a01.x, a01.y, a01.z, a01.w}, lo_b[4] = {b01.x, b01.y, b01.z, b01.w};
         uint32_t hi_a[4] = {a23.x, a23.y, a23.z, a23.w}, hi_b[4] = {b23.x, b23.y, b23.z, b23.w};
         if (nvalid < 32) {
-            // tokens past `length` carry stale scales: zero them (their p is
-            // 0, and 0 * NaN would reach the accumulator)
+            // positions past `length` (or past a fallback step's 8 tokens)
+            // carry stale scales: zero them (their p is 0, and 0 * NaN would
+            // reach the accumulator)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 if (t0 + q >= nvalid) lo_a[q] = hi_a[q] = 0u;
@@ -300,7 +382,7 @@ __device__ __forceinline__ void process_half(const DecodeArgs &a, const uint8_t 
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const uint32_t wa = (gg < 2) ? lo_a[q] : hi_a[q], wb = (gg < 2) ? lo_b[q] : hi_b[q];
-                // (scale of token q, scale of token q+4) for group gg
+                // (scale of position q, scale of position q+4) for group gg
                 const uint32_t sp = (gg & 1) ? __builtin_amdgcn_perm(wb, wa, 0x07060302u)
                                              : __builtin_amdgcn_perm(wb, wa, 0x05040100u);
                 // p * s_v in fp16: one rounding of p, one of the product
@@ -310,49 +392,29 @@ __device__ __forceinline__ void process_half(const DecodeArgs &a, const uint8_t 
             w.acc[2 * gg] = mfma(i4x8_to_h8(vt[2 * gg]), bop, w.acc[2 * gg]);
             w.acc[2 * gg + 1] = mfma(i4x8_to_h8(vt[2 * gg + 1]), bop, w.acc[2 * gg + 1]);
         }
-    } else {
-        const uint4 bop = make_uint4(__builtin_bit_cast(uint32_t, pp[0]), __builtin_bit_cast(uint32_t, pp[1]),
-                                     __builtin_bit_cast(uint32_t, pp[2]), __builtin_bit_cast(uint32_t, pp[3]));
-        const int tb = 8 * g4;  // tokens tb + q and tb + 4 + q of the half
-        // gather all 64 values first (one shared wait), then the 8
-        // contractions; rows past `length` are still inside the block's
-        // storage: load them, then zero them (a stale value could be NaN, and
-        // 0 * NaN would reach the accumulator)
-        uint32_t lo[8][4], hi[8][4];
-#pragma unroll
-        for (int mt = 0; mt < 8; ++mt) {
-            const uint16_t *vcol = a.c.v16 + row0 * D + 16 * mt + m;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                lo[mt][q] = vcol[(tb + q) * D];
-                hi[mt][q] = vcol[(tb + 4 + q) * D];
-            }
-        }
-#pragma unroll
-        for (int mt = 0; mt < 8; ++mt) {
-            uint32_t r[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                r[q] = ((tb + q < nvalid) ? lo[mt][q] : 0u) | (((tb + 4 + q < nvalid) ? hi[mt][q] : 0u) << 16);
-            w.acc[mt] = mfma(make_uint4(r[0], r[1], r[2], r[3]), bop, w.acc[mt]);
-        }
     }
 }
 
 }  // namespace
 
-// Largest per-split block count the mask table of this kernel holds.
-constexpr int MFMA_MAX_BPS = 1024;
+// Entries of the table of blocks that one workgroup's share of steps touches:
+// at most half its steps (every block has two or more) plus the two blocks
+// cut by its range ends.
+constexpr int TBL = 4 * MFMA_MAX_BPS + 8;
 
-__global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
-    // 8 waves x 3 stages x 6656 B = 159,744 B of ring.  Before the stream
-    // starts, wave 0's stage 2 holds the query rows; after it ends, the ring
-    // holds the wave merge.
+__global__ __launch_bounds__(NW * 64, 2) void decode_mfma_kernel(DecodeArgs a) {
+    // NW waves x 3 stages x 6656 B of ring.  Before the stream starts, wave
+    // 0's stage 2 holds the query rows and the ring from wave 1 on the masks
+    // of every block of (b, kvh); after it ends, the ring holds the wave merge.
     __shared__ __attribute__((aligned(16))) uint8_t ring[NW][NSTAGE][ST_BYTES];
+    __shared__ int16_t toff_lds[TBL];  // share-local index of each listed block's first step
+    __shared__ uint8_t tmk_lds[TBL];   // its fallback mask
     __shared__ float qn_lds[16];
-    __shared__ uint8_t mask_lds[MFMA_MAX_BPS];
     __shared__ float wm[NW][16], wl[NW][16];
+    __shared__ int wsum_lds[NW];
+    __shared__ int blo_lds, ntbl_lds;
     uint16_t(*q_lds)[D] = reinterpret_cast<uint16_t(*)[D]>(&ring[0][2][0]);
+    uint8_t *maskb = &ring[1][0][0];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept scalar
@@ -361,24 +423,127 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
     const int64_t kvh = blockIdx.y, b = blockIdx.z;
     const int64_t bh = b * a.hkv + kvh;
     const int g = a.g;
-    const int64_t blk0 = (int64_t)split * a.bps;
-    const int64_t blk1 = blk0 + a.bps < a.nb ? blk0 + a.bps : a.nb;
-
-    // this wave's blocks: first, first + NW, ..., streamed as halves
-    // k = 0 .. 2*nblk-1 (block k/2, half k%2); half k lives in stage k % 3
-    const int64_t first = blk0 + wave;
-    const int64_t nblk = first < blk1 ? (blk1 - 1 - first) / NW + 1 : 0;
-    const int64_t nhalf = 2 * nblk;
-    const uint32_t ring0 = (uint32_t)(uintptr_t)&ring[wave][0][0];
-    auto stage_addr = [&](int64_t k) { return ring0 + (uint32_t)((k % NSTAGE) * ST_BYTES); };
-    auto issue = [&](int64_t k) { issue_half(a, bh, first + (k >> 1) * NW, (int)(k & 1), stage_addr(k), lane); };
-    // start streaming before the query and mask set-up so it overlaps them
-    // (stages 0 and 1 only: stage 2 of wave 0 holds the query rows for now)
-    if (nhalf > 0) issue(0);
-    if (nhalf > 1) issue(1);
+    const int nb = (int)a.nb;
+    constexpr int NT = NW * 64;
 
     const float qn = load_q_and_norm(a.q, b * a.hq + kvh * g, g, q_lds, qn_lds);
-    compute_masks(a, bh, blk0, blk1, qn, mask_lds);
+
+    // masks of every block of (b, kvh); mask_out receives this workgroup's
+    // home range of bps blocks
+    {
+        const int64_t h0 = (int64_t)split * a.bps, h1 = h0 + a.bps;
+        for (int i = tid; i < nb; i += NT) {
+            const int64_t si = bh * a.nbc + i;
+            const uint32_t mk = block_mask(a.sm, qn, a.c.k_err[si], a.c.v_err[si], a.tau_k, a.tau_v);
+            maskb[i] = (uint8_t)mk;
+            if (a.mask_out && i >= h0 && i < h1) a.mask_out[bh * a.nb + i] = (uint8_t)mk;
+        }
+    }
+    __syncthreads();
+
+    // Work of (b, kvh) in steps: 2 per certified block (its halves), 8 per
+    // fallback block (its 8-token steps).  Split s takes steps [r0, r1) of the
+    // sequence in block order, so splits carry equal work however the
+    // fallback blocks fall.  Thread t sums the contiguous blocks [t*c, t*c+c).
+    const int c = (nb + NT - 1) / NT;
+    const int i0 = tid * c < nb ? tid * c : nb, i1 = i0 + c < nb ? i0 + c : nb;
+    int mysum = 0;
+    for (int i = i0; i < i1; ++i) mysum += maskb[i] ? 8 : 2;
+    int incl = mysum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_up(incl, o);
+        if (lane >= o) incl += v;
+    }
+    if (lane == 63) wsum_lds[wave] = incl;
+    __syncthreads();
+    int before = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        const int v = wsum_lds[w];
+        before += w < wave ? v : 0;
+        total += v;
+    }
+    const int excl = before + incl - mysum;  // steps before block i0
+    const int r0 = (int)((int64_t)split * total / a.splits);
+    const int r1 = (int)((int64_t)(split + 1) * total / a.splits);
+    // first and last block of the share, then the table
+    {
+        int p = excl;
+        for (int i = i0; i < i1; ++i) {
+            const int w = maskb[i] ? 8 : 2;
+            if (p <= r0 && r0 < p + w) blo_lds = i;
+            if (p <= r1 - 1 && r1 - 1 < p + w) ntbl_lds = i;  // last block, made a count below
+            p += w;
+        }
+    }
+    __syncthreads();
+    const int blo = blo_lds;
+    {
+        int p = excl;
+        for (int i = i0; i < i1; ++i) {
+            const uint32_t mk = maskb[i];
+            const int w = mk ? 8 : 2;
+            if (p < r1 && p + w > r0) {
+                toff_lds[i - blo] = (int16_t)(p - r0);
+                tmk_lds[i - blo] = (uint8_t)mk;
+            }
+            p += w;
+        }
+    }
+    __syncthreads();
+    const int ntbl = r1 > r0 ? ntbl_lds - blo + 1 : 0;
+
+    // This wave's steps are the share's steps wave, wave + NW, ...  A step is
+    // found in the table with a 64-entry window held one entry per lane: the
+    // listed block is the last one whose first step is at or before it.
+    const int nshare = r1 - r0;
+    const int64_t nsteps = nshare > wave ? (nshare - 1 - wave) / NW + 1 : 0;
+    struct Window {
+        int jb;        // table index of lane 0
+        int off;       // this lane's entry: first step, mask
+        uint32_t mk;
+    };
+    auto load_window = [&](Window &wn, int jb) {
+        wn.jb = jb;
+        const int j = jb + lane;
+        wn.off = j < ntbl ? toff_lds[j] : 0x7fffffff;
+        wn.mk = j < ntbl ? tmk_lds[j] : 0u;
+    };
+    // step k of this wave -> block, sub-step (half or fallback step), mask
+    auto find = [&](Window &wn, int64_t k, int64_t &blk, int &sub, uint32_t &mk) {
+        const int t = wave + NW * (int)k;
+        uint64_t bal = __builtin_amdgcn_ballot_w64(wn.off <= t);
+        while ((bal >> 63) && wn.jb + 64 < ntbl) {
+            load_window(wn, wn.jb + 63);
+            bal = __builtin_amdgcn_ballot_w64(wn.off <= t);
+        }
+        const int idx = 63 - __builtin_clzll(bal);
+        blk = blo + wn.jb + idx;
+        sub = t - __builtin_amdgcn_readlane(wn.off, idx);
+        mk = __builtin_amdgcn_readlane(wn.mk, idx);
+    };
+    Window iwin, pwin;  // issue and process cursors
+    load_window(iwin, 0);
+    pwin = iwin;
+    const uint32_t ring0 = (uint32_t)(uintptr_t)&ring[wave][0][0];
+    uint32_t istage = 0;  // stage of the next issue
+    auto issue = [&](int64_t k) {
+        int64_t blk;
+        int sub;
+        uint32_t mk;
+        find(iwin, k, blk, sub, mk);
+        const uint32_t st = ring0 + istage * ST_BYTES;
+        if (mk)
+            issue_fb(a, bh, blk, sub, mk, st, lane);
+        else
+            issue_half(a, bh, blk, sub, st, lane);
+        istage = istage == NSTAGE - 1 ? 0 : istage + 1;
+    };
+    // stages 0 and 1 only: stage 2 of wave 0 still holds the query rows (the
+    // masks are no longer needed)
+    if (nsteps > 0) issue(0);
+    if (nsteps > 1) issue(1);
 
     // B operands of Q.K^T: lane (n = head, dg) holds q[n][32dg + 8s .. +8] at step s
     uint4 qb[4];
@@ -393,27 +558,38 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) ws.acc[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-    // Before computing half k the copies of half k+2 are issued; waiting until
-    // at most the copies issued after half k's (0, 1 or 2 halves' worth) are
-    // outstanding makes half k resident.  Any other load issued in between
-    // only makes the wait stronger.
+    // Before computing step k the copies of step k+2 are issued; waiting until
+    // at most the copies issued after step k's (0, 1 or 2 steps' worth, 8
+    // instructions each) are outstanding makes step k resident.  Any other
+    // load issued in between only makes the wait stronger.
     auto step = [&](int64_t k, int s) {
-        if (k + 2 < nhalf) issue(k + 2);
-        const int64_t after = (nhalf - 1 - k) < 2 ? (nhalf - 1 - k) : 2;
+        if (k + 2 < nsteps) issue(k + 2);
+        const int64_t after = (nsteps - 1 - k) < 2 ? (nsteps - 1 - k) : 2;
         if (after == 2)
-            wait_vmcnt<2 * DMA_PER_HALF>();
+            wait_vmcnt<2 * DMA_PER_STEP>();
         else if (after == 1)
-            wait_vmcnt<DMA_PER_HALF>();
+            wait_vmcnt<DMA_PER_STEP>();
         else
             wait_vmcnt<0>();
-        const int64_t blk = first + (k >> 1) * NW;
-        process_half(a, &ring[wave][s][0], bh, blk, (int)(k & 1),
-                     __builtin_amdgcn_readfirstlane(mask_lds[blk - blk0]), qb, sml2, ws, lane);
+        int64_t blk;
+        int sub;
+        uint32_t mk;
+        find(pwin, k, blk, sub, mk);
+        const uint8_t *stage = &ring[wave][s][0];
+        if (mk == 0u) {
+            const int64_t left = a.length - (blk * BLK + 32 * sub);
+            const int nvalid = (int)(left < 32 ? (left > 0 ? left : 0) : 32);
+            if (nvalid > 0) process_step<false>(stage, 0u, nvalid, qb, sml2, ws, lane);
+        } else {
+            const int64_t left = a.length - (blk * BLK + 8 * sub);
+            const int nvalid = (int)(left < 8 ? (left > 0 ? left : 0) : 8);
+            if (nvalid > 0) process_step<true>(stage, mk, nvalid, qb, sml2, ws, lane);
+        }
     };
-    for (int64_t k = 0; k < nhalf; k += NSTAGE) {
+    for (int64_t k = 0; k < nsteps; k += NSTAGE) {
         step(k, 0);
-        if (k + 1 < nhalf) step(k + 1, 1);
-        if (k + 2 < nhalf) step(k + 2, 2);
+        if (k + 1 < nsteps) step(k + 1, 1);
+        if (k + 2 < nsteps) step(k + 2, 2);
     }
 
     // ---------------- merge waves, then splits
@@ -441,7 +617,7 @@ bool mfma_supports(int g) { return g >= 1 && g <= 16; }
 
 hipError_t launch_decode_mfma(const DecodeArgs &a, int batch, hipStream_t s) {
     dim3 grid((unsigned)a.splits, (unsigned)a.hkv, (unsigned)batch);
-    hipLaunchKernelGGL(decode_mfma_kernel, grid, dim3(512), 0, s, a);
+    hipLaunchKernelGGL(decode_mfma_kernel, grid, dim3(NW * 64), 0, s, a);
     hipError_t e = hipGetLastError();
     return e != hipSuccess ? e : launch_merge(a, batch, s);
 }

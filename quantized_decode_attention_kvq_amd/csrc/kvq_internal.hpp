@@ -56,6 +56,7 @@ struct DecodeArgs {
 // Upper limits that size the workspace and LDS tables.
 constexpr int MAX_SPLITS = 128;
 constexpr int MAX_BPS = 1024;  // blocks per split (mask table in LDS)
+constexpr int MFMA_MAX_BPS = 128;  // blocks per split of the matrix-core kernel (block table in LDS)
 
 hipError_t launch_append(const AppendArgs &a, int batch, int64_t nblk, hipStream_t s);
 hipError_t launch_bounds(const BoundsArgs &a, int batch, hipStream_t s);
