@@ -135,16 +135,16 @@ __device__ __forceinline__ int half_row(int e, int m) { return 8 * (m >> 2) + 4 
 //   [6400, 6656)  value scales: dword t < 32 = groups (0,1) of token t,
 //                 dword 32 + t = groups (2,3)
 constexpr int ST_K = 0, ST_V = 4096, ST_KS = 6144, ST_VS = 6400, ST_BYTES = 6656;
-// A fallback step (tokens 8j .. 8j+7 of a block) in the same stage:
-//   [0, 2048)     FP16 key rows: chunk e (1 KB), lane (s, dg, r) = lane
-//                 16s + 4dg + r: token 4e + r, channels [32dg + 8s, +8);
-//                 or the 8 key code rows, row-major [8][128] (1 KB)
-//   [2048, 4096)  FP16 value rows, row-major [8][128];
-//                 or value codes [128 channels][4 bytes] (tokens 8j .. 8j+7)
-//   [4096, 5120)  sink of the padding copies
-//   [6144, 6400)  key scales, dword 4t = token t (t < 8)
-//   [6400, 6656)  value scales, dword t = groups (0,1), 32 + t = (2,3)
-constexpr int FB_K = 0, FB_V = 2048, FB_SINK = 4096;
+// A fallback step (tokens 8j .. 8j+7 of a block, inside half u = j/4 at
+// positions 8(j%4) .. 8(j%4)+7) uses the same stage: a part served from the
+// codes is copied exactly as for half u (only the step's positions are used);
+// a part served from FP16 rows takes
+//   keys   [0, 2048): chunk e (1 KB), lane (s, dg, r) = lane 16s + 4dg + r:
+//          token 4e + r of the step, channels [32dg + 8s, +8);
+//   values [4096, 6144): the step's 8 rows, row-major [8][128];
+// and the copies are padded up to 8 with dwords of the block's statistics
+// into a region the step leaves unused.
+constexpr int FB_K16 = 0, FB_V16 = 4096;
 constexpr int NSTAGE = 3;
 constexpr int DMA_PER_STEP = 8;  // copy instructions of every step (half or fallback step)
 
@@ -176,98 +176,108 @@ __device__ __forceinline__ void wait_vmcnt() {
     asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
 }
 
-// Issues the copies of half u of block `blk` of (b, kvh) into the stage at
-// LDS byte address `stage` (wave-uniform).  Every source address lies inside
-// the block.
-__device__ __forceinline__ void issue_half(const DecodeArgs &a, int64_t bh, int64_t blk, int u,
-                                           uint32_t stage, int lane) {
+// Copies of the code parts of half u: keys (4 chunks + scales, 5 copies) and
+// values (2 chunks + scales, 3 copies).
+__device__ __forceinline__ void issue_keys(const DecodeArgs &a, int64_t row0, int u, uint32_t stage, int lane) {
     const int m = lane & 15, dg = lane >> 4, l32 = lane & 31;
-    const int64_t row0 = bh * a.cap + blk * BLK;
     const int8_t *kc = a.c.k_codes + (row0 + 32 * u) * D + 32 * dg;
 #pragma unroll
     for (int e = 0; e < 2; ++e)
 #pragma unroll
         for (int h = 0; h < 2; ++h) dma16(stage + ST_K + (2 * e + h) * 1024, kc + half_row(e, m) * D + 16 * h);
+    dma2(stage + ST_KS, a.c.k_scales + row0 + 32 * u + l32);
+}
+__device__ __forceinline__ void issue_values(const DecodeArgs &a, int64_t bh, int64_t blk, int64_t row0, int u,
+                                             uint32_t stage, int lane) {
+    const int l32 = lane & 31;
     const uint8_t *vc = a.c.v_codes + (bh * a.nbc + blk) * (D * BLK / 2) + lane * (BLK / 2) + 16 * u;
     dma16(stage + ST_V, vc);
     dma16(stage + ST_V + 1024, vc + 64 * (BLK / 2));
-    dma2(stage + ST_KS, a.c.k_scales + row0 + 32 * u + l32);
     dma4(stage + ST_VS, a.c.v_scales + (row0 + 32 * u + l32) * 4 + 2 * (lane >> 5));
 }
 
-// Issues the copies of fallback step j (tokens 8j .. 8j+7) of block `blk`
-// with fallback mask mk: FP16 rows for the parts whose bit is set, codes and
-// scales for the others, then padding copies up to DMA_PER_STEP (a dword of
-// the block's statistics into the sink).  Every source address lies inside the
-// block.
+// Issues the copies of half u of block `blk` of (b, kvh) into the stage at
+// LDS byte address `stage` (wave-uniform).  Every source address lies inside
+// the block.
+__device__ __forceinline__ void issue_half(const DecodeArgs &a, int64_t bh, int64_t blk, int u,
+                                           uint32_t stage, int lane) {
+    const int64_t row0 = bh * a.cap + blk * BLK;
+    issue_keys(a, row0, u, stage, lane);
+    issue_values(a, bh, blk, row0, u, stage, lane);
+}
+
+// Issues the 8 copies of fallback step j (tokens 8j .. 8j+7) of block `blk`
+// with fallback mask mk (nonzero).  Every source address lies inside the block.
 __device__ __forceinline__ void issue_fb(const DecodeArgs &a, int64_t bh, int64_t blk, int j,
                                          uint32_t mk, uint32_t stage, int lane) {
-    const int64_t row0 = bh * a.cap + blk * BLK + 8 * j;
-    const int t8 = lane & 7;
-    int n = 0;
+    const int64_t row0 = bh * a.cap + blk * BLK;  // first token of the block
+    const int64_t rs = row0 + 8 * j;              // first token of the step
+    const int u = j >> 2;
+    const float *pad = a.c.k_err + bh * a.nbc + blk;
     if (mk & 1u) {
         const int r = lane & 3, dg = (lane >> 2) & 3, st = lane >> 4;
 #pragma unroll
-        for (int e = 0; e < 2; ++e) dma16(stage + FB_K + 1024 * e, a.c.k16 + (row0 + 4 * e + r) * D + 32 * dg + 8 * st);
-        n += 2;
+        for (int e = 0; e < 2; ++e) dma16(stage + FB_K16 + 1024 * e, a.c.k16 + (rs + 4 * e + r) * D + 32 * dg + 8 * st);
     } else {
-        dma16(stage + FB_K, a.c.k_codes + (row0 + (lane >> 3)) * D + 16 * t8);
-        dma2(stage + ST_KS, a.c.k_scales + row0 + t8);
-        n += 2;
+        issue_keys(a, row0, u, stage, lane);
     }
     if (mk & 2u) {
 #pragma unroll
-        for (int d = 0; d < 2; ++d) dma16(stage + FB_V + 1024 * d, a.c.v16 + (row0 + 4 * d + (lane >> 4)) * D + 8 * (lane & 15));
-        n += 2;
+        for (int d = 0; d < 2; ++d) dma16(stage + FB_V16 + 1024 * d, a.c.v16 + (rs + 4 * d + (lane >> 4)) * D + 8 * (lane & 15));
     } else {
-        const uint8_t *vc = a.c.v_codes + (bh * a.nbc + blk) * (D * BLK / 2) + 4 * j;
-#pragma unroll
-        for (int d = 0; d < 2; ++d) dma4(stage + FB_V + 256 * d, vc + (64 * d + lane) * (BLK / 2));
-        dma4(stage + ST_VS, a.c.v_scales + (row0 + t8) * 4 + 2 * (lane >> 5));
-        n += 3;
+        issue_values(a, bh, blk, row0, u, stage, lane);
     }
-    const float *sink_src = a.c.k_err + bh * a.nbc + blk;
-    for (int i = 0; n < DMA_PER_STEP; ++i, ++n) dma4(stage + FB_SINK + 256 * i, sink_src);
+    // padding: K16 + value codes (5 copies) -> 3 into the unused key-code
+    // region; K16 + V16 (4) -> 4 there; key codes + V16 (7) -> 1 into the
+    // unused value-scale region
+    if ((mk & 1u) && !(mk & 2u)) {
+#pragma unroll
+        for (int i = 0; i < 3; ++i) dma4(stage + 2048 + 256 * i, pad);
+    } else if (mk & 1u) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dma4(stage + 2048 + 256 * i, pad);
+    } else {
+        dma4(stage + ST_VS, pad);
+    }
 }
 
 // Scores, online softmax and P.V of one step for one wave, from its stage in
-// LDS.  A half (FB = false) covers 32 tokens of codes; a fallback step (FB =
-// true) covers 8 tokens, each tensor as FP16 rows (its bit in mk set) or as
-// codes, and its tokens take the positions 0..7 of a half.  nvalid: tokens of
-// the step before `length` (positions >= nvalid are masked).  Scores are kept
-// in log2 units (sm * log2(e) folded into the per-token key factor) so the
+// LDS.  The step covers positions [p_lo, p_hi) of a 32-token half: a whole
+// certified half (mk = 0, [0, valid tokens)), or the 8 positions of a fallback
+// step, whose parts with a bit in mk come as FP16 rows.  Scores are kept in
+// log2 units (sm * log2(e) folded into the per-token key factor) so the
 // softmax uses exp2.  State: m_run / l_run of head m (this lane's column; l as
-// this lane's share of the 8-token groups) and the P.V accumulators.
+// this lane's share of the 8-position groups) and the P.V accumulators.
 struct WaveState {
     float m_run, l_run;
     float4_t acc[8];
 };
 
-template <bool FB>
-__device__ __forceinline__ void process_step(const uint8_t *stage, uint32_t mk, int nvalid,
-                                             const uint4 (&qb)[4], float sml2, WaveState &w, int lane) {
+template <typename Mid>
+__device__ __forceinline__ void process_step(const uint8_t *stage, uint32_t mk, int p_lo, int p_hi,
+                                             const uint4 (&qb)[4], float sml2, WaveState &w, int lane,
+                                             Mid &&mid) {
     const int m = lane & 15, g4 = lane >> 4;
+    const bool partial = p_lo > 0 || p_hi < 32;  // wave-uniform
 
-    // ---------------- Q.K^T: S^T[token][head] for the 2 subtiles
+    // ---------------- Q.K^T: S^T[position][head] for the 2 subtiles
     float4_t sc[2];
-    if (FB && (mk & 1u)) {
-        // FP16 key rows: subtile e row r holds token 4e + (r & 3)
+    if (mk & 1u) {
+        // FP16 key rows: subtile e row r holds token 4e + (r & 3) of the step
+        // (the rows of group p_lo/8 are the step's positions; others masked)
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
             float4_t c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int st = 0; st < 4; ++st)
-                c = mfma(*reinterpret_cast<const uint4 *>(stage + FB_K + 1024 * e + 16 * (16 * st + 4 * g4 + (m & 3))),
+                c = mfma(*reinterpret_cast<const uint4 *>(stage + FB_K16 + 1024 * e + 16 * (16 * st + 4 * g4 + (m & 3))),
                          qb[st], c);
             sc[e] = c * sml2;
         }
     } else {
         uint4 kt[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            kt[j] = FB ? *reinterpret_cast<const uint4 *>(stage + FB_K + (4 * (j >> 1) + (m & 3)) * D + 32 * g4 +
-                                                           16 * (j & 1))
-                       : *reinterpret_cast<const uint4 *>(stage + ST_K + j * 1024 + 16 * lane);
+        for (int j = 0; j < 4; ++j) kt[j] = *reinterpret_cast<const uint4 *>(stage + ST_K + j * 1024 + 16 * lane);
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
             float4_t c = {0.f, 0.f, 0.f, 0.f};
@@ -277,7 +287,7 @@ __device__ __forceinline__ void process_step(const uint8_t *stage, uint32_t mk, 
             c = mfma(i8x8_to_h8(kt[2 * e + 1].z, kt[2 * e + 1].w), qb[3], c);
             sc[e] = c;
         }
-        // key scales of tokens 8*g4 + 4e + i of the half (one dword per token)
+        // key scales of positions 8*g4 + 4e + i (one dword per token)
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
             const uint4 f = *reinterpret_cast<const uint4 *>(stage + ST_KS + 4 * (8 * g4 + 4 * e));
@@ -288,20 +298,25 @@ __device__ __forceinline__ void process_step(const uint8_t *stage, uint32_t mk, 
         }
     }
 
+    mid();
+
     // ---------------- online softmax of head m over this step
-    const int tk0 = 8 * g4;  // this lane's 8 positions of the half: tk0 + 4e + i
+    const int tk0 = 8 * g4;  // this lane's 8 positions: tk0 + 4e + i
+    if (partial) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (tk0 + 4 * e + i < p_lo || tk0 + 4 * e + i >= p_hi) sc[e][i] = NEG_INF;
+    }
     float bmax = NEG_INF;
 #pragma unroll
     for (int e = 0; e < 2; ++e)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if (tk0 + 4 * e + i >= nvalid) sc[e][i] = NEG_INF;
-            bmax = fmaxf(bmax, sc[e][i]);
-        }
+        for (int i = 0; i < 4; ++i) bmax = fmaxf(bmax, sc[e][i]);
     bmax = max_across_rows(bmax);
     const float m_new = fmaxf(w.m_run, bmax);
-    // a step with no valid token leaves the state unchanged: m_new may then
-    // still be -inf
+    // a step with no finite score so far leaves m_new at -inf
     const float alpha = (m_new == NEG_INF) ? 1.0f : __builtin_amdgcn_exp2f(w.m_run - m_new);
     float pv[2][4];
     float psum = 0.0f;
@@ -324,24 +339,23 @@ __device__ __forceinline__ void process_step(const uint8_t *stage, uint32_t mk, 
     half2_t pp[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) pp[q] = __builtin_bit_cast(half2_t, pack_h2(pv[0][q], pv[1][q]));
-    if (FB && (mk & 2u)) {
-        // FP16 value rows: lane (m, kg = 0) gathers channel 16mt + m of the 8
-        // tokens; other lanes and positions >= nvalid give 0 (a stale row could
-        // hold NaN, and 0 * NaN would reach the accumulator)
+    if (mk & 2u) {
+        // FP16 value rows: lane (m, kg = p_lo/8) gathers channel 16mt + m of
+        // the step's tokens; other lanes and tokens past p_hi give 0 (a stale
+        // row could hold NaN, and 0 * NaN would reach the accumulator).  All
+        // 64 reads first, then the selects, so that the reads share one wait.
         const uint4 bop = make_uint4(__builtin_bit_cast(uint32_t, pp[0]), __builtin_bit_cast(uint32_t, pp[1]),
                                      __builtin_bit_cast(uint32_t, pp[2]), __builtin_bit_cast(uint32_t, pp[3]));
-        // all 64 reads first (unconditional, inside the stage), then the
-        // selects, so that the reads share one wait
         uint32_t v[8][8];
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) {
-            const uint16_t *col = reinterpret_cast<const uint16_t *>(stage + FB_V) + 16 * mt + m;
+            const uint16_t *col = reinterpret_cast<const uint16_t *>(stage + FB_V16) + 16 * mt + m;
 #pragma unroll
             for (int t = 0; t < 8; ++t) v[mt][t] = col[t * D];
         }
-        uint32_t keep = 0;  // bit t: position t holds a valid token for this lane
+        uint32_t keep = 0;  // bit t: token t of the step is valid in this lane
 #pragma unroll
-        for (int t = 0; t < 8; ++t) keep |= (g4 == 0 && t < nvalid) ? (1u << t) : 0u;
+        for (int t = 0; t < 8; ++t) keep |= (tk0 == p_lo && p_lo + t < p_hi) ? (1u << t) : 0u;
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) {
             uint32_t r[4];
@@ -355,25 +369,23 @@ __device__ __forceinline__ void process_step(const uint8_t *stage, uint32_t mk, 
         uint32_t vt[8];
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt)
-            vt[mt] = FB ? *reinterpret_cast<const uint32_t *>(stage + FB_V + 4 * (16 * mt + m))
-                        : *reinterpret_cast<const uint32_t *>(stage + ST_V + (mt >> 2) * 1024 +
-                                                              16 * (16 * (mt & 3) + m) + 4 * g4);
+            vt[mt] = *reinterpret_cast<const uint32_t *>(stage + ST_V + (mt >> 2) * 1024 + 16 * (16 * (mt & 3) + m) +
+                                                         4 * g4);
         // scales of positions 8kg + [0, 8): dwords of groups (0,1) and (2,3)
-        const int t0 = 8 * g4;
-        const uint4 a01 = *reinterpret_cast<const uint4 *>(stage + ST_VS + 4 * t0);
-        const uint4 b01 = *reinterpret_cast<const uint4 *>(stage + ST_VS + 4 * (t0 + 4));
-        const uint4 a23 = *reinterpret_cast<const uint4 *>(stage + ST_VS + 128 + 4 * t0);
-        const uint4 b23 = *reinterpret_cast<const uint4 *>(stage + ST_VS + 128 + 4 * (t0 + 4));
+        const uint4 a01 = *reinterpret_cast<const uint4 *>(stage + ST_VS + 4 * tk0);
+        const uint4 b01 = *reinterpret_cast<const uint4 *>(stage + ST_VS + 4 * (tk0 + 4));
+        const uint4 a23 = *reinterpret_cast<const uint4 *>(stage + ST_VS + 128 + 4 * tk0);
+        const uint4 b23 = *reinterpret_cast<const uint4 *>(stage + ST_VS + 128 + 4 * (tk0 + 4));
         uint32_t lo_a[4] = {a01.x, a01.y, a01.z, a01.w}, lo_b[4] = {b01.x, b01.y, b01.z, b01.w};
         uint32_t hi_a[4] = {a23.x, a23.y, a23.z, a23.w}, hi_b[4] = {b23.x, b23.y, b23.z, b23.w};
-        if (nvalid < 32) {
-            // positions past `length` (or past a fallback step's 8 tokens)
-            // carry stale scales: zero them (their p is 0, and 0 * NaN would
+        if (partial) {
+            // positions outside the step carry scales of other tokens (stale
+            // past `length`): zero them (their p is 0, and 0 * NaN would
             // reach the accumulator)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                if (t0 + q >= nvalid) lo_a[q] = hi_a[q] = 0u;
-                if (t0 + 4 + q >= nvalid) lo_b[q] = hi_b[q] = 0u;
+                if (tk0 + q < p_lo || tk0 + q >= p_hi) lo_a[q] = hi_a[q] = 0u;
+                if (tk0 + 4 + q < p_lo || tk0 + 4 + q >= p_hi) lo_b[q] = hi_b[q] = 0u;
             }
         }
 #pragma unroll
@@ -426,18 +438,31 @@ __global__ __launch_bounds__(NW * 64, 2) void decode_mfma_kernel(DecodeArgs a) {
     const int nb = (int)a.nb;
     constexpr int NT = NW * 64;
 
+    // block statistics of the first PF * NT blocks, fetched while the query
+    // rows load
+    constexpr int PF = 4;
+    float ke[PF], ve[PF];
+#pragma unroll
+    for (int r = 0; r < PF; ++r) {
+        const int i = tid + r * NT;
+        ke[r] = i < nb ? a.c.k_err[bh * a.nbc + i] : 0.0f;
+        ve[r] = i < nb ? a.c.v_err[bh * a.nbc + i] : 0.0f;
+    }
     const float qn = load_q_and_norm(a.q, b * a.hq + kvh * g, g, q_lds, qn_lds);
 
     // masks of every block of (b, kvh); mask_out receives this workgroup's
     // home range of bps blocks
     {
         const int64_t h0 = (int64_t)split * a.bps, h1 = h0 + a.bps;
-        for (int i = tid; i < nb; i += NT) {
-            const int64_t si = bh * a.nbc + i;
-            const uint32_t mk = block_mask(a.sm, qn, a.c.k_err[si], a.c.v_err[si], a.tau_k, a.tau_v);
+        auto put = [&](int i, float kerr, float verr) {
+            const uint32_t mk = block_mask(a.sm, qn, kerr, verr, a.tau_k, a.tau_v);
             maskb[i] = (uint8_t)mk;
             if (a.mask_out && i >= h0 && i < h1) a.mask_out[bh * a.nb + i] = (uint8_t)mk;
-        }
+        };
+#pragma unroll
+        for (int r = 0; r < PF; ++r)
+            if (tid + r * NT < nb) put(tid + r * NT, ke[r], ve[r]);
+        for (int i = tid + PF * NT; i < nb; i += NT) put(i, a.c.k_err[bh * a.nbc + i], a.c.v_err[bh * a.nbc + i]);
     }
     __syncthreads();
 
@@ -563,28 +588,29 @@ __global__ __launch_bounds__(NW * 64, 2) void decode_mfma_kernel(DecodeArgs a) {
     // instructions each) are outstanding makes step k resident.  Any other
     // load issued in between only makes the wait stronger.
     auto step = [&](int64_t k, int s) {
-        if (k + 2 < nsteps) issue(k + 2);
-        const int64_t after = (nsteps - 1 - k) < 2 ? (nsteps - 1 - k) : 2;
-        if (after == 2)
-            wait_vmcnt<2 * DMA_PER_STEP>();
-        else if (after == 1)
+        // step k+1 was issued before; step k+2 is issued once step k's key
+        // part is in the matrix cores
+        if (k + 1 < nsteps)
             wait_vmcnt<DMA_PER_STEP>();
         else
             wait_vmcnt<0>();
+        auto mid = [&]() {
+            if (k + 2 < nsteps) issue(k + 2);
+        };
         int64_t blk;
         int sub;
         uint32_t mk;
         find(pwin, k, blk, sub, mk);
         const uint8_t *stage = &ring[wave][s][0];
-        if (mk == 0u) {
-            const int64_t left = a.length - (blk * BLK + 32 * sub);
-            const int nvalid = (int)(left < 32 ? (left > 0 ? left : 0) : 32);
-            if (nvalid > 0) process_step<false>(stage, 0u, nvalid, qb, sml2, ws, lane);
-        } else {
-            const int64_t left = a.length - (blk * BLK + 8 * sub);
-            const int nvalid = (int)(left < 8 ? (left > 0 ? left : 0) : 8);
-            if (nvalid > 0) process_step<true>(stage, mk, nvalid, qb, sml2, ws, lane);
-        }
+        // positions [p_lo, p_hi) of the half: the valid tokens of the step
+        const int step_len = mk ? 8 : 32;
+        const int p_lo = mk ? 8 * (sub & 3) : 0;
+        const int64_t left = a.length - (blk * BLK + (mk ? 8 * sub : 32 * sub));
+        const int nvalid = (int)(left < step_len ? (left > 0 ? left : 0) : step_len);
+        if (nvalid > 0)
+            process_step(stage, mk, p_lo, p_lo + nvalid, qb, sml2, ws, lane, mid);
+        else
+            mid();
     };
     for (int64_t k = 0; k < nsteps; k += NSTAGE) {
         step(k, 0);
