@@ -2,8 +2,9 @@
 
 One step = one decode step of one attention layer for the whole batch:
 kvq_quantize_append of the new token of every sequence (quantize-on-append),
-then kvq_decode_attn (bounds, fallback masks, split-K streaming attention and
-the cross-split merge, fused in one kernel).  Inputs are resident in HBM when
+then kvq_decode_attn (a split-K kernel: bounds, fallback masks, streamed
+tiles and the online softmax; then a kernel merging the splits).  Inputs are
+resident in HBM when
 the timed region starts.  Several layers' caches ("replicas") are cycled so
 that consecutive steps never find their KV stream in the 256 MB Infinity
 Cache, as in a real multi-layer decode.
@@ -11,9 +12,12 @@ Cache, as in a real multi-layer decode.
 Prints one JSON line:
   value      effective KV bandwidth of the step: algorithmic bytes / step time
              (GB/s, 1e9 B/s); tokens_per_s and pct_of_hbm_peak beside it.
-  roofline   for the dominant kernel (the decode kernel): its algorithmic
-             bytes per launch / its mean launch time from HIP events on its
-             stream, against the 8 TB/s HBM3E peak.
+  roofline   for the dominant kernel (the split-K decode kernel): its
+             algorithmic bytes per launch (all of the decode's bytes but the
+             output) / its mean launch time from HIP events on its stream (the
+             library records one between the split-K and merge kernels),
+             against the 8 TB/s HBM3E peak; traffic from committed rocprofv3
+             FETCH_SIZE / WRITE_SIZE runs when they match the sources.
   cpu_baseline  the CPU oracle (fp64, OpenMP) timed on a bounded sample of
              the same workload, same byte accounting.
 
@@ -45,6 +49,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="llama3_8b_32k")
     p.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma"])
+    p.add_argument("--q-heads", type=int, default=0,
+                   help="query heads (0: the workload's), for group-size comparisons")
     p.add_argument("--splits", type=int, default=0)
     p.add_argument("--replicas", type=int, default=0, help="layer caches cycled (0: enough for >= 2 GB)")
     p.add_argument("--fallback-frac", type=float, default=None,
@@ -78,9 +84,11 @@ def append_bytes(B, Hkv, n=1):
     return B * Hkv * n * (512 + 128 + 2 + 64 + 8 + 8)
 
 
-def traffic_from_counters(launches_per_step_kernel):
-    """HBM bytes per decode launch from committed rocprofv3 counter runs, or
-    None when they are absent or were taken on different kernel sources."""
+def traffic_from_counters():
+    """HBM bytes per split-K launch (FETCH_SIZE + WRITE_SIZE, each scaled by
+    the same counter's reading on a plain 1 GiB copy) from the committed
+    rocprofv3 counter runs, or None when they are absent or were taken on
+    other kernel sources."""
     if not os.path.exists(PROFILE_COUNTERS):
         return None
     try:
@@ -88,7 +96,7 @@ def traffic_from_counters(launches_per_step_kernel):
         if c.get("kernel_source_hash") != kernel_source_hash():
             return None
         return float(c["hbm_bytes_per_launch"])
-    except Exception:
+    except (OSError, ValueError, KeyError):
         return None
 
 
@@ -142,6 +150,8 @@ def main():
 
     torch.cuda.set_device(0)
     w = workloads.WORKLOADS[args.workload]
+    if args.q_heads:
+        w = w.scaled(Hq=args.q_heads)
     if w.name == "bulk_quantize":
         sys.exit("bench.py: use --workload with a decode workload (bulk_quantize is a parity case)")
     dev = "cuda"
@@ -191,9 +201,10 @@ def main():
         if ev is not None:
             ev[0].record(stream)
         kvq.kvq_decode_attn(c, q, sm, tau_k, tau_v, out=out, mask_out=mask if i == 0 else None,
-                            workspace=ws[i % R], stream=stream, kernel=kernel, splits=args.splits)
+                            workspace=ws[i % R], stream=stream, kernel=kernel, splits=args.splits,
+                            split_done=None if ev is None else ev[1])
         if ev is not None:
-            ev[1].record(stream)
+            ev[2].record(stream)
 
     step(0)
     torch.cuda.synchronize()
@@ -205,8 +216,13 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    # per timed step: before the decode call, between its split-K and merge
+    # kernels (recorded by the library), after it; each recorded once here so
+    # that the event exists before the library records it
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
+    for e3 in evs:
+        for e in e3:
+            e.record(stream)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -214,8 +230,9 @@ def main():
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     ms_step = dt / args.steps * 1e3
-    dec_ms = [a.elapsed_time(b) for a, b in evs]
-    dec_ms_mean = float(np.mean(dec_ms))
+    split_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    merge_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    call_ms = float(np.mean([e[0].elapsed_time(e[2]) for e in evs]))
 
     if args.calibrate_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -224,8 +241,13 @@ def main():
         torch.cuda.synchronize()
 
     gbs = step_bytes / (ms_step * 1e-3) / 1e9
-    dec_gbs = dec_bytes / (dec_ms_mean * 1e-3) / 1e9
-    traffic = traffic_from_counters(1)
+    # the split-K kernel reads the tiles, statistics and q; the merge kernel
+    # writes the output
+    split_bytes = dec_bytes - w.B * w.Hq * 256
+    split_gbs = split_bytes / (split_ms * 1e-3) / 1e9
+    traffic = traffic_from_counters()
+    kname = {"mfma": "decode_mfma_kernel", "valu": "decode_valu_kernel"}.get(
+        args.kernel, "decode_mfma_kernel" if w.G <= 16 else "decode_valu_kernel")
     line = {
         "metric": "quantized-KV decode attention: effective KV GB/s (% of HBM peak), tokens/s",
         "value": round(gbs, 2),
@@ -253,15 +275,18 @@ def main():
             "bytes_per_step": step_bytes,
         },
         "roofline": {
-            "kernel": "kvq decode (split-K, fused bounds + merge)",
+            "kernel": kname + " (split-K: bounds, masks, tiles, online softmax)",
             "bound": "hbm",
-            "achieved": round(dec_gbs, 2),
+            "achieved": round(split_gbs, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+            "frac": round(split_gbs / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "algorithmic_bytes_per_launch": dec_bytes,
-            "mean_launch_ms": round(dec_ms_mean, 5),
+            "algorithmic_bytes_per_launch": split_bytes,
+            "mean_launch_ms": round(split_ms, 5),
+            "merge_kernel_ms": round(merge_ms, 5),
+            "decode_call_ms": round(call_ms, 5),
+            "decode_call_gbs": round(dec_bytes / (call_ms * 1e-3) / 1e9, 2),
         },
     }
     if not args.no_cpu_baseline:

@@ -156,16 +156,18 @@ kvq_status kvq_decode_attn(const kvq_cache *c, const uint16_t *q, int32_t q_head
                            float tau_k, float tau_v, uint16_t *out, uint8_t *mask_out,
                            void *workspace, size_t ws_bytes, void *stream);
 
-/* Decode kernel selection, for measurement.  kvq_decode_attn uses
+/* Decode kernel selection and timing, for measurement.  kvq_decode_attn uses
  * KVQ_KERNEL_AUTO; kvq_decode_attn_ex lets a benchmark force a variant and a
- * split count (0 = automatic).  Same semantics and errors as
- * kvq_decode_attn; a variant that does not support the group size returns
- * KVQ_ERR_UNSUPPORTED. */
+ * split count (0 = automatic), and, when split_done is a hipEvent_t (passed
+ * as void*, NULL = none), records it on the stream between the split-K kernel
+ * and the merge kernel, so that the split-K kernel can be timed alone.  Same
+ * semantics and errors as kvq_decode_attn; a variant that does not support
+ * the group size or the context length returns KVQ_ERR_UNSUPPORTED. */
 typedef enum { KVQ_KERNEL_AUTO = 0, KVQ_KERNEL_VALU = 1, KVQ_KERNEL_MFMA = 2 } kvq_kernel;
 kvq_status kvq_decode_attn_ex(const kvq_cache *c, const uint16_t *q, int32_t q_heads,
                               float sm_scale, float tau_k, float tau_v, uint16_t *out,
                               uint8_t *mask_out, void *workspace, size_t ws_bytes, void *stream,
-                              int32_t kernel, int32_t splits);
+                              int32_t kernel, int32_t splits, void *split_done);
 
 /* Human-readable name of a status code (static string). */
 const char *kvq_status_str(kvq_status s);

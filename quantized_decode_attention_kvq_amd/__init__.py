@@ -77,7 +77,7 @@ def lib():
         L.kvq_decode_workspace_bytes.restype = sz
         L.kvq_decode_attn.argtypes = [CP, P, i32, f32, f32, f32, P, P, P, sz, P]
         L.kvq_decode_attn.restype = ctypes.c_int
-        L.kvq_decode_attn_ex.argtypes = [CP, P, i32, f32, f32, f32, P, P, P, sz, P, i32, i32]
+        L.kvq_decode_attn_ex.argtypes = [CP, P, i32, f32, f32, f32, P, P, P, sz, P, i32, i32, P]
         L.kvq_decode_attn_ex.restype = ctypes.c_int
         L.kvq_status_str.argtypes = [ctypes.c_int]
         L.kvq_status_str.restype = ctypes.c_char_p
@@ -193,9 +193,11 @@ def make_workspace(cache: KVCache, q_heads: int, device=None):
 
 
 def kvq_decode_attn(cache: KVCache, q, sm_scale=DEFAULT_SM_SCALE, tau_k=0.0, tau_v=0.0, out=None,
-                    mask_out=None, workspace=None, stream=None, kernel=KERNEL_AUTO, splits=0):
+                    mask_out=None, workspace=None, stream=None, kernel=KERNEL_AUTO, splits=0, split_done=None):
     """Certified decode attention: q [B][Hq][128] fp16 -> out [B][Hq][128] fp16.
-    mask_out (optional uint8 [B][Hkv][nblocks]) receives the fallback masks."""
+    mask_out (optional uint8 [B][Hkv][nblocks]) receives the fallback masks.
+    split_done (optional torch.cuda.Event, already recorded once so that it
+    exists) is recorded between the split-K kernel and the merge kernel."""
     _check_q(cache, q)
     if out is None:
         out = torch.empty_like(q)
@@ -204,6 +206,7 @@ def kvq_decode_attn(cache: KVCache, q, sm_scale=DEFAULT_SM_SCALE, tau_k=0.0, tau
     c = cache.c_struct()
     st = lib().kvq_decode_attn_ex(ctypes.byref(c), _ptr(q), q.shape[1], sm_scale, tau_k, tau_v, _ptr(out),
                                   _ptr(mask_out), _ptr(workspace), workspace.numel(), _stream(stream),
-                                  int(kernel), int(splits))
+                                  int(kernel), int(splits),
+                                  None if split_done is None else ctypes.c_void_p(split_done.cuda_event))
     _check("kvq_decode_attn", st)
     return out

@@ -211,7 +211,7 @@ size_t kvq_decode_workspace_bytes(const kvq_cache *c, int32_t q_heads) {
 kvq_status kvq_decode_attn_ex(const kvq_cache *c, const uint16_t *q, int32_t q_heads,
                               float sm_scale, float tau_k, float tau_v, uint16_t *out,
                               uint8_t *mask_out, void *workspace, size_t ws_bytes, void *stream,
-                              int32_t kernel, int32_t splits) {
+                              int32_t kernel, int32_t splits, void *split_done) {
     kvq_status st = check_shape(c);
     if (st != KVQ_OK) return st;
     if ((st = check_query(c, q, q_heads, sm_scale, tau_k, tau_v)) != KVQ_OK) return st;
@@ -259,6 +259,8 @@ kvq_status kvq_decode_attn_ex(const kvq_cache *c, const uint16_t *q, int32_t q_h
 
     hipError_t e = (k == KVQ_KERNEL_MFMA) ? kvq::launch_decode_mfma(a, c->batch, (hipStream_t)stream)
                                           : kvq::launch_decode_valu(a, c->batch, (hipStream_t)stream);
+    if (e == hipSuccess && split_done) e = hipEventRecord((hipEvent_t)split_done, (hipStream_t)stream);
+    if (e == hipSuccess) e = kvq::launch_merge(a, c->batch, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e);
     return KVQ_OK;
 }
@@ -267,7 +269,7 @@ kvq_status kvq_decode_attn(const kvq_cache *c, const uint16_t *q, int32_t q_head
                            float tau_k, float tau_v, uint16_t *out, uint8_t *mask_out,
                            void *workspace, size_t ws_bytes, void *stream) {
     return kvq_decode_attn_ex(c, q, q_heads, sm_scale, tau_k, tau_v, out, mask_out, workspace,
-                              ws_bytes, stream, KVQ_KERNEL_AUTO, 0);
+                              ws_bytes, stream, KVQ_KERNEL_AUTO, 0, nullptr);
 }
 
 }  // extern "C"

@@ -644,8 +644,7 @@ bool mfma_supports(int g) { return g >= 1 && g <= 16; }
 hipError_t launch_decode_mfma(const DecodeArgs &a, int batch, hipStream_t s) {
     dim3 grid((unsigned)a.splits, (unsigned)a.hkv, (unsigned)batch);
     hipLaunchKernelGGL(decode_mfma_kernel, grid, dim3(NW * 64), 0, s, a);
-    hipError_t e = hipGetLastError();
-    return e != hipSuccess ? e : launch_merge(a, batch, s);
+    return hipGetLastError();
 }
 
 }  // namespace kvq

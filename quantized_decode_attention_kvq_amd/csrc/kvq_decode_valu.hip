@@ -319,8 +319,7 @@ hipError_t launch_decode_valu(const DecodeArgs &a, int batch, hipStream_t s) {
         hipLaunchKernelGGL(decode_valu_kernel<8>, grid, dim3(256), 0, s, a);
     else
         hipLaunchKernelGGL(decode_valu_kernel<16>, grid, dim3(256), 0, s, a);
-    hipError_t e = hipGetLastError();
-    return e != hipSuccess ? e : launch_merge(a, batch, s);
+    return hipGetLastError();
 }
 
 }  // namespace kvq

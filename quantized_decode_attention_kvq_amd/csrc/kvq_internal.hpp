@@ -60,6 +60,7 @@ constexpr int MFMA_MAX_BPS = 128;  // blocks per split of the matrix-core kernel
 
 hipError_t launch_append(const AppendArgs &a, int batch, int64_t nblk, hipStream_t s);
 hipError_t launch_bounds(const BoundsArgs &a, int batch, hipStream_t s);
+// The split-K kernels (the cross-split merge is launched separately).
 hipError_t launch_decode_valu(const DecodeArgs &a, int batch, hipStream_t s);
 hipError_t launch_decode_mfma(const DecodeArgs &a, int batch, hipStream_t s);
 hipError_t launch_merge(const DecodeArgs &a, int batch, hipStream_t s);
