@@ -57,6 +57,8 @@ def parse():
                    help="fraction of blocks per bound that fall back (default: the workload's; 0: none)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU work of the oracle sample")
+    p.add_argument("--graph", type=int, default=1,
+                   help="1: replay each layer's step (append + decode) from a captured HIP graph; 0: eager launches")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run one 1 GiB device copy (reference kernel for HBM counters)")
     return p.parse_args()
@@ -216,20 +218,53 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # per timed step: before the decode call, between its split-K and merge
-    # kernels (recorded by the library), after it; each recorded once here so
-    # that the event exists before the library records it
+    # Step launcher of the timed loop: the eager step, or one captured HIP
+    # graph per layer cache holding the same launches (append + decode +
+    # merge), as a serving loop would replay them.
+    run = step
+    if args.graph:
+        graphs = []
+        side = torch.cuda.Stream()
+        for r in range(R):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=side):
+                c = caches[r]
+                c.length = w.T - 1
+                kvq.kvq_quantize_append(c, 1, torch.cuda.current_stream())
+                kvq.kvq_decode_attn(c, q, sm, tau_k, tau_v, out=out, workspace=ws[r],
+                                    stream=torch.cuda.current_stream(), kernel=kernel, splits=args.splits)
+            graphs.append(g)
+        torch.cuda.synchronize()
+
+        def run(i):
+            graphs[i % R].replay()
+        for i in range(args.warmup):
+            run(i)
+        torch.cuda.synchronize()
+
+    # timed loop: exactly `steps` steps between synchronisations
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        run(i)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    ms_step = dt / args.steps * 1e3
+
+    # kernel timing, right after: the same steps launched eagerly with HIP
+    # events on the stream before the decode call, between its split-K and
+    # merge kernels (recorded by the library) and after it; each event is
+    # recorded once first so that it exists before the library records it
     evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
     for e3 in evs:
         for e in e3:
             e.record(stream)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
+    t1 = time.perf_counter()
     for i in range(args.steps):
         step(i, evs[i])
     torch.cuda.synchronize()
-    dt = time.perf_counter() - t0
-    ms_step = dt / args.steps * 1e3
+    ms_step_events = (time.perf_counter() - t1) / args.steps * 1e3
     split_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     merge_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
     call_ms = float(np.mean([e[0].elapsed_time(e[2]) for e in evs]))
@@ -271,7 +306,7 @@ def main():
             "fallback_blocks_value": round(float(((m >> 1) & 1).mean()), 5),
             "tau_k": tau_k if np.isfinite(tau_k) else "inf", "tau_v": tau_v if np.isfinite(tau_v) else "inf",
             "layers_cycled": R,
-            "kernel": args.kernel, "splits": args.splits,
+            "kernel": args.kernel, "splits": args.splits, "hip_graph": bool(args.graph),
             "bytes_per_step": step_bytes,
         },
         "roofline": {
@@ -287,6 +322,7 @@ def main():
             "merge_kernel_ms": round(merge_ms, 5),
             "decode_call_ms": round(call_ms, 5),
             "decode_call_gbs": round(dec_bytes / (call_ms * 1e-3) / 1e9, 2),
+            "eager_ms_per_step_with_events": round(ms_step_events, 5),
         },
     }
     if not args.no_cpu_baseline:
