@@ -61,8 +61,7 @@ typedef float float2_t __attribute__((ext_vector_type(2)));
 
 namespace {
 
-constexpr int NW = 8;         // waves per workgroup (one workgroup per CU)
-constexpr int FBS = 8 / NW;   // fallback steps of one fallback block per wave
+constexpr int NW = 8;  // waves per workgroup (one workgroup per CU, NW/4 waves per SIMD)
 constexpr float NEG_INF = -__builtin_huge_valf();
 
 __device__ __forceinline__ float4_t mfma(uint4 a, uint4 b, float4_t c) {
@@ -145,27 +144,31 @@ constexpr int ST_K = 0, ST_V = 4096, ST_KS = 6144, ST_VS = 6400, ST_BYTES = 6656
 // and the copies are padded up to 8 with dwords of the block's statistics
 // into a region the step leaves unused.
 constexpr int FB_K16 = 0, FB_V16 = 4096;
-constexpr int NSTAGE = 3;
+constexpr int NSTAGE = 3;  // LDS stages per wave
+// With three stages the copies of step k+2 are issued in the middle of step k;
+// with two, those of step k+1 at the start of step k.
+constexpr bool EARLY_ISSUE = NSTAGE == 2;
 constexpr int DMA_PER_STEP = 8;  // copy instructions of every step (half or fallback step)
 
 // Copies of global memory into LDS that bypass the registers.  M0 holds the
 // wave-uniform LDS destination; lane l writes its bytes at M0 + l*size (16 B
 // per lane for dwordx4; a zero-extended dword per lane for dword and ushort).
-// The copy is issued in inline assembly so that its completion is tracked
-// here, with s_waitcnt vmcnt, rather than by the compiler's conservative wait
-// before every LDS read.  The preceding lgkmcnt(0) retires any LDS read of
-// the stage being refilled.
-__device__ __forceinline__ void dma16(uint32_t lds, const void *src) {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-                 :: "s"(lds), "v"(src) : "memory", "m0");
+// The source is a wave-uniform base address (scalar registers) plus this
+// lane's 32-bit byte offset.  The copy is issued in inline assembly so that
+// its completion is tracked here, with s_waitcnt vmcnt, rather than by the
+// compiler's conservative wait before every LDS read.  The preceding
+// lgkmcnt(0) retires any LDS read of the stage being refilled.
+__device__ __forceinline__ void dma16(uint32_t lds, const void *base, uint32_t off) {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :: "s"(lds), "v"(off), "s"(base) : "memory", "m0");
 }
-__device__ __forceinline__ void dma4(uint32_t lds, const void *src) {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
-                 :: "s"(lds), "v"(src) : "memory", "m0");
+__device__ __forceinline__ void dma4(uint32_t lds, const void *base, uint32_t off) {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+                 :: "s"(lds), "v"(off), "s"(base) : "memory", "m0");
 }
-__device__ __forceinline__ void dma2(uint32_t lds, const void *src) {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_ushort %1, off"
-                 :: "s"(lds), "v"(src) : "memory", "m0");
+__device__ __forceinline__ void dma2(uint32_t lds, const void *base, uint32_t off) {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_ushort %1, %2"
+                 :: "s"(lds), "v"(off), "s"(base) : "memory", "m0");
 }
 
 // Waits until at most N of this wave's memory loads are outstanding (loads
@@ -176,31 +179,41 @@ __device__ __forceinline__ void wait_vmcnt() {
     asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
 }
 
+// The lane index, opaque to the optimizer: the per-lane copy offsets derived
+// from it are recomputed at each issue (a few VALU operations) instead of
+// being hoisted out of the stream loop, where they would hold registers.
+__device__ __forceinline__ int opaque_lane(int lane) {
+    asm volatile("" : "+v"(lane));
+    return lane;
+}
+
 // Copies of the code parts of half u: keys (4 chunks + scales, 5 copies) and
-// values (2 chunks + scales, 3 copies).
+// values (2 chunks + scales, 3 copies).  row0: first token of the block.
 __device__ __forceinline__ void issue_keys(const DecodeArgs &a, int64_t row0, int u, uint32_t stage, int lane) {
     const int m = lane & 15, dg = lane >> 4, l32 = lane & 31;
-    const int8_t *kc = a.c.k_codes + (row0 + 32 * u) * D + 32 * dg;
+    const int8_t *kc = a.c.k_codes + (row0 + 32 * u) * D;
 #pragma unroll
     for (int e = 0; e < 2; ++e)
 #pragma unroll
-        for (int h = 0; h < 2; ++h) dma16(stage + ST_K + (2 * e + h) * 1024, kc + half_row(e, m) * D + 16 * h);
-    dma2(stage + ST_KS, a.c.k_scales + row0 + 32 * u + l32);
+        for (int h = 0; h < 2; ++h)
+            dma16(stage + ST_K + (2 * e + h) * 1024, kc, (uint32_t)(half_row(e, m) * D + 32 * dg + 16 * h));
+    dma2(stage + ST_KS, a.c.k_scales + row0 + 32 * u, (uint32_t)(2 * l32));
 }
 __device__ __forceinline__ void issue_values(const DecodeArgs &a, int64_t bh, int64_t blk, int64_t row0, int u,
                                              uint32_t stage, int lane) {
     const int l32 = lane & 31;
-    const uint8_t *vc = a.c.v_codes + (bh * a.nbc + blk) * (D * BLK / 2) + lane * (BLK / 2) + 16 * u;
-    dma16(stage + ST_V, vc);
-    dma16(stage + ST_V + 1024, vc + 64 * (BLK / 2));
-    dma4(stage + ST_VS, a.c.v_scales + (row0 + 32 * u + l32) * 4 + 2 * (lane >> 5));
+    const uint8_t *vc = a.c.v_codes + (bh * a.nbc + blk) * (D * BLK / 2) + 16 * u;
+    dma16(stage + ST_V, vc, (uint32_t)(lane * (BLK / 2)));
+    dma16(stage + ST_V + 1024, vc, (uint32_t)((64 + lane) * (BLK / 2)));
+    dma4(stage + ST_VS, a.c.v_scales + (row0 + 32 * u) * 4, (uint32_t)(2 * (4 * l32 + 2 * (lane >> 5))));
 }
 
 // Issues the copies of half u of block `blk` of (b, kvh) into the stage at
 // LDS byte address `stage` (wave-uniform).  Every source address lies inside
 // the block.
 __device__ __forceinline__ void issue_half(const DecodeArgs &a, int64_t bh, int64_t blk, int u,
-                                           uint32_t stage, int lane) {
+                                           uint32_t stage, int lane_) {
+    const int lane = opaque_lane(lane_);
     const int64_t row0 = bh * a.cap + blk * BLK;
     issue_keys(a, row0, u, stage, lane);
     issue_values(a, bh, blk, row0, u, stage, lane);
@@ -209,7 +222,8 @@ __device__ __forceinline__ void issue_half(const DecodeArgs &a, int64_t bh, int6
 // Issues the 8 copies of fallback step j (tokens 8j .. 8j+7) of block `blk`
 // with fallback mask mk (nonzero).  Every source address lies inside the block.
 __device__ __forceinline__ void issue_fb(const DecodeArgs &a, int64_t bh, int64_t blk, int j,
-                                         uint32_t mk, uint32_t stage, int lane) {
+                                         uint32_t mk, uint32_t stage, int lane_) {
+    const int lane = opaque_lane(lane_);
     const int64_t row0 = bh * a.cap + blk * BLK;  // first token of the block
     const int64_t rs = row0 + 8 * j;              // first token of the step
     const int u = j >> 2;
@@ -217,13 +231,16 @@ __device__ __forceinline__ void issue_fb(const DecodeArgs &a, int64_t bh, int64_
     if (mk & 1u) {
         const int r = lane & 3, dg = (lane >> 2) & 3, st = lane >> 4;
 #pragma unroll
-        for (int e = 0; e < 2; ++e) dma16(stage + FB_K16 + 1024 * e, a.c.k16 + (rs + 4 * e + r) * D + 32 * dg + 8 * st);
+        for (int e = 0; e < 2; ++e)
+            dma16(stage + FB_K16 + 1024 * e, a.c.k16 + rs * D, (uint32_t)(2 * ((4 * e + r) * D + 32 * dg + 8 * st)));
     } else {
         issue_keys(a, row0, u, stage, lane);
     }
     if (mk & 2u) {
 #pragma unroll
-        for (int d = 0; d < 2; ++d) dma16(stage + FB_V16 + 1024 * d, a.c.v16 + (rs + 4 * d + (lane >> 4)) * D + 8 * (lane & 15));
+        for (int d = 0; d < 2; ++d)
+            dma16(stage + FB_V16 + 1024 * d, a.c.v16 + rs * D,
+                  (uint32_t)(2 * ((4 * d + (lane >> 4)) * D + 8 * (lane & 15))));
     } else {
         issue_values(a, bh, blk, row0, u, stage, lane);
     }
@@ -232,12 +249,12 @@ __device__ __forceinline__ void issue_fb(const DecodeArgs &a, int64_t bh, int64_
     // unused value-scale region
     if ((mk & 1u) && !(mk & 2u)) {
 #pragma unroll
-        for (int i = 0; i < 3; ++i) dma4(stage + 2048 + 256 * i, pad);
+        for (int i = 0; i < 3; ++i) dma4(stage + 2048 + 256 * i, pad, 0u);
     } else if (mk & 1u) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dma4(stage + 2048 + 256 * i, pad);
+        for (int i = 0; i < 4; ++i) dma4(stage + 2048 + 256 * i, pad, 0u);
     } else {
-        dma4(stage + ST_VS, pad);
+        dma4(stage + ST_VS, pad, 0u);
     }
 }
 
@@ -414,8 +431,8 @@ __device__ __forceinline__ void process_step(const uint8_t *stage, uint32_t mk, 
 // cut by its range ends.
 constexpr int TBL = 4 * MFMA_MAX_BPS + 8;
 
-__global__ __launch_bounds__(NW * 64, 2) void decode_mfma_kernel(DecodeArgs a) {
-    // NW waves x 3 stages x 6656 B of ring.  Before the stream starts, wave
+__global__ __launch_bounds__(NW * 64, NW / 4) void decode_mfma_kernel(DecodeArgs a) {
+    // NW waves x NSTAGE stages x 6656 B of ring.  Before the stream starts, wave
     // 0's stage 2 holds the query rows and the ring from wave 1 on the masks
     // of every block of (b, kvh); after it ends, the ring holds the wave merge.
     __shared__ __attribute__((aligned(16))) uint8_t ring[NW][NSTAGE][ST_BYTES];
@@ -425,7 +442,7 @@ __global__ __launch_bounds__(NW * 64, 2) void decode_mfma_kernel(DecodeArgs a) {
     __shared__ float wm[NW][16], wl[NW][16];
     __shared__ int wsum_lds[NW];
     __shared__ int blo_lds, ntbl_lds;
-    uint16_t(*q_lds)[D] = reinterpret_cast<uint16_t(*)[D]>(&ring[0][2][0]);
+    uint16_t(*q_lds)[D] = reinterpret_cast<uint16_t(*)[D]>(&ring[0][NSTAGE - 1][0]);
     uint8_t *maskb = &ring[1][0][0];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -565,16 +582,17 @@ __global__ __launch_bounds__(NW * 64, 2) void decode_mfma_kernel(DecodeArgs a) {
             issue_half(a, bh, blk, sub, st, lane);
         istage = istage == NSTAGE - 1 ? 0 : istage + 1;
     };
-    // stages 0 and 1 only: stage 2 of wave 0 still holds the query rows (the
-    // masks are no longer needed)
-    if (nsteps > 0) issue(0);
-    if (nsteps > 1) issue(1);
+    // all stages but the last: the last stage of wave 0 still holds the query
+    // rows (the masks are no longer needed)
+#pragma unroll
+    for (int k = 0; k < NSTAGE - 1; ++k)
+        if (k < nsteps) issue(k);
 
     // B operands of Q.K^T: lane (n = head, dg) holds q[n][32dg + 8s .. +8] at step s
     uint4 qb[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) qb[s] = *reinterpret_cast<const uint4 *>(&q_lds[m][32 * g4 + 8 * s]);
-    __syncthreads();  // every wave holds its q operands: stage 2 of wave 0 is free
+    __syncthreads();  // every wave holds its q operands: the last stage of wave 0 is free
 
     const float sml2 = a.sm * 1.4426950408889634f;  // scores in log2 units
     WaveState ws;
@@ -583,19 +601,20 @@ __global__ __launch_bounds__(NW * 64, 2) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) ws.acc[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-    // Before computing step k the copies of step k+2 are issued; waiting until
-    // at most the copies issued after step k's (0, 1 or 2 steps' worth, 8
-    // instructions each) are outstanding makes step k resident.  Any other
-    // load issued in between only makes the wait stronger.
+    // When step k starts, the copies of steps k and k+1 have been issued
+    // (with two stages, those of step k+1 just now); waiting until at most
+    // the 8 copies of step k+1 are outstanding makes step k resident.  Any
+    // other load issued in between only makes the wait stronger.  With three
+    // stages the copies of step k+2 are issued once step k's key part is in
+    // the matrix cores.
     auto step = [&](int64_t k, int s) {
-        // step k+1 was issued before; step k+2 is issued once step k's key
-        // part is in the matrix cores
+        if (EARLY_ISSUE && k + 1 < nsteps) issue(k + 1);
         if (k + 1 < nsteps)
             wait_vmcnt<DMA_PER_STEP>();
         else
             wait_vmcnt<0>();
         auto mid = [&]() {
-            if (k + 2 < nsteps) issue(k + 2);
+            if (!EARLY_ISSUE && k + 2 < nsteps) issue(k + 2);
         };
         int64_t blk;
         int sub;
@@ -613,9 +632,9 @@ __global__ __launch_bounds__(NW * 64, 2) void decode_mfma_kernel(DecodeArgs a) {
             mid();
     };
     for (int64_t k = 0; k < nsteps; k += NSTAGE) {
-        step(k, 0);
-        if (k + 1 < nsteps) step(k + 1, 1);
-        if (k + 2 < nsteps) step(k + 2, 2);
+#pragma unroll
+        for (int s = 0; s < NSTAGE; ++s)
+            if (k + s < nsteps) step(k + s, s);
     }
 
     // ---------------- merge waves, then splits
