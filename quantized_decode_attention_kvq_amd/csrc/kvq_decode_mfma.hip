@@ -442,6 +442,7 @@ __global__ __launch_bounds__(NW * 64, NW / 4) void decode_mfma_kernel(DecodeArgs
     __shared__ float wm[NW][16], wl[NW][16];
     __shared__ int wsum_lds[NW];
     __shared__ int blo_lds, ntbl_lds;
+    __shared__ int next_lds;  // next unclaimed step of the share
     uint16_t(*q_lds)[D] = reinterpret_cast<uint16_t(*)[D]>(&ring[0][NSTAGE - 1][0]);
     uint8_t *maskb = &ring[1][0][0];
 
@@ -521,6 +522,7 @@ __global__ __launch_bounds__(NW * 64, NW / 4) void decode_mfma_kernel(DecodeArgs
     }
     __syncthreads();
     const int blo = blo_lds;
+    if (tid == 0) next_lds = 0;
     {
         int p = excl;
         for (int i = i0; i < i1; ++i) {
@@ -536,11 +538,14 @@ __global__ __launch_bounds__(NW * 64, NW / 4) void decode_mfma_kernel(DecodeArgs
     __syncthreads();
     const int ntbl = r1 > r0 ? ntbl_lds - blo + 1 : 0;
 
-    // This wave's steps are the share's steps wave, wave + NW, ...  A step is
-    // found in the table with a 64-entry window held one entry per lane: the
-    // listed block is the last one whose first step is at or before it.
+    // The share's steps are claimed by the waves one at a time, at issue
+    // time, from a counter in LDS, so that a wave that runs ahead (the SIMD
+    // issues the older of its two waves first) takes more steps and the waves
+    // of the workgroup finish together.  A wave's claims increase, so a step
+    // is found in the table with a 64-entry window that only moves forward,
+    // held one entry per lane: the listed block is the last one whose first
+    // step is at or before it.
     const int nshare = r1 - r0;
-    const int64_t nsteps = nshare > wave ? (nshare - 1 - wave) / NW + 1 : 0;
     struct Window {
         int jb;        // table index of lane 0
         int off;       // this lane's entry: first step, mask
@@ -552,9 +557,8 @@ __global__ __launch_bounds__(NW * 64, NW / 4) void decode_mfma_kernel(DecodeArgs
         wn.off = j < ntbl ? toff_lds[j] : 0x7fffffff;
         wn.mk = j < ntbl ? tmk_lds[j] : 0u;
     };
-    // step k of this wave -> block, sub-step (half or fallback step), mask
-    auto find = [&](Window &wn, int64_t k, int64_t &blk, int &sub, uint32_t &mk) {
-        const int t = wave + NW * (int)k;
+    // share step t -> block, sub-step (half or fallback step), mask
+    auto find = [&](Window &wn, int t, int64_t &blk, int &sub, uint32_t &mk) {
         uint64_t bal = __builtin_amdgcn_ballot_w64(wn.off <= t);
         while ((bal >> 63) && wn.jb + 64 < ntbl) {
             load_window(wn, wn.jb + 63);
@@ -568,25 +572,33 @@ __global__ __launch_bounds__(NW * 64, NW / 4) void decode_mfma_kernel(DecodeArgs
     Window iwin, pwin;  // issue and process cursors
     load_window(iwin, 0);
     pwin = iwin;
+    auto claim = [&]() -> int {
+        int t = 0;
+        if (lane == 0) t = atomicAdd(&next_lds, 1);
+        return __builtin_amdgcn_readfirstlane(t);
+    };
     const uint32_t ring0 = (uint32_t)(uintptr_t)&ring[wave][0][0];
-    uint32_t istage = 0;  // stage of the next issue
-    auto issue = [&](int64_t k) {
-        int64_t blk;
-        int sub;
-        uint32_t mk;
-        find(iwin, k, blk, sub, mk);
-        const uint32_t st = ring0 + istage * ST_BYTES;
-        if (mk)
-            issue_fb(a, bh, blk, sub, mk, st, lane);
-        else
-            issue_half(a, bh, blk, sub, st, lane);
-        istage = istage == NSTAGE - 1 ? 0 : istage + 1;
+    // claims of the steps in the stages (>= nshare: none)
+    int tq[NSTAGE];
+    auto claim_issue = [&](int st) {
+        const int t = claim();
+        tq[st] = t;
+        if (t < nshare) {
+            int64_t blk;
+            int sub;
+            uint32_t mk;
+            find(iwin, t, blk, sub, mk);
+            const uint32_t sa = ring0 + st * ST_BYTES;
+            if (mk)
+                issue_fb(a, bh, blk, sub, mk, sa, lane);
+            else
+                issue_half(a, bh, blk, sub, sa, lane);
+        }
     };
     // all stages but the last: the last stage of wave 0 still holds the query
     // rows (the masks are no longer needed)
 #pragma unroll
-    for (int k = 0; k < NSTAGE - 1; ++k)
-        if (k < nsteps) issue(k);
+    for (int st = 0; st < NSTAGE - 1; ++st) claim_issue(st);
 
     // B operands of Q.K^T: lane (n = head, dg) holds q[n][32dg + 8s .. +8] at step s
     uint4 qb[4];
@@ -601,25 +613,30 @@ __global__ __launch_bounds__(NW * 64, NW / 4) void decode_mfma_kernel(DecodeArgs
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) ws.acc[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-    // When step k starts, the copies of steps k and k+1 have been issued
-    // (with two stages, those of step k+1 just now); waiting until at most
-    // the 8 copies of step k+1 are outstanding makes step k resident.  Any
-    // other load issued in between only makes the wait stronger.  With three
-    // stages the copies of step k+2 are issued once step k's key part is in
-    // the matrix cores.
-    auto step = [&](int64_t k, int s) {
-        if (EARLY_ISSUE && k + 1 < nsteps) issue(k + 1);
-        if (k + 1 < nsteps)
+    // Stage s holds claim tq[s].  When the step in stage s starts, the step in
+    // the next stage has been claimed and issued too if it exists (with two
+    // stages, just now); waiting until at most its 8 copies are outstanding
+    // makes stage s resident.  Any other load issued in between only makes
+    // the wait stronger.  With three stages the stage after that is claimed
+    // and issued once this step's key part is in the matrix cores.  Returns
+    // false once the wave has no step left.
+    auto step = [&](int s) -> bool {
+        const int t = tq[s];
+        if (t >= nshare) return false;
+        const int s1 = s + 1 == NSTAGE ? 0 : s + 1;
+        const int s2 = s1 + 1 == NSTAGE ? 0 : s1 + 1;
+        if (EARLY_ISSUE) claim_issue(s1);
+        if (tq[s1] < nshare)
             wait_vmcnt<DMA_PER_STEP>();
         else
             wait_vmcnt<0>();
         auto mid = [&]() {
-            if (!EARLY_ISSUE && k + 2 < nsteps) issue(k + 2);
+            if (!EARLY_ISSUE) claim_issue(s2);
         };
         int64_t blk;
         int sub;
         uint32_t mk;
-        find(pwin, k, blk, sub, mk);
+        find(pwin, t, blk, sub, mk);
         const uint8_t *stage = &ring[wave][s][0];
         // positions [p_lo, p_hi) of the half: the valid tokens of the step
         const int step_len = mk ? 8 : 32;
@@ -630,11 +647,12 @@ __global__ __launch_bounds__(NW * 64, NW / 4) void decode_mfma_kernel(DecodeArgs
             process_step(stage, mk, p_lo, p_lo + nvalid, qb, sml2, ws, lane, mid);
         else
             mid();
+        return true;
     };
-    for (int64_t k = 0; k < nsteps; k += NSTAGE) {
+    for (bool more = true; more;) {
 #pragma unroll
         for (int s = 0; s < NSTAGE; ++s)
-            if (k + s < nsteps) step(k + s, s);
+            if (more) more = step(s);
     }
 
     // ---------------- merge waves, then splits

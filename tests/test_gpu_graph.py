@@ -1,6 +1,8 @@
 """A decode step (quantize-on-append of one token, certified decode, split
-merge) captured in a HIP graph replays to the same bytes as the eager step,
-on every replay, with eager work and synchronisations between replays.  The
+merge) captured in a HIP graph replays like the eager step on every replay,
+with eager work and synchronisations between replays: the appended codes are
+bitwise equal and the outputs agree to fp16 rounding (the decode kernel's
+waves claim their steps dynamically, so accumulation order may differ).  The
 library only launches kernels on the caller's stream, so it is capturable."""
 import numpy as np
 import pytest
@@ -8,7 +10,7 @@ import torch
 
 import quantized_decode_attention_kvq_amd as kvq
 import workloads
-from kvq_testlib import SM, gpu_cache
+from kvq_testlib import SM, gpu_cache, normwise_err
 
 pytestmark = pytest.mark.gpu
 
@@ -31,7 +33,7 @@ def test_captured_step_replays_like_eager():
     out_e = torch.empty_like(q)
     step(ce, wse, out_e, torch.cuda.current_stream())
     torch.cuda.synchronize()
-    ref = out_e.cpu().numpy().view(np.uint16)
+    ref = out_e.float().cpu().numpy()
     ref_codes = ce.k_codes[:, :, :w.T].cpu().numpy()  # rows past `length` are never written
 
     # captured step on a second cache
@@ -50,9 +52,9 @@ def test_captured_step_replays_like_eager():
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        np.testing.assert_array_equal(out_g.cpu().numpy().view(np.uint16), ref, err_msg=f"replay {rep}")
+        assert normwise_err(out_g.float().cpu().numpy(), ref).max() <= 2.0 ** -10, f"replay {rep}"
         np.testing.assert_array_equal(cg.k_codes[:, :, :w.T].cpu().numpy(), ref_codes, err_msg=f"replay {rep} codes")
         # eager work between replays
         step(ce, wse, out_e, torch.cuda.current_stream())
         torch.cuda.synchronize()
-        np.testing.assert_array_equal(out_e.cpu().numpy().view(np.uint16), ref)
+        assert normwise_err(out_e.float().cpu().numpy(), ref).max() <= 2.0 ** -10

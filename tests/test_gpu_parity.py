@@ -120,16 +120,23 @@ def test_decode_split_counts(splits):
     _decode_check(w, d, 0.1, splits=splits)
 
 
-def test_decode_is_deterministic():
+def test_decode_is_repeatable():
+    # The matrix-core kernel's waves claim steps dynamically, so the order in
+    # which a wave accumulates its steps can differ between runs: masks are
+    # bitwise equal, outputs agree to fp16 rounding.
     w = small("llama3_8b_32k", B=2, T=2000)
     d = workloads.make(w)
     gc = gpu_cache(d, w.T)
     q = d["q"].cuda()
     ws = kvq.make_workspace(gc, w.Hq)
-    a = kvq.kvq_decode_attn(gc, q, SM, 0.05, 0.05, workspace=ws).clone()
-    b = kvq.kvq_decode_attn(gc, q, SM, 0.05, 0.05, workspace=ws).clone()
+    nb = gc.nblocks
+    ma = torch.empty((w.B, w.Hkv, nb), dtype=torch.uint8, device="cuda")
+    mb = torch.empty_like(ma)
+    a = kvq.kvq_decode_attn(gc, q, SM, 0.05, 0.05, workspace=ws, mask_out=ma).clone()
+    b = kvq.kvq_decode_attn(gc, q, SM, 0.05, 0.05, workspace=ws, mask_out=mb).clone()
     torch.cuda.synchronize()
-    assert torch.equal(a, b)
+    assert torch.equal(ma, mb)
+    assert normwise_err(a.float().cpu().numpy(), b.float().cpu().numpy()).max() <= 2.0 ** -10
 
 
 def test_decode_empty_and_single_token():
