@@ -57,6 +57,8 @@ def parse():
                    help="fraction of blocks per bound that fall back (default: the workload's; 0: none)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU work of the oracle sample")
+    p.add_argument("--taus", default=None,
+                   help="explicit tolerances 'tau_k,tau_v' (inf allowed), overriding --fallback-frac")
     p.add_argument("--graph", type=int, default=1,
                    help="1: replay each layer's step (append + decode) from a captured HIP graph; 0: eager launches")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -136,6 +138,60 @@ def cpu_baseline(w, d, tau_k, tau_v, sm, target_s):
             "tokens_per_s_equiv": round(n / len(groups) * w.B / dt, 3)}
 
 
+def bench_quantize(args, w):
+    """Quantize-on-append throughput: one step appends the workload's T new
+    tokens of every KV head to an empty cache (bulk prefill).  Algorithmic
+    bytes per token-head: 512 fp16 K and V bytes read; 128 key codes, 2 key
+    scale bytes, 64 value-code bytes and 8 value-scale bytes written; plus 8
+    bytes of block statistics per block."""
+    import numpy as np
+    import torch
+
+    import quantized_decode_attention_kvq_amd as kvq
+    import workloads
+
+    d = workloads.make(w, "cuda")
+    c = kvq.KVCache(w.B, w.Hkv, w.cap, k16=d["k16"], v16=d["v16"])
+    del d
+    stream = torch.cuda.current_stream()
+    th = w.B * w.Hkv * w.T
+    nbytes = th * (512 + 128 + 2 + 64 + 8) + w.B * w.Hkv * ((w.T + 63) // 64) * 8
+
+    def step(ev=None):
+        c.length = 0
+        if ev is not None:
+            ev[0].record(stream)
+        kvq.kvq_quantize_append(c, w.T, stream)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) / args.steps * 1e3
+    k_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    gbs = nbytes / (ms_step * 1e-3) / 1e9
+    kgbs = nbytes / (k_ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "quantize-on-append (bulk prefill): GB/s (% of HBM peak), tokens/s",
+        "value": round(gbs, 2), "unit": "GB/s", "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "tokens_per_s": round(w.B * w.T / (ms_step * 1e-3), 1), "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp16 in, int8 K / int4 V codes out, fp64 error sums",
+        "data": "synthetic (seeded normal fp16 K/V with 3 K outlier channels x20)",
+        "config": {"workload": f"{w.name}: {w.T} new tokens x {w.Hkv} KV heads x D128, one bulk append",
+                   "bytes_per_step": nbytes},
+        "roofline": {"kernel": "quantize_append_kernel", "bound": "hbm", "achieved": round(kgbs, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(kgbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": nbytes, "mean_launch_ms": round(k_ms, 5)},
+    }), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -155,7 +211,7 @@ def main():
     if args.q_heads:
         w = w.scaled(Hq=args.q_heads)
     if w.name == "bulk_quantize":
-        sys.exit("bench.py: use --workload with a decode workload (bulk_quantize is a parity case)")
+        return bench_quantize(args, w)
     dev = "cuda"
     sm = kvq.DEFAULT_SM_SCALE
     kernel = {"auto": kvq.KERNEL_AUTO, "valu": kvq.KERNEL_VALU, "mfma": kvq.KERNEL_MFMA}[args.kernel]
@@ -189,6 +245,8 @@ def main():
 
     frac = w.fallback_frac if args.fallback_frac is None else args.fallback_frac
     tau_k, tau_v = tau(kbn, frac), tau(vbn, frac)
+    if args.taus:
+        tau_k, tau_v = (float(x) for x in args.taus.split(","))
     c0.length = w.T - 1
 
     out = torch.empty_like(q)

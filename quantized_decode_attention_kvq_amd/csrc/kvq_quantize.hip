@@ -34,12 +34,26 @@ __device__ __forceinline__ float elem(const uint32_t w[4], int k) {
     return h2f((k & 1) ? (w[k >> 1] >> 16) : (w[k >> 1] & 0xFFFFu));
 }
 
-// round_half_even(x / s) clamped to [-lim, lim]; s > 0.  IEEE binary32
-// division (correctly rounded) followed by rint: the quotient of two fp16
-// values cannot be moved across a half-integer by that rounding.
-__device__ __forceinline__ int quant_code(float x, float s, int lim) {
-    int c = (int)__builtin_rintf(__fdiv_rn(x, s));
-    return c < -lim ? -lim : (c > lim ? lim : c);
+// round_half_even(x / s) clamped to [-lim, lim], for fp16 values x and s > 0,
+// with r ~ 1/s (any estimate within a few ulps) and hs = s/2.  The estimate
+// rint(x*r) is off by at most one, and only next to a half-integer; the
+// residual x - c*s is exact in fp32 (c*s has at most 19 significant bits, and
+// x and c*s lie on the grid of the smaller of their fp16 ulps whenever c is
+// nonzero), so comparing it with s/2 -- ties going to the even code --
+// corrects the estimate exactly.  r == 0 marks a zero scale.  Returns the
+// code; e receives x - c*s for the final (clamped) code, also exact.
+__device__ __forceinline__ int quant_code(float x, float s, float r, float hs, int lim, float &e) {
+    float c = __builtin_rintf(x * r);
+    const float d = __builtin_fmaf(-c, s, x);
+    const bool odd = ((int)c & 1) != 0;
+    if (d > hs || (d == hs && odd))
+        c += 1.0f;
+    else if (d < -hs || (d == -hs && odd))
+        c -= 1.0f;
+    c = __builtin_fminf(__builtin_fmaxf(c, (float)-lim), (float)lim);
+    c = r == 0.0f ? 0.0f : c;  // zero scale (also rows holding Inf/NaN): code 0
+    e = __builtin_fmaf(-c, s, x);
+    return (int)c;
 }
 
 __global__ __launch_bounds__(256) void quantize_append_kernel(AppendArgs a) {
@@ -77,13 +91,16 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(AppendArgs a) {
         const bool knonfin = am >= 0x7C00u;
         const uint32_t ksb = knonfin ? 0u : f2h_rn(__fdiv_rn(h2f(am), 127.0f));
         const float ks = h2f(ksb);
+        // a zero scale (tiny, all-zero or non-finite row) gives codes 0
+        const float kr_ = ks != 0.0f ? __builtin_amdgcn_rcpf(ks) : 0.0f;
+        const float khs = ks != 0.0f ? 0.5f * ks : __builtin_huge_valf();
         uint32_t kc[2] = {0u, 0u};
         double sq[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             const float x = elem(kw, k);
-            const int c = (ks != 0.0f) ? quant_code(x, ks, 127) : 0;
-            const float e = __fsub_rn(x, __fmul_rn(ks, (float)c));  // exact
+            float e;
+            const int c = quant_code(x, ks, kr_, khs, 127, e);
             sq[k] = sq64(e);
             kc[k >> 2] |= ((uint32_t)c & 0xFFu) << (8 * (k & 3));
         }
@@ -99,13 +116,16 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(AppendArgs a) {
         const bool vnonfin = vm >= 0x7C00u;
         const uint32_t vsb = vnonfin ? 0u : f2h_rn(__fdiv_rn(h2f(vm), 7.0f));
         const float vs = h2f(vsb);
+        const float vr_ = vs != 0.0f ? __builtin_amdgcn_rcpf(vs) : 0.0f;
+        const float vhs = vs != 0.0f ? 0.5f * vs : __builtin_huge_valf();
         uint32_t vc[2] = {0u, 0u};
         float verr = 0.0f;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             const float x = elem(vw, k);
-            const int c = (vs != 0.0f) ? quant_code(x, vs, 7) : 0;
-            const float e = __builtin_fabsf(__fsub_rn(x, __fmul_rn(vs, (float)c)));  // exact
+            float e;
+            const int c = quant_code(x, vs, vr_, vhs, 7, e);
+            e = __builtin_fabsf(e);
             verr = verr > e ? verr : e;
             vc[k >> 2] |= ((uint32_t)c & 0x0Fu) << (8 * (k & 3));
         }
@@ -152,27 +172,38 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(AppendArgs a) {
         const int j = tid >> 1;         // channel
         const int i0 = (tid & 1) * 16;  // first byte (token pair) of this thread
         uint8_t *dst = a.c.v_codes + (head * (a.cap / BLK) + blk) * (D * BLK / 2) + j * (BLK / 2) + i0;
-        uint4 old = make_uint4(0, 0, 0, 0);
-        if (has_old) old = *reinterpret_cast<const uint4 *>(dst);
-        const uint32_t ow[4] = {old.x, old.y, old.z, old.w};
+        // tokens [lo, hi) of the block are new, [0, lo) kept, [hi, 64) zero
+        const int lo = (int)(t_begin - t_first), hi = (int)(t_end - t_first);
         uint32_t nw[4] = {0u, 0u, 0u, 0u};
+        if (lo == 0 && hi == BLK) {
+            // the whole block is new: pair the staged low nibbles
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            uint32_t byte = 0;
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                const int tk = 2 * (i0 + i) + half;
-                const int64_t t = t_first + tk;
-                uint32_t nib;
-                if (t < a.len0)
-                    nib = (ow[i >> 2] >> (8 * (i & 3) + 4 * half)) & 0x0Fu;
-                else if (t < a.len1)
-                    nib = vtile[tk][j] & 0x0Fu;
-                else
-                    nib = 0u;
-                byte |= nib << (4 * half);
+            for (int i = 0; i < 16; ++i) {
+                const int tk = 2 * (i0 + i);
+                const uint32_t byte = (vtile[tk][j] & 0x0Fu) | ((uint32_t)(vtile[tk + 1][j] & 0x0Fu) << 4);
+                nw[i >> 2] |= byte << (8 * (i & 3));
             }
-            nw[i >> 2] |= byte << (8 * (i & 3));
+        } else {
+            uint4 old = make_uint4(0, 0, 0, 0);
+            if (has_old) old = *reinterpret_cast<const uint4 *>(dst);
+            const uint32_t ow[4] = {old.x, old.y, old.z, old.w};
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                uint32_t byte = 0;
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    const int tk = 2 * (i0 + i) + half;
+                    uint32_t nib;
+                    if (tk < lo)
+                        nib = (ow[i >> 2] >> (8 * (i & 3) + 4 * half)) & 0x0Fu;
+                    else if (tk < hi)
+                        nib = vtile[tk][j] & 0x0Fu;
+                    else
+                        nib = 0u;
+                    byte |= nib << (4 * half);
+                }
+                nw[i >> 2] |= byte << (8 * (i & 3));
+            }
         }
         *reinterpret_cast<uint4 *>(dst) = make_uint4(nw[0], nw[1], nw[2], nw[3]);
     }
