@@ -432,18 +432,16 @@ __device__ __forceinline__ void process_step(const uint8_t *stage, uint32_t mk, 
 constexpr int TBL = 4 * MFMA_MAX_BPS + 8;
 
 __global__ __launch_bounds__(NW * 64, NW / 4) void decode_mfma_kernel(DecodeArgs a) {
-    // NW waves x NSTAGE stages x 6656 B of ring.  Before the stream starts, wave
-    // 0's stage 2 holds the query rows and the ring from wave 1 on the masks
-    // of every block of (b, kvh); after it ends, the ring holds the wave merge.
+    // NW waves x NSTAGE stages x 6656 B of ring.  Before the stream starts, the
+    // ring from wave 1 on holds the masks of every block of (b, kvh); after it
+    // ends, the ring holds the wave merge.
     __shared__ __attribute__((aligned(16))) uint8_t ring[NW][NSTAGE][ST_BYTES];
     __shared__ int16_t toff_lds[TBL];  // share-local index of each listed block's first step
     __shared__ uint8_t tmk_lds[TBL];   // its fallback mask
-    __shared__ float qn_lds[16];
     __shared__ float wm[NW][16], wl[NW][16];
     __shared__ int wsum_lds[NW];
     __shared__ int blo_lds, ntbl_lds;
     __shared__ int next_lds;  // next unclaimed step of the share
-    uint16_t(*q_lds)[D] = reinterpret_cast<uint16_t(*)[D]>(&ring[0][NSTAGE - 1][0]);
     uint8_t *maskb = &ring[1][0][0];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -466,7 +464,40 @@ __global__ __launch_bounds__(NW * 64, NW / 4) void decode_mfma_kernel(DecodeArgs
         ke[r] = i < nb ? a.c.k_err[bh * a.nbc + i] : 0.0f;
         ve[r] = i < nb ? a.c.v_err[bh * a.nbc + i] : 0.0f;
     }
-    const float qn = load_q_and_norm(a.q, b * a.hq + kvh * g, g, q_lds, qn_lds);
+    // B operands of Q.K^T, loaded by every wave straight from HBM: lane
+    // (n = head, dg) holds q[n][32dg + 8s .. +8] at step s (heads >= G: 0).
+    // The same registers give the query norms: run 4dg + s of head n is its
+    // 8 channels at step s, so the pinned tree's run pairs (r, r+8), (r, r+4)
+    // are lanes dg, dg^2 and dg, dg^1, and (r, r+2), (r, r+1) are in-lane.
+    uint4 qb[4];
+    float qn;
+    {
+        const bool live = m < g;
+        const uint16_t *qr = a.q + (b * a.hq + kvh * g + (live ? m : 0)) * D + 32 * g4;
+        double run[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const uint4 v = *reinterpret_cast<const uint4 *>(qr + 8 * s);
+            qb[s] = live ? v : make_uint4(0u, 0u, 0u, 0u);
+            const uint32_t w4[4] = {qb[s].x, qb[s].y, qb[s].z, qb[s].w};
+            double t[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                t[2 * i] = sq64(h2f(w4[i] & 0xFFFFu));
+                t[2 * i + 1] = sq64(h2f(w4[i] >> 16));
+            }
+            run[s] = ((t[0] + t[1]) + (t[2] + t[3])) + ((t[4] + t[5]) + (t[6] + t[7]));
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) run[s] = run[s] + shfl_xor_d(run[s], 32);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) run[s] = run[s] + shfl_xor_d(run[s], 16);
+        float qh = (float)__dsqrt_rn((run[0] + run[2]) + (run[1] + run[3]));
+        // group norm: max over the heads (lanes m; heads >= G have norm 0)
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) qh = max_keep_nan(qh, __shfl_xor(qh, o));
+        qn = qh;
+    }
 
     // masks of every block of (b, kvh); mask_out receives this workgroup's
     // home range of bps blocks
@@ -595,16 +626,9 @@ __global__ __launch_bounds__(NW * 64, NW / 4) void decode_mfma_kernel(DecodeArgs
                 issue_half(a, bh, blk, sub, sa, lane);
         }
     };
-    // all stages but the last: the last stage of wave 0 still holds the query
-    // rows (the masks are no longer needed)
+    // all stages but the last (the masks in the ring are no longer needed)
 #pragma unroll
     for (int st = 0; st < NSTAGE - 1; ++st) claim_issue(st);
-
-    // B operands of Q.K^T: lane (n = head, dg) holds q[n][32dg + 8s .. +8] at step s
-    uint4 qb[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) qb[s] = *reinterpret_cast<const uint4 *>(&q_lds[m][32 * g4 + 8 * s]);
-    __syncthreads();  // every wave holds its q operands: the last stage of wave 0 is free
 
     const float sml2 = a.sm * 1.4426950408889634f;  // scores in log2 units
     WaveState ws;
