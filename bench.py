@@ -1,10 +1,10 @@
 """Benchmark of the certified quantized-KV decode step on one MI355X.
 
 One step = one decode step of one attention layer for the whole batch:
-kvq_quantize_append of the new token of every sequence (quantize-on-append),
-then kvq_decode_attn (a split-K kernel: bounds, fallback masks, streamed
-tiles and the online softmax; then a kernel merging the splits).  Inputs are
-resident in HBM when
+kvq_append_decode, i.e. quantize-on-append of the new token of every sequence
+fused into the split-K decode kernel (bounds, fallback masks, streamed tiles
+and the online softmax), then a kernel merging the splits (--unfused: the
+append as its own kernel first).  Inputs are resident in HBM when
 the timed region starts.  Several layers' caches ("replicas") are cycled so
 that consecutive steps never find their KV stream in the 256 MB Infinity
 Cache, as in a real multi-layer decode.
@@ -59,6 +59,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU work of the oracle sample")
     p.add_argument("--taus", default=None,
                    help="explicit tolerances 'tau_k,tau_v' (inf allowed), overriding --fallback-frac")
+    p.add_argument("--unfused", action="store_true",
+                   help="step as two calls (kvq_quantize_append, kvq_decode_attn) instead of kvq_append_decode")
     p.add_argument("--graph", type=int, default=1,
                    help="1: replay each layer's step (append + decode) from a captured HIP graph; 0: eager launches")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -254,17 +256,19 @@ def main():
     ws = [kvq.make_workspace(c, w.Hq) for c in caches]
     stream = torch.cuda.current_stream()
 
-    def step(i, ev=None):
+    def step(i, ev=None, strm=None):
+        strm = stream if strm is None else strm
         c = caches[i % R]
         c.length = w.T - 1
-        kvq.kvq_quantize_append(c, 1, stream)
+        if args.unfused:
+            kvq.kvq_quantize_append(c, 1, strm)
         if ev is not None:
-            ev[0].record(stream)
-        kvq.kvq_decode_attn(c, q, sm, tau_k, tau_v, out=out, mask_out=mask if i == 0 else None,
-                            workspace=ws[i % R], stream=stream, kernel=kernel, splits=args.splits,
-                            split_done=None if ev is None else ev[1])
+            ev[0].record(strm)
+        call = kvq.kvq_decode_attn if args.unfused else kvq.kvq_append_decode
+        call(c, q, sm, tau_k, tau_v, out=out, mask_out=mask if i == 0 else None, workspace=ws[i % R],
+             stream=strm, kernel=kernel, splits=args.splits, split_done=None if ev is None else ev[1])
         if ev is not None:
-            ev[2].record(stream)
+            ev[2].record(strm)
 
     step(0)
     torch.cuda.synchronize()
@@ -286,11 +290,7 @@ def main():
         for r in range(R):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=side):
-                c = caches[r]
-                c.length = w.T - 1
-                kvq.kvq_quantize_append(c, 1, torch.cuda.current_stream())
-                kvq.kvq_decode_attn(c, q, sm, tau_k, tau_v, out=out, workspace=ws[r],
-                                    stream=torch.cuda.current_stream(), kernel=kernel, splits=args.splits)
+                step(r, strm=torch.cuda.current_stream())
             graphs.append(g)
         torch.cuda.synchronize()
 
@@ -365,6 +365,7 @@ def main():
             "tau_k": tau_k if np.isfinite(tau_k) else "inf", "tau_v": tau_v if np.isfinite(tau_v) else "inf",
             "layers_cycled": R,
             "kernel": args.kernel, "splits": args.splits, "hip_graph": bool(args.graph),
+            "fused_append": not args.unfused,
             "bytes_per_step": step_bytes,
         },
         "roofline": {

@@ -156,8 +156,23 @@ kvq_status kvq_decode_attn(const kvq_cache *c, const uint16_t *q, int32_t q_head
                            float tau_k, float tau_v, uint16_t *out, uint8_t *mask_out,
                            void *workspace, size_t ws_bytes, void *stream);
 
-/* Decode kernel selection and timing, for measurement.  kvq_decode_attn uses
- * KVQ_KERNEL_AUTO; kvq_decode_attn_ex lets a benchmark force a variant and a
+/* One decode step in one launch: quantize-on-append of token `length` of
+ * every sequence (its FP16 rows must already be in k16/v16), then certified
+ * decode attention over length+1 tokens; on success c->length grows by one.
+ * Equivalent to kvq_quantize_append(c, 1, stream) followed by
+ * kvq_decode_attn(): the same tier-1 bytes, block statistics and masks, and
+ * the same output up to the order of floating-point accumulation.  The
+ * matrix-core kernel performs the append itself (every workgroup of a
+ * (batch, KV head) quantizes the new token for its masks, one of them writes
+ * it), saving the append launch; with the VALU kernel the append is a
+ * separate launch.  Errors: as kvq_decode_attn, plus CAPACITY when
+ * length == capacity. */
+kvq_status kvq_append_decode(kvq_cache *c, const uint16_t *q, int32_t q_heads, float sm_scale,
+                             float tau_k, float tau_v, uint16_t *out, uint8_t *mask_out,
+                             void *workspace, size_t ws_bytes, void *stream);
+
+/* Decode kernel selection and timing, for measurement.  kvq_decode_attn and
+ * kvq_append_decode use KVQ_KERNEL_AUTO; the _ex forms let a benchmark force a variant and a
  * split count (0 = automatic), and, when split_done is a hipEvent_t (passed
  * as void*, NULL = none), records it on the stream between the split-K kernel
  * and the merge kernel, so that the split-K kernel can be timed alone.  Same
@@ -168,6 +183,10 @@ kvq_status kvq_decode_attn_ex(const kvq_cache *c, const uint16_t *q, int32_t q_h
                               float sm_scale, float tau_k, float tau_v, uint16_t *out,
                               uint8_t *mask_out, void *workspace, size_t ws_bytes, void *stream,
                               int32_t kernel, int32_t splits, void *split_done);
+kvq_status kvq_append_decode_ex(kvq_cache *c, const uint16_t *q, int32_t q_heads, float sm_scale,
+                                float tau_k, float tau_v, uint16_t *out, uint8_t *mask_out,
+                                void *workspace, size_t ws_bytes, void *stream, int32_t kernel,
+                                int32_t splits, void *split_done);
 
 /* Human-readable name of a status code (static string). */
 const char *kvq_status_str(kvq_status s);

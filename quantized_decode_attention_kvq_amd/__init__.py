@@ -51,7 +51,8 @@ class _Cache(ctypes.Structure):
 
 _lib = None
 EXPORTS = ("kvq_cache_bytes", "kvq_quantize_append", "kvq_bounds", "kvq_decode_workspace_bytes",
-           "kvq_decode_attn", "kvq_decode_attn_ex", "kvq_status_str", "kvq_last_hip_error")
+           "kvq_decode_attn", "kvq_decode_attn_ex", "kvq_append_decode", "kvq_append_decode_ex",
+           "kvq_status_str", "kvq_last_hip_error")
 
 
 def lib_path():
@@ -79,6 +80,10 @@ def lib():
         L.kvq_decode_attn.restype = ctypes.c_int
         L.kvq_decode_attn_ex.argtypes = [CP, P, i32, f32, f32, f32, P, P, P, sz, P, i32, i32, P]
         L.kvq_decode_attn_ex.restype = ctypes.c_int
+        L.kvq_append_decode.argtypes = [CP, P, i32, f32, f32, f32, P, P, P, sz, P]
+        L.kvq_append_decode.restype = ctypes.c_int
+        L.kvq_append_decode_ex.argtypes = [CP, P, i32, f32, f32, f32, P, P, P, sz, P, i32, i32, P]
+        L.kvq_append_decode_ex.restype = ctypes.c_int
         L.kvq_status_str.argtypes = [ctypes.c_int]
         L.kvq_status_str.restype = ctypes.c_char_p
         L.kvq_last_hip_error.argtypes = []
@@ -209,4 +214,25 @@ def kvq_decode_attn(cache: KVCache, q, sm_scale=DEFAULT_SM_SCALE, tau_k=0.0, tau
                                   int(kernel), int(splits),
                                   None if split_done is None else ctypes.c_void_p(split_done.cuda_event))
     _check("kvq_decode_attn", st)
+    return out
+
+
+def kvq_append_decode(cache: KVCache, q, sm_scale=DEFAULT_SM_SCALE, tau_k=0.0, tau_v=0.0, out=None,
+                      mask_out=None, workspace=None, stream=None, kernel=KERNEL_AUTO, splits=0, split_done=None):
+    """One decode step: quantize token cache.length (its fp16 rows already in
+    cache.k16/v16) and attend over cache.length+1 tokens, in one launch of the
+    matrix-core kernel; advances cache.length.  Same arguments and results as
+    kvq_quantize_append(cache, 1) followed by kvq_decode_attn."""
+    _check_q(cache, q)
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        workspace = make_workspace(cache, q.shape[1], q.device)
+    c = cache.c_struct()
+    st = lib().kvq_append_decode_ex(ctypes.byref(c), _ptr(q), q.shape[1], sm_scale, tau_k, tau_v, _ptr(out),
+                                    _ptr(mask_out), _ptr(workspace), workspace.numel(), _stream(stream),
+                                    int(kernel), int(splits),
+                                    None if split_done is None else ctypes.c_void_p(split_done.cuda_event))
+    _check("kvq_append_decode", st)
+    cache.length = int(c.length)
     return out

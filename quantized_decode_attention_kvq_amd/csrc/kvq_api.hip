@@ -208,10 +208,17 @@ size_t kvq_decode_workspace_bytes(const kvq_cache *c, int32_t q_heads) {
     return ws_layout(c, q_heads / c->kv_heads, max_splits(c)).total;
 }
 
-kvq_status kvq_decode_attn_ex(const kvq_cache *c, const uint16_t *q, int32_t q_heads,
-                              float sm_scale, float tau_k, float tau_v, uint16_t *out,
-                              uint8_t *mask_out, void *workspace, size_t ws_bytes, void *stream,
-                              int32_t kernel, int32_t splits, void *split_done) {
+}  // extern "C"
+
+namespace {
+
+// Decode over the cache's tokens; with append, token `length` (already in
+// k16/v16) is first quantized into tier 1 and joins the decode: fused into
+// the matrix-core kernel, or as an append launch before the VALU kernel.
+// On success with append, c->length grows by one.
+kvq_status decode_impl(kvq_cache *c, const uint16_t *q, int32_t q_heads, float sm_scale, float tau_k,
+                       float tau_v, uint16_t *out, uint8_t *mask_out, void *workspace, size_t ws_bytes,
+                       void *stream, int32_t kernel, int32_t splits, void *split_done, bool append) {
     kvq_status st = check_shape(c);
     if (st != KVQ_OK) return st;
     if ((st = check_query(c, q, q_heads, sm_scale, tau_k, tau_v)) != KVQ_OK) return st;
@@ -219,11 +226,13 @@ kvq_status kvq_decode_attn_ex(const kvq_cache *c, const uint16_t *q, int32_t q_h
     if (!out) return KVQ_ERR_INVALID_ARG;
     if (!aligned(out, 16)) return KVQ_ERR_ALIGNMENT;
     if (kernel < KVQ_KERNEL_AUTO || kernel > KVQ_KERNEL_MFMA || splits < 0) return KVQ_ERR_INVALID_ARG;
+    if (append && c->length >= c->capacity) return KVQ_ERR_CAPACITY;
     const int32_t g = q_heads / c->kv_heads;
     if (!workspace || ws_bytes < kvq_decode_workspace_bytes(c, q_heads)) return KVQ_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return KVQ_ERR_ALIGNMENT;
 
-    const int64_t nb = (c->length + kvq::BLK - 1) / kvq::BLK;
+    const int64_t length = c->length + (append ? 1 : 0);  // tokens the decode attends to
+    const int64_t nb = (length + kvq::BLK - 1) / kvq::BLK;
     const int64_t nbc = c->capacity / kvq::BLK;
     if (nb > (int64_t)kvq::MAX_BPS * kvq::MAX_SPLITS) return KVQ_ERR_UNSUPPORTED;
     // the matrix-core kernel lists at most MFMA_MAX_BPS blocks per split
@@ -236,6 +245,12 @@ kvq_status kvq_decode_attn_ex(const kvq_cache *c, const uint16_t *q, int32_t q_h
     const int64_t bps = nb > 0 ? (nb + s - 1) / s : 1;
     const int64_t s_eff = nb > 0 ? (nb + bps - 1) / bps : 1;
 
+    if (append && !mf) {
+        // no fused path in the VALU kernel: append first
+        if ((st = kvq_quantize_append(c, 1, stream)) != KVQ_OK) return st;
+        append = false;
+    }
+
     const WsLayout w = ws_layout(c, g, s_eff);
     kvq::DecodeArgs a;
     a.c = ptrs(c);
@@ -245,7 +260,7 @@ kvq_status kvq_decode_attn_ex(const kvq_cache *c, const uint16_t *q, int32_t q_h
     a.part_ml = reinterpret_cast<float2 *>((char *)workspace + w.ml);
     a.part_acc = reinterpret_cast<float *>((char *)workspace + w.acc);
     a.cap = c->capacity;
-    a.length = c->length;
+    a.length = length;
     a.nbc = nbc;
     a.nb = nb;
     a.hkv = c->kv_heads;
@@ -256,13 +271,27 @@ kvq_status kvq_decode_attn_ex(const kvq_cache *c, const uint16_t *q, int32_t q_h
     a.sm = sm_scale;
     a.tau_k = tau_k;
     a.tau_v = tau_v;
+    a.t_new = append ? c->length : -1;
 
-    hipError_t e = (k == KVQ_KERNEL_MFMA) ? kvq::launch_decode_mfma(a, c->batch, (hipStream_t)stream)
-                                          : kvq::launch_decode_valu(a, c->batch, (hipStream_t)stream);
+    hipError_t e = mf ? kvq::launch_decode_mfma(a, c->batch, (hipStream_t)stream)
+                      : kvq::launch_decode_valu(a, c->batch, (hipStream_t)stream);
     if (e == hipSuccess && split_done) e = hipEventRecord((hipEvent_t)split_done, (hipStream_t)stream);
     if (e == hipSuccess) e = kvq::launch_merge(a, c->batch, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e);
+    if (append) c->length = length;
     return KVQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kvq_status kvq_decode_attn_ex(const kvq_cache *c, const uint16_t *q, int32_t q_heads,
+                              float sm_scale, float tau_k, float tau_v, uint16_t *out,
+                              uint8_t *mask_out, void *workspace, size_t ws_bytes, void *stream,
+                              int32_t kernel, int32_t splits, void *split_done) {
+    return decode_impl(const_cast<kvq_cache *>(c), q, q_heads, sm_scale, tau_k, tau_v, out, mask_out, workspace,
+                       ws_bytes, stream, kernel, splits, split_done, false);
 }
 
 kvq_status kvq_decode_attn(const kvq_cache *c, const uint16_t *q, int32_t q_heads, float sm_scale,
@@ -270,6 +299,21 @@ kvq_status kvq_decode_attn(const kvq_cache *c, const uint16_t *q, int32_t q_head
                            void *workspace, size_t ws_bytes, void *stream) {
     return kvq_decode_attn_ex(c, q, q_heads, sm_scale, tau_k, tau_v, out, mask_out, workspace,
                               ws_bytes, stream, KVQ_KERNEL_AUTO, 0, nullptr);
+}
+
+kvq_status kvq_append_decode_ex(kvq_cache *c, const uint16_t *q, int32_t q_heads, float sm_scale,
+                                float tau_k, float tau_v, uint16_t *out, uint8_t *mask_out,
+                                void *workspace, size_t ws_bytes, void *stream, int32_t kernel,
+                                int32_t splits, void *split_done) {
+    return decode_impl(c, q, q_heads, sm_scale, tau_k, tau_v, out, mask_out, workspace, ws_bytes, stream,
+                       kernel, splits, split_done, true);
+}
+
+kvq_status kvq_append_decode(kvq_cache *c, const uint16_t *q, int32_t q_heads, float sm_scale,
+                             float tau_k, float tau_v, uint16_t *out, uint8_t *mask_out,
+                             void *workspace, size_t ws_bytes, void *stream) {
+    return kvq_append_decode_ex(c, q, q_heads, sm_scale, tau_k, tau_v, out, mask_out, workspace, ws_bytes,
+                                stream, KVQ_KERNEL_AUTO, 0, nullptr);
 }
 
 }  // extern "C"

@@ -52,6 +52,7 @@
 // is ever waited on while later steps are in flight.
 // Waves and splits are merged by log-sum-exp in a second kernel.
 #include "kvq_decode_common.hpp"
+#include "kvq_quant_row.hpp"
 
 namespace kvq {
 
@@ -426,6 +427,39 @@ __device__ __forceinline__ void process_step(const uint8_t *stage, uint32_t mk, 
 
 }  // namespace
 
+// Writes the appended token (position q of a half) into a stage whose code
+// parts were copied from HBM before workgroup 0 of (b, kvh) wrote the token:
+// its 128 key codes (8 slots of 16 B in the key chunks), its key scale
+// dwords, the nibble of each channel's byte and its value-scale dwords.
+// Parts served as FP16 rows (bits of mk) are read from the caller's rows and
+// need nothing.  Called by the whole wave after the stage is resident.
+__device__ __forceinline__ void patch_new_token(uint8_t *stage, uint32_t mk, int q, const uint8_t *nk,
+                                                const uint8_t *nv, uint16_t nks, const uint16_t *nvs,
+                                                int lane) {
+    if (!(mk & 1u)) {
+        const int e = (q >> 2) & 1, mrow = 4 * (q >> 3) + (q & 3);
+        if (lane < 8) {
+            const int dg = lane >> 1, h = lane & 1;
+            *reinterpret_cast<uint4 *>(stage + ST_K + (2 * e + h) * 1024 + 16 * (mrow + 16 * dg)) =
+                *reinterpret_cast<const uint4 *>(nk + 32 * dg + 16 * h);
+        }
+        if (lane == 8) *reinterpret_cast<uint32_t *>(stage + ST_KS + 4 * q) = nks;
+        if (lane == 9) *reinterpret_cast<uint32_t *>(stage + ST_KS + 4 * (q + 32)) = nks;
+    }
+    if (!(mk & 2u)) {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int c = lane + 64 * k;
+            uint8_t *bp = stage + ST_V + (c >> 6) * 1024 + 16 * (c & 63) + (q >> 1);
+            const uint32_t nib = nv[c] & 0x0Fu;
+            *bp = (q & 1) ? (uint8_t)((*bp & 0x0Fu) | (nib << 4)) : (uint8_t)((*bp & 0xF0u) | nib);
+        }
+        if (lane == 10) *reinterpret_cast<uint32_t *>(stage + ST_VS + 4 * q) = (uint32_t)nvs[0] | ((uint32_t)nvs[1] << 16);
+        if (lane == 11)
+            *reinterpret_cast<uint32_t *>(stage + ST_VS + 128 + 4 * q) = (uint32_t)nvs[2] | ((uint32_t)nvs[3] << 16);
+    }
+}
+
 // Entries of the table of blocks that one workgroup's share of steps touches:
 // at most half its steps (every block has two or more) plus the two blocks
 // cut by its range ends.
@@ -499,11 +533,45 @@ __global__ __launch_bounds__(NW * 64, NW / 4) void decode_mfma_kernel(DecodeArgs
         qn = qh;
     }
 
+    // ---------------- fused append: token t_new of (b, kvh) is quantized by
+    // every workgroup of (b, kvh) (wave 0, one 16-lane group), with the same
+    // arithmetic as the append kernel; the statistics of its block then enter
+    // the masks below, workgroup 0 of (b, kvh) writes the token's tier-1 bytes,
+    // and the wave whose step holds the token patches it into its stage.
+    __shared__ __attribute__((aligned(16))) uint8_t nk_lds[D];  // key codes of the new token
+    __shared__ __attribute__((aligned(16))) uint8_t nv_lds[D];  // its value codes (low nibbles)
+    __shared__ uint16_t nks_lds, nvs_lds[4];                     // its key and value scales
+    __shared__ float nerr_lds[2];                                // its key and value errors
+    const int64_t t_new = a.t_new;
+    const int64_t blk_new = t_new >= 0 ? t_new / BLK : -1;
+    const int p_new = t_new >= 0 ? (int)(t_new % BLK) : 0;
+    if (t_new >= 0) {
+        if (wave == 0 && lane < 16) {
+            const int64_t row = bh * a.cap + t_new;
+            const RowQuant rq = quant_row16(a.c.k16 + row * D, a.c.v16 + row * D, lane);
+            *reinterpret_cast<uint2 *>(&nk_lds[8 * lane]) = make_uint2(rq.kc[0], rq.kc[1]);
+            *reinterpret_cast<uint2 *>(&nv_lds[8 * lane]) = make_uint2(rq.vc[0], rq.vc[1]);
+            if ((lane & 3) == 0) nvs_lds[lane >> 2] = (uint16_t)rq.vsb;
+            if (lane == 0) {
+                nks_lds = (uint16_t)rq.ksb;
+                nerr_lds[0] = rq.kerr;
+                nerr_lds[1] = rq.verr;
+            }
+        }
+        __syncthreads();
+    }
+
     // masks of every block of (b, kvh); mask_out receives this workgroup's
     // home range of bps blocks
     {
         const int64_t h0 = (int64_t)split * a.bps, h1 = h0 + a.bps;
         auto put = [&](int i, float kerr, float verr) {
+            if (i == blk_new) {
+                // the block holding the appended token: its statistics after
+                // the append (max with the earlier tokens of the block)
+                kerr = p_new > 0 ? fmaxf(nerr_lds[0], kerr) : nerr_lds[0];
+                verr = p_new > 0 ? fmaxf(nerr_lds[1], verr) : nerr_lds[1];
+            }
             const uint32_t mk = block_mask(a.sm, qn, kerr, verr, a.tau_k, a.tau_v);
             maskb[i] = (uint8_t)mk;
             if (a.mask_out && i >= h0 && i < h1) a.mask_out[bh * a.nb + i] = (uint8_t)mk;
@@ -514,6 +582,36 @@ __global__ __launch_bounds__(NW * 64, NW / 4) void decode_mfma_kernel(DecodeArgs
         for (int i = tid + PF * NT; i < nb; i += NT) put(i, a.c.k_err[bh * a.nbc + i], a.c.v_err[bh * a.nbc + i]);
     }
     __syncthreads();
+
+    // workgroup 0 of (b, kvh) writes the appended token's tier-1 bytes and
+    // its block's statistics (as the append kernel would); no other
+    // workgroup reads them in this launch except through a stage, which the
+    // patch below corrects
+    if (t_new >= 0 && split == 0) {
+        const int64_t row = bh * a.cap + t_new;
+        if (tid < 8) *reinterpret_cast<uint4 *>(a.c.k_codes + row * D + 16 * tid) =
+            *reinterpret_cast<const uint4 *>(&nk_lds[16 * tid]);
+        if (tid == 8) a.c.k_scales[row] = nks_lds;
+        if (tid >= 12 && tid < 16) a.c.v_scales[row * 4 + (tid - 12)] = nvs_lds[tid - 12];
+        uint8_t *vblk = a.c.v_codes + (bh * a.nbc + blk_new) * (D * BLK / 2);
+        if (p_new == 0) {
+            // a new block: byte (c, 0) holds the token's nibble, every other
+            // nibble of the block is 0
+            for (int i = tid; i < D * 2; i += NT)
+                *reinterpret_cast<uint4 *>(vblk + 16 * i) =
+                    make_uint4((i & 1) ? 0u : (uint32_t)(nv_lds[i >> 1] & 0x0Fu), 0u, 0u, 0u);
+        } else if (tid < D) {
+            uint8_t *bp = vblk + tid * (BLK / 2) + (p_new >> 1);
+            const uint32_t nib = nv_lds[tid] & 0x0Fu;
+            *bp = (p_new & 1) ? (uint8_t)((*bp & 0x0Fu) | (nib << 4)) : (uint8_t)nib;
+        }
+        if (tid == 0) {
+            const int64_t si = bh * a.nbc + blk_new;
+            const float ko = a.c.k_err[si], vo = a.c.v_err[si];
+            a.c.k_err[si] = p_new > 0 ? fmaxf(nerr_lds[0], ko) : nerr_lds[0];
+            a.c.v_err[si] = p_new > 0 ? fmaxf(nerr_lds[1], vo) : nerr_lds[1];
+        }
+    }
 
     // Work of (b, kvh) in steps: 2 per certified block (its halves), 8 per
     // fallback block (its 8-token steps).  Split s takes steps [r0, r1) of the
@@ -661,7 +759,9 @@ __global__ __launch_bounds__(NW * 64, NW / 4) void decode_mfma_kernel(DecodeArgs
         int sub;
         uint32_t mk;
         find(pwin, t, blk, sub, mk);
-        const uint8_t *stage = &ring[wave][s][0];
+        uint8_t *stage = &ring[wave][s][0];
+        if (blk == blk_new && (mk ? (p_new >> 3) == sub : (p_new >> 5) == sub))
+            patch_new_token(stage, mk, p_new & 31, nk_lds, nv_lds, nks_lds, nvs_lds, lane);
         // positions [p_lo, p_hi) of the half: the valid tokens of the step
         const int step_len = mk ? 8 : 32;
         const int p_lo = mk ? 8 * (sub & 3) : 0;

@@ -51,6 +51,7 @@ struct DecodeArgs {
     int32_t hkv, hq, g;
     int32_t splits, bps;  // number of splits and blocks per split
     float sm, tau_k, tau_v;
+    int64_t t_new;  // token appended by this launch (fused append), or -1
 };
 
 // Upper limits that size the workspace and LDS tables.

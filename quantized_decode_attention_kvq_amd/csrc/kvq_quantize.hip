@@ -13,48 +13,10 @@
 // lanes for a 32-channel value group, and the fixed fp64 tree for ||k - k^||.
 // Value nibbles are staged as bytes in LDS and packed channel-major on the way
 // out; key codes go straight from registers to HBM (128 B per row, coalesced).
-#include "kvq_device.hpp"
 #include "kvq_internal.hpp"
+#include "kvq_quant_row.hpp"
 
 namespace kvq {
-
-__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
-
-// Max of |x| over the 8 fp16 values of a lane, as a bit pattern (for
-// non-negative fp16 the bit pattern orders like the value; Inf and NaN sort
-// above every finite value).
-__device__ __forceinline__ uint32_t absmax_bits(const uint32_t w[4]) {
-    uint32_t m = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) m = umax(m, umax(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
-    return m;
-}
-
-__device__ __forceinline__ float elem(const uint32_t w[4], int k) {
-    return h2f((k & 1) ? (w[k >> 1] >> 16) : (w[k >> 1] & 0xFFFFu));
-}
-
-// round_half_even(x / s) clamped to [-lim, lim], for fp16 values x and s > 0,
-// with r ~ 1/s (any estimate within a few ulps) and hs = s/2.  The estimate
-// rint(x*r) is off by at most one, and only next to a half-integer; the
-// residual x - c*s is exact in fp32 (c*s has at most 19 significant bits, and
-// x and c*s lie on the grid of the smaller of their fp16 ulps whenever c is
-// nonzero), so comparing it with s/2 -- ties going to the even code --
-// corrects the estimate exactly.  r == 0 marks a zero scale.  Returns the
-// code; e receives x - c*s for the final (clamped) code, also exact.
-__device__ __forceinline__ int quant_code(float x, float s, float r, float hs, int lim, float &e) {
-    float c = __builtin_rintf(x * r);
-    const float d = __builtin_fmaf(-c, s, x);
-    const bool odd = ((int)c & 1) != 0;
-    if (d > hs || (d == hs && odd))
-        c += 1.0f;
-    else if (d < -hs || (d == -hs && odd))
-        c -= 1.0f;
-    c = __builtin_fminf(__builtin_fmaxf(c, (float)-lim), (float)lim);
-    c = r == 0.0f ? 0.0f : c;  // zero scale (also rows holding Inf/NaN): code 0
-    e = __builtin_fmaf(-c, s, x);
-    return (int)c;
-}
 
 __global__ __launch_bounds__(256) void quantize_append_kernel(AppendArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t vtile[BLK][D];  // new value codes (low nibble), [token][channel]
@@ -80,60 +42,10 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(AppendArgs a) {
         if (t < t_begin || t >= t_end) continue;
         const int64_t roff = (row_base + t) * D + 8 * lane16;
 
-        // ---------------- key row: int8 per token, scale absmax/127
-        const uint4 kr = *reinterpret_cast<const uint4 *>(a.c.k16 + roff);
-        const uint32_t kw[4] = {kr.x, kr.y, kr.z, kr.w};
-        uint32_t am = absmax_bits(kw);
-        am = umax(am, __shfl_xor(am, 1));
-        am = umax(am, __shfl_xor(am, 2));
-        am = umax(am, __shfl_xor(am, 4));
-        am = umax(am, __shfl_xor(am, 8));
-        const bool knonfin = am >= 0x7C00u;
-        const uint32_t ksb = knonfin ? 0u : f2h_rn(__fdiv_rn(h2f(am), 127.0f));
-        const float ks = h2f(ksb);
-        // a zero scale (tiny, all-zero or non-finite row) gives codes 0
-        const float kr_ = ks != 0.0f ? __builtin_amdgcn_rcpf(ks) : 0.0f;
-        const float khs = ks != 0.0f ? 0.5f * ks : __builtin_huge_valf();
-        uint32_t kc[2] = {0u, 0u};
-        double sq[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const float x = elem(kw, k);
-            float e;
-            const int c = quant_code(x, ks, kr_, khs, 127, e);
-            sq[k] = sq64(e);
-            kc[k >> 2] |= ((uint32_t)c & 0xFFu) << (8 * (k & 3));
-        }
-        const double ss = tree128(sq);
-        const float kerr = knonfin ? __builtin_huge_valf() : (float)__dsqrt_rn(ss);
-
-        // ---------------- value row: int4 per 32-channel group, scale absmax/7
-        const uint4 vr = *reinterpret_cast<const uint4 *>(a.c.v16 + roff);
-        const uint32_t vw[4] = {vr.x, vr.y, vr.z, vr.w};
-        uint32_t vm = absmax_bits(vw);
-        vm = umax(vm, __shfl_xor(vm, 1));
-        vm = umax(vm, __shfl_xor(vm, 2));
-        const bool vnonfin = vm >= 0x7C00u;
-        const uint32_t vsb = vnonfin ? 0u : f2h_rn(__fdiv_rn(h2f(vm), 7.0f));
-        const float vs = h2f(vsb);
-        const float vr_ = vs != 0.0f ? __builtin_amdgcn_rcpf(vs) : 0.0f;
-        const float vhs = vs != 0.0f ? 0.5f * vs : __builtin_huge_valf();
-        uint32_t vc[2] = {0u, 0u};
-        float verr = 0.0f;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const float x = elem(vw, k);
-            float e;
-            const int c = quant_code(x, vs, vr_, vhs, 7, e);
-            e = __builtin_fabsf(e);
-            verr = verr > e ? verr : e;
-            vc[k >> 2] |= ((uint32_t)c & 0x0Fu) << (8 * (k & 3));
-        }
-        verr = vnonfin ? __builtin_huge_valf() : verr;
-        verr = fmaxf(verr, __shfl_xor(verr, 1));
-        verr = fmaxf(verr, __shfl_xor(verr, 2));
-        verr = fmaxf(verr, __shfl_xor(verr, 4));  // row: max over the 4 groups
-        verr = fmaxf(verr, __shfl_xor(verr, 8));
+        const RowQuant rq = quant_row16(a.c.k16 + (row_base + t) * D, a.c.v16 + (row_base + t) * D, lane16);
+        const uint32_t kc[2] = {rq.kc[0], rq.kc[1]}, vc[2] = {rq.vc[0], rq.vc[1]};
+        const uint32_t ksb = rq.ksb, vsb = rq.vsb;
+        const float kerr = rq.kerr, verr = rq.verr;
 
         *reinterpret_cast<uint2 *>(a.c.k_codes + roff) = make_uint2(kc[0], kc[1]);
         if (lane16 == 0) a.c.k_scales[row_base + t] = (uint16_t)ksb;

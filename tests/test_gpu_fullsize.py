@@ -1,6 +1,7 @@
 """GPU parity at the workloads' full sizes, in the launch configuration the
-benchmark times (kvq_decode_attn with the automatic kernel and split choice,
-after a bulk prefill and a one-token append).
+benchmark times (kvq_append_decode with the automatic kernel and split
+choice: one fused append of the last token and decode, after a bulk
+prefill).
 
 The oracle cannot process a whole 32k- or 128k-token batch in seconds, so it
 checks sampled (batch, KV head) groups one by one: the group's tier-1 bytes,
@@ -54,14 +55,17 @@ def test_decode_full_size_sampled(name):
     print(f"[full size] {w}", flush=True)
     d = workloads.make(w, "cuda")
     c = kvq.KVCache(w.B, w.Hkv, w.cap, k16=d["k16"], v16=d["v16"])
-    kvq.kvq_quantize_append(c, w.T - 1)
-    kvq.kvq_quantize_append(c, 1)
     q = d["q"].contiguous()
+    # tolerances from the bounds of the full cache (as the benchmark does)
+    kvq.kvq_quantize_append(c, w.T)
     kb, vb, _ = kvq.kvq_bounds(c, q, SM, 0.0, 0.0, want=("kb", "vb"))
     tk, tv = _taus(kb, vb, w.fallback_frac)
+    # the benchmark's step: prefill T-1 tokens, then one fused append + decode
+    c.length = w.T - 1
+    mask = torch.full(kb.shape, 0xEE, dtype=torch.uint8, device="cuda")
+    out = kvq.kvq_append_decode(c, q, SM, tk, tv, mask_out=mask)
+    assert c.length == w.T
     _, _, bmask = kvq.kvq_bounds(c, q, SM, tk, tv, want=("mask",))
-    mask = torch.full_like(bmask, 0xEE)
-    out = kvq.kvq_decode_attn(c, q, SM, tk, tv, mask_out=mask)
     torch.cuda.synchronize()
     # every group: the masks used are the bounds' masks
     assert torch.equal(mask, bmask)
