@@ -488,6 +488,23 @@ __global__ __launch_bounds__(NW * 64, NW / 4) void decode_mfma_kernel(DecodeArgs
     const int nb = (int)a.nb;
     constexpr int NT = NW * 64;
 
+    // fused append: token t_new of (b, kvh) is quantized by every workgroup
+    // of (b, kvh), in the 16-lane group holding the mask thread of its block
+    // (block i has thread i % NT), with the same arithmetic as the append
+    // kernel; that thread puts the token's statistics into its block's mask,
+    // workgroup 0 of (b, kvh) writes the token's tier-1 bytes, and the wave
+    // whose step holds the token patches it into its stage.  Its rows are
+    // loaded first, with the block statistics and the query rows.
+    const int64_t t_new = a.t_new;
+    const int64_t blk_new = t_new >= 0 ? t_new / BLK : -1;
+    const int p_new = t_new >= 0 ? (int)(t_new % BLK) : 0;
+    const bool qgroup = t_new >= 0 && (tid >> 4) == (int)((blk_new % NT) >> 4);
+    RowIn rin;
+    if (qgroup) {
+        const int64_t row = bh * a.cap + t_new;
+        rin = load_row16(a.c.k16 + row * D, a.c.v16 + row * D, tid & 15);
+    }
+
     // block statistics of the first PF * NT blocks, fetched while the query
     // rows load
     constexpr int PF = 4;
@@ -533,32 +550,22 @@ __global__ __launch_bounds__(NW * 64, NW / 4) void decode_mfma_kernel(DecodeArgs
         qn = qh;
     }
 
-    // ---------------- fused append: token t_new of (b, kvh) is quantized by
-    // every workgroup of (b, kvh) (wave 0, one 16-lane group), with the same
-    // arithmetic as the append kernel; the statistics of its block then enter
-    // the masks below, workgroup 0 of (b, kvh) writes the token's tier-1 bytes,
-    // and the wave whose step holds the token patches it into its stage.
     __shared__ __attribute__((aligned(16))) uint8_t nk_lds[D];  // key codes of the new token
     __shared__ __attribute__((aligned(16))) uint8_t nv_lds[D];  // its value codes (low nibbles)
     __shared__ uint16_t nks_lds, nvs_lds[4];                     // its key and value scales
     __shared__ float nerr_lds[2];                                // its key and value errors
-    const int64_t t_new = a.t_new;
-    const int64_t blk_new = t_new >= 0 ? t_new / BLK : -1;
-    const int p_new = t_new >= 0 ? (int)(t_new % BLK) : 0;
-    if (t_new >= 0) {
-        if (wave == 0 && lane < 16) {
-            const int64_t row = bh * a.cap + t_new;
-            const RowQuant rq = quant_row16(a.c.k16 + row * D, a.c.v16 + row * D, lane);
-            *reinterpret_cast<uint2 *>(&nk_lds[8 * lane]) = make_uint2(rq.kc[0], rq.kc[1]);
-            *reinterpret_cast<uint2 *>(&nv_lds[8 * lane]) = make_uint2(rq.vc[0], rq.vc[1]);
-            if ((lane & 3) == 0) nvs_lds[lane >> 2] = (uint16_t)rq.vsb;
-            if (lane == 0) {
-                nks_lds = (uint16_t)rq.ksb;
-                nerr_lds[0] = rq.kerr;
-                nerr_lds[1] = rq.verr;
-            }
+    RowQuant rq = {};
+    if (qgroup) {
+        rq = quant_row16(rin);
+        const int l16 = tid & 15;
+        *reinterpret_cast<uint2 *>(&nk_lds[8 * l16]) = make_uint2(rq.kc[0], rq.kc[1]);
+        *reinterpret_cast<uint2 *>(&nv_lds[8 * l16]) = make_uint2(rq.vc[0], rq.vc[1]);
+        if ((l16 & 3) == 0) nvs_lds[l16 >> 2] = (uint16_t)rq.vsb;
+        if (l16 == 0) {
+            nks_lds = (uint16_t)rq.ksb;
+            nerr_lds[0] = rq.kerr;
+            nerr_lds[1] = rq.verr;
         }
-        __syncthreads();
     }
 
     // masks of every block of (b, kvh); mask_out receives this workgroup's
@@ -567,10 +574,11 @@ __global__ __launch_bounds__(NW * 64, NW / 4) void decode_mfma_kernel(DecodeArgs
         const int64_t h0 = (int64_t)split * a.bps, h1 = h0 + a.bps;
         auto put = [&](int i, float kerr, float verr) {
             if (i == blk_new) {
-                // the block holding the appended token: its statistics after
-                // the append (max with the earlier tokens of the block)
-                kerr = p_new > 0 ? fmaxf(nerr_lds[0], kerr) : nerr_lds[0];
-                verr = p_new > 0 ? fmaxf(nerr_lds[1], verr) : nerr_lds[1];
+                // the block holding the appended token (this thread is in the
+                // lane group that quantized it): its statistics after the
+                // append (max with the earlier tokens of the block)
+                kerr = p_new > 0 ? fmaxf(rq.kerr, kerr) : rq.kerr;
+                verr = p_new > 0 ? fmaxf(rq.verr, verr) : rq.verr;
             }
             const uint32_t mk = block_mask(a.sm, qn, kerr, verr, a.tau_k, a.tau_v);
             maskb[i] = (uint8_t)mk;
@@ -601,15 +609,27 @@ __global__ __launch_bounds__(NW * 64, NW / 4) void decode_mfma_kernel(DecodeArgs
                 *reinterpret_cast<uint4 *>(vblk + 16 * i) =
                     make_uint4((i & 1) ? 0u : (uint32_t)(nv_lds[i >> 1] & 0x0Fu), 0u, 0u, 0u);
         } else if (tid < D) {
-            uint8_t *bp = vblk + tid * (BLK / 2) + (p_new >> 1);
-            const uint32_t nib = nv_lds[tid] & 0x0Fu;
-            *bp = (p_new & 1) ? (uint8_t)((*bp & 0x0Fu) | (nib << 4)) : (uint8_t)nib;
+            // replace the token's nibble in its byte with two atomics (clear,
+            // then set; same address, so in order) rather than a read-back
+            // that would hold this wave until the load returns
+            const int byte = tid * (BLK / 2) + (p_new >> 1);
+            const int sh = 8 * (byte & 3) + 4 * (p_new & 1);
+            unsigned int *word = reinterpret_cast<unsigned int *>(vblk + (byte & ~3));
+            atomicAnd(word, ~(0x0Fu << sh));
+            atomicOr(word, (uint32_t)(nv_lds[tid] & 0x0Fu) << sh);
         }
         if (tid == 0) {
+            // block statistics: max with the earlier tokens' (non-negative
+            // floats and +Inf order like their bit patterns), or the token's
+            // own for a new block
             const int64_t si = bh * a.nbc + blk_new;
-            const float ko = a.c.k_err[si], vo = a.c.v_err[si];
-            a.c.k_err[si] = p_new > 0 ? fmaxf(nerr_lds[0], ko) : nerr_lds[0];
-            a.c.v_err[si] = p_new > 0 ? fmaxf(nerr_lds[1], vo) : nerr_lds[1];
+            if (p_new > 0) {
+                atomicMax(reinterpret_cast<unsigned int *>(a.c.k_err + si), __float_as_uint(nerr_lds[0]));
+                atomicMax(reinterpret_cast<unsigned int *>(a.c.v_err + si), __float_as_uint(nerr_lds[1]));
+            } else {
+                a.c.k_err[si] = nerr_lds[0];
+                a.c.v_err[si] = nerr_lds[1];
+            }
         }
     }
 

@@ -51,20 +51,33 @@ __device__ __forceinline__ int quant_code(float x, float s, float r, float hs, i
 }
 
 // One token row quantized by a group of 16 lanes (lane16 holds channels
-// 8*lane16 .. +7).  Every lane returns its 8 key codes (bytes), its 8 value
-// codes (low nibble of each byte), the row's key scale and key error, its
-// 32-channel group's value scale, and the row's value error (max over the
-// four groups).  Uses xor-shuffles within the 16-lane group only.
+// 8*lane16 .. +7; load_row16 lets the caller issue the loads early).  Every
+// lane returns its 8 key codes (bytes), its 8 value codes (low nibble of each
+// byte), the row's key scale and key error, its 32-channel group's value
+// scale, and the row's value error (max over the four groups).  Uses
+// xor-shuffles within the 16-lane group only.
 struct RowQuant {
     uint32_t kc[2], vc[2];
     uint32_t ksb, vsb;
     float kerr, verr;
 };
 
-__device__ __forceinline__ RowQuant quant_row16(const uint16_t *k16row, const uint16_t *v16row, int lane16) {
+// The raw fp16 channels of one token row held by a lane: keys and values.
+struct RowIn {
+    uint4 k, v;
+};
+
+__device__ __forceinline__ RowIn load_row16(const uint16_t *k16row, const uint16_t *v16row, int lane16) {
+    RowIn r;
+    r.k = *reinterpret_cast<const uint4 *>(k16row + 8 * lane16);
+    r.v = *reinterpret_cast<const uint4 *>(v16row + 8 * lane16);
+    return r;
+}
+
+__device__ __forceinline__ RowQuant quant_row16(const RowIn &in) {
     RowQuant o;
     // ---------------- key row: int8 per token, scale absmax/127
-    const uint4 kr = *reinterpret_cast<const uint4 *>(k16row + 8 * lane16);
+    const uint4 kr = in.k;
     const uint32_t kw[4] = {kr.x, kr.y, kr.z, kr.w};
     uint32_t am = absmax_bits(kw);
     am = umax(am, __shfl_xor(am, 1));
@@ -91,7 +104,7 @@ __device__ __forceinline__ RowQuant quant_row16(const uint16_t *k16row, const ui
     const float kerr = knonfin ? __builtin_huge_valf() : (float)__dsqrt_rn(ss);
 
     // ---------------- value row: int4 per 32-channel group, scale absmax/7
-    const uint4 vr = *reinterpret_cast<const uint4 *>(v16row + 8 * lane16);
+    const uint4 vr = in.v;
     const uint32_t vw[4] = {vr.x, vr.y, vr.z, vr.w};
     uint32_t vm = absmax_bits(vw);
     vm = umax(vm, __shfl_xor(vm, 1));
@@ -127,6 +140,10 @@ __device__ __forceinline__ RowQuant quant_row16(const uint16_t *k16row, const ui
     o.kerr = kerr;
     o.verr = verr;
     return o;
+}
+
+__device__ __forceinline__ RowQuant quant_row16(const uint16_t *k16row, const uint16_t *v16row, int lane16) {
+    return quant_row16(load_row16(k16row, v16row, lane16));
 }
 
 }  // namespace kvq
