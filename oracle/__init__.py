@@ -60,6 +60,9 @@ def lib():
         L.kvqo_attention.argtypes = [i32, i32, i32, i64, i64, P, f32, f32, f32,
                                      P, P, P, P, P, P, P, P, P, P]
         L.kvqo_attention.restype = None
+        L.kvqo_certificate.argtypes = [i32, i32, i32, i64, i64, P, f32, f32, f32, ctypes.c_double,
+                                       P, P, P, P, P, P, P, P, P, P, P, P, P]
+        L.kvqo_certificate.restype = None
         _lib = L
     return _lib
 
@@ -191,6 +194,24 @@ class Cache:
                              _p(self.v_codes), _p(self.v_scales), _p(self.k_err), _p(self.v_err),
                              _p(out), _p(mask))
         return out, mask[:, :, : self.nblocks]
+
+
+    def certificate(self, q, sm, tau_k, tau_v, tau_out=float("inf")):
+        """Per-head certificate and rung-3 recompute (see kvqo_certificate):
+        dict of out (fp64 [B][Hq][128], recomputed heads dense), cert, e_key,
+        e_val (fp64 [B][Hq]) and recomputed (uint8 [B][Hq])."""
+        q = _c(q, np.float16)
+        B, Hq, d = q.shape
+        assert B == self.B and d == D and Hq % self.Hkv == 0
+        r = {k: np.zeros((B, Hq), np.float64) for k in ("cert", "e_key", "e_val")}
+        r["out"] = np.zeros((B, Hq, D), np.float64)
+        r["recomputed"] = np.zeros((B, Hq), np.uint8)
+        lib().kvqo_certificate(B, Hq, self.Hkv, self.cap, self.length, _p(q), sm, tau_k, tau_v,
+                               float(tau_out), _p(self.k16), _p(self.v16), _p(self.k_codes),
+                               _p(self.k_scales), _p(self.v_codes), _p(self.v_scales), _p(self.k_err),
+                               _p(self.v_err), _p(r["out"]), _p(r["cert"]), _p(r["e_key"]),
+                               _p(r["e_val"]), _p(r["recomputed"]))
+        return r
 
 
 def tau_for_fraction(values, frac):

@@ -426,3 +426,153 @@ void kvqo_attention(int B, int Hq, int Hkv, int64_t cap, int64_t length, const u
     if (!mask)
         free(m);
 }
+
+/* ------------------------------------------------------------ certificate */
+
+/* Per-head output certificate and per-head recompute ("Runtime-Certified
+ * Bounded-Error Quantized Attention", technical summary, Methodology 2,
+ * "Two-Term Error Decomposition", and Methodology 3, rung 3 of the fallback
+ * ladder, "Per-Head Fallback").  For every (b, query head h):
+ *   p^   : the softmax weights of the decode above (keys k~ per the masks);
+ *   o^   : sum_t p^_t v~_t, the decode output;
+ *   o    : the dense output over the FP16 keys and values.
+ * Reading of the two terms (the page names them, prints no formula):
+ *   key term   E_key = tanh(Delta/2) * R.  Every key-certified block moves a
+ *              logit by at most sm*qn_h*k_err (Cauchy-Schwarz; qn_h is this
+ *              head's own norm), fallback blocks not at all, so all logit
+ *              moves lie in [-Delta, Delta] with
+ *              Delta = sm*qn_h*max{k_err_b : b key-certified}; then the total
+ *              variation between the dense and the decode softmax is at most
+ *              tanh(Delta/2), and sum_t (p_t - p^_t) v_tj is at most that times
+ *              the range of channel j over the tokens, bounded by
+ *              R = 2*max(7*S + eta_max, A): S is the largest value scale of a
+ *              value-certified token (|v~| <= 7*S there), eta_max the largest
+ *              v_err of a value-certified block (|v - v~| <= eta_max), A the
+ *              largest |v| of a value-fallback token.
+ *   value term E_val = sum over value-certified blocks b of m^_b * v_err_b,
+ *              m^_b = sum_{t in b} p^_t, which bounds sum_t p^_t (v_t - v~_t).
+ * Since o - o^ = sum_t (p_t - p^_t) v_t + sum_t p^_t (v_t - v~_t), every
+ * |o_j - o^_j| <= cert = E_key + E_val (exact arithmetic).
+ * Rung 3: a head with cert > tau_out is recomputed on the FP16 keys and
+ * values: its output is o and recomputed[h] = 1.
+ * out, cert, e_key, e_val: double [B][Hq](x128 for out); recomputed uint8
+ * [B][Hq].  length == 0 gives zeros. */
+void kvqo_certificate(int B, int Hq, int Hkv, int64_t cap, int64_t length, const uint16_t *q,
+                      float sm, float tau_k, float tau_v, double tau_out, const uint16_t *k16,
+                      const uint16_t *v16, const int8_t *k_codes, const uint16_t *k_scales,
+                      const uint8_t *v_codes, const uint16_t *v_scales, const float *k_err,
+                      const float *v_err, double *out, double *cert, double *e_key, double *e_val,
+                      uint8_t *recomputed)
+{
+    int G = Hq / Hkv;
+    int64_t nblk = (length + BLK - 1) / BLK;
+    uint8_t *m = (uint8_t *)malloc((size_t)B * Hkv * (size_t)(nblk ? nblk : 1));
+    kvqo_bounds(B, Hq, Hkv, cap, length, q, sm, tau_k, tau_v, k_err, v_err, NULL, NULL, m);
+
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int b = 0; b < B; ++b)
+        for (int hq = 0; hq < Hq; ++hq) {
+            int h = hq / G;
+            size_t oi = (size_t)b * Hq + hq;
+            const uint8_t *mb = m + ((size_t)b * Hkv + h) * (size_t)nblk;
+            double qv[D];
+            for (int j = 0; j < D; ++j)
+                qv[j] = kvqo_f16_to_f64(q[oi * D + j]);
+            double *o = out + oi * D;
+            for (int j = 0; j < D; ++j)
+                o[j] = 0.0;
+            cert[oi] = e_key[oi] = e_val[oi] = 0.0;
+            recomputed[oi] = 0;
+            if (length == 0)
+                continue;
+            /* the decode's weights and output */
+            double *logit = (double *)malloc(sizeof(double) * (size_t)length);
+            double *dlogit = (double *)malloc(sizeof(double) * (size_t)length);
+            double mx = -INFINITY, dmx = -INFINITY;
+            for (int64_t t = 0; t < length; ++t) {
+                size_t r = row_index(b, h, t, Hkv, cap);
+                int fbk = mb[t / BLK] & 1;
+                double s = kvqo_f16_to_f64(k_scales[r]);
+                double acc = 0.0, dacc = 0.0;
+                for (int j = 0; j < D; ++j) {
+                    double k16v = kvqo_f16_to_f64(k16[r * D + j]);
+                    double k = fbk ? k16v : s * (double)k_codes[r * D + j];
+                    acc += qv[j] * k;
+                    dacc += qv[j] * k16v;
+                }
+                logit[t] = (double)sm * acc;
+                dlogit[t] = (double)sm * dacc;
+                if (logit[t] > mx)
+                    mx = logit[t];
+                if (dlogit[t] > dmx)
+                    dmx = dlogit[t];
+            }
+            double wsum = 0.0, dsum = 0.0;
+            for (int64_t t = 0; t < length; ++t) {
+                wsum += exp(logit[t] - mx);
+                dsum += exp(dlogit[t] - dmx);
+            }
+            double od[D];
+            for (int j = 0; j < D; ++j)
+                od[j] = 0.0;
+            double kmax = 0.0, etamax = 0.0, smax = 0.0, amax = 0.0, ev = 0.0;
+            double mass = 0.0; /* m^ of the current block */
+            for (int64_t t = 0; t < length; ++t) {
+                size_t r = row_index(b, h, t, Hkv, cap);
+                int64_t blk = t / BLK;
+                int fbk = mb[blk] & 1, fbv = (mb[blk] >> 1) & 1;
+                size_t si = blk_index(b, h, blk, Hkv, cap);
+                double p = exp(logit[t] - mx) / wsum;
+                double pd = exp(dlogit[t] - dmx) / dsum;
+                if (!fbk && (double)k_err[si] > kmax)
+                    kmax = (double)k_err[si];
+                if (!fbv && (double)v_err[si] > etamax)
+                    etamax = (double)v_err[si];
+                for (int g = 0; g < D / VG; ++g) {
+                    double sv = kvqo_f16_to_f64(v_scales[r * (D / VG) + g]);
+                    if (!fbv && sv > smax)
+                        smax = sv;
+                }
+                for (int j = 0; j < D; ++j) {
+                    double v16j = kvqo_f16_to_f64(v16[r * D + j]);
+                    double v;
+                    if (fbv) {
+                        v = v16j;
+                        if (fabs(v16j) > amax)
+                            amax = fabs(v16j);
+                    } else {
+                        int high;
+                        size_t ob = v_byte(b, h, t, j, Hkv, cap, &high);
+                        int nib = high ? (v_codes[ob] >> 4) : (v_codes[ob] & 0x0F);
+                        int c = nib >= 8 ? nib - 16 : nib;
+                        v = kvqo_f16_to_f64(v_scales[r * (D / VG) + j / VG]) * (double)c;
+                    }
+                    o[j] += p * v;
+                    od[j] += pd * v16j;
+                }
+                /* value term: the block's mass times its value error */
+                mass += p;
+                if (t % BLK == BLK - 1 || t == length - 1) {
+                    if (!fbv)
+                        ev += mass * (double)v_err[si];
+                    mass = 0.0;
+                }
+            }
+            double qn = (double)kvqo_qnorm(q + oi * D);
+            double delta = (double)sm * qn * kmax;
+            double r2 = 7.0 * smax + etamax;
+            double rng = 2.0 * (r2 > amax ? r2 : amax);
+            double ek = tanh(delta / 2.0) * rng;
+            e_key[oi] = ek;
+            e_val[oi] = ev;
+            cert[oi] = ek + ev;
+            if (cert[oi] > tau_out) {
+                recomputed[oi] = 1;
+                for (int j = 0; j < D; ++j)
+                    o[j] = od[j];
+            }
+            free(logit);
+            free(dlogit);
+        }
+    free(m);
+}
