@@ -171,6 +171,36 @@ kvq_status kvq_append_decode(kvq_cache *c, const uint16_t *q, int32_t q_heads, f
                              float tau_k, float tau_v, uint16_t *out, uint8_t *mask_out,
                              void *workspace, size_t ws_bytes, void *stream);
 
+/* Certified decode with a per-head output certificate and per-head FP16
+ * recompute ("Runtime-Certified Bounded-Error Quantized Attention",
+ * Methodology 2, two-term error decomposition; Methodology 3, rung 3 of the
+ * fallback ladder, per-head fallback).  As kvq_decode_attn (or, with
+ * append != 0, as kvq_append_decode: token `length` is quantized first and
+ * c->length grows by one), and in addition, for every query head h:
+ *   cert [B][q_heads] (float, required) receives E_key + E_val, a bound on
+ *     max_j |o_dense[h][j] - o[h][j]| between the decode output and dense
+ *     FP16 attention, in exact arithmetic: E_key = tanh(Delta/2)*R with
+ *     Delta = sm*||q_h||*(largest key error of a key-certified block) and
+ *     R = 2*max(7*S + eta, A) (S: largest value scale of a value-certified
+ *     token, eta: largest value error of a value-certified block, A: largest
+ *     |v| of a value-fallback token); E_val = sum over value-certified blocks
+ *     of (attention mass of the block) * (its value error).  Rounded up to
+ *     fp32; the kernel's own floating-point rounding is not included.
+ *   heads with cert > tau_out are recomputed over the FP16 keys and values
+ *     (their out rows become the dense result) and get recomputed[h] = 1
+ *     (recomputed [B][q_heads] uint8, may be NULL).  tau_out = +INFINITY
+ *     skips the recompute launches.
+ * Runs on the matrix-core kernel only (KVQ_ERR_UNSUPPORTED where
+ * kvq_decode_attn would pick the VALU kernel).  The recompute costs two more
+ * launches (a decode and a merge restricted on the device to the groups and
+ * heads flagged), whatever the flags.  Errors: as kvq_decode_attn; also
+ * INVALID_ARG for cert == NULL or a NaN tau_out, CAPACITY for append at
+ * length == capacity. */
+kvq_status kvq_decode_attn_cert(kvq_cache *c, const uint16_t *q, int32_t q_heads, float sm_scale,
+                                float tau_k, float tau_v, float tau_out, int32_t append, uint16_t *out,
+                                float *cert, uint8_t *recomputed, uint8_t *mask_out, void *workspace,
+                                size_t ws_bytes, void *stream);
+
 /* Decode kernel selection and timing, for measurement.  kvq_decode_attn and
  * kvq_append_decode use KVQ_KERNEL_AUTO; the _ex forms let a benchmark force a variant and a
  * split count (0 = automatic), and, when split_done is a hipEvent_t (passed

@@ -52,7 +52,7 @@ class _Cache(ctypes.Structure):
 _lib = None
 EXPORTS = ("kvq_cache_bytes", "kvq_quantize_append", "kvq_bounds", "kvq_decode_workspace_bytes",
            "kvq_decode_attn", "kvq_decode_attn_ex", "kvq_append_decode", "kvq_append_decode_ex",
-           "kvq_status_str", "kvq_last_hip_error")
+           "kvq_decode_attn_cert", "kvq_status_str", "kvq_last_hip_error")
 
 
 def lib_path():
@@ -84,6 +84,8 @@ def lib():
         L.kvq_append_decode.restype = ctypes.c_int
         L.kvq_append_decode_ex.argtypes = [CP, P, i32, f32, f32, f32, P, P, P, sz, P, i32, i32, P]
         L.kvq_append_decode_ex.restype = ctypes.c_int
+        L.kvq_decode_attn_cert.argtypes = [CP, P, i32, f32, f32, f32, f32, i32, P, P, P, P, P, sz, P]
+        L.kvq_decode_attn_cert.restype = ctypes.c_int
         L.kvq_status_str.argtypes = [ctypes.c_int]
         L.kvq_status_str.restype = ctypes.c_char_p
         L.kvq_last_hip_error.argtypes = []
@@ -236,3 +238,30 @@ def kvq_append_decode(cache: KVCache, q, sm_scale=DEFAULT_SM_SCALE, tau_k=0.0, t
     _check("kvq_append_decode", st)
     cache.length = int(c.length)
     return out
+
+
+def kvq_decode_attn_cert(cache: KVCache, q, sm_scale=DEFAULT_SM_SCALE, tau_k=0.0, tau_v=0.0,
+                         tau_out=float("inf"), append=False, out=None, cert=None, recomputed=None,
+                         mask_out=None, workspace=None, stream=None):
+    """Certified decode with a per-head output certificate (float32 [B][Hq])
+    and recompute on FP16 of the heads whose certificate exceeds tau_out
+    (recomputed: uint8 [B][Hq], 1 for those heads).  With append, token
+    cache.length is quantized first and cache.length advances.  Returns
+    (out, cert, recomputed)."""
+    _check_q(cache, q)
+    B, Hq = q.shape[0], q.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    if cert is None:
+        cert = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if recomputed is None:
+        recomputed = torch.empty((B, Hq), dtype=torch.uint8, device=q.device)
+    if workspace is None:
+        workspace = make_workspace(cache, Hq, q.device)
+    c = cache.c_struct()
+    st = lib().kvq_decode_attn_cert(ctypes.byref(c), _ptr(q), Hq, sm_scale, tau_k, tau_v, tau_out,
+                                    1 if append else 0, _ptr(out), _ptr(cert), _ptr(recomputed),
+                                    _ptr(mask_out), _ptr(workspace), workspace.numel(), _stream(stream))
+    _check("kvq_decode_attn_cert", st)
+    cache.length = int(c.length)
+    return out, cert, recomputed

@@ -59,16 +59,25 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Workspace layout: [part_ml float2 x B*Hkv*S*G, padded to 256 B]
 //                   [part_acc float x B*Hkv*S*G*128]
+//                   certificate: [part_e float x B*Hkv*S*G] [part_sa float2 x
+//                   B*Hkv*S] [part_kv float2 x B*Hkv] [flags uint8 x B*Hq]
+//                   [gate uint8 x B*Hkv], each padded to 256 B
 struct WsLayout {
-    size_t ml, acc, total;
+    size_t ml, acc, e, sa, kv, flags, gate, total;
 };
 
 WsLayout ws_layout(const kvq_cache *c, int32_t g, int64_t splits) {
     const size_t bh = (size_t)c->batch * (size_t)c->kv_heads;
+    const size_t parts = bh * (size_t)splits * (size_t)g;
     WsLayout w;
     w.ml = 0;
-    w.acc = round_up(bh * (size_t)splits * (size_t)g * sizeof(float2), 256);
-    w.total = w.acc + bh * (size_t)splits * (size_t)g * kvq::D * sizeof(float);
+    w.acc = round_up(parts * sizeof(float2), 256);
+    w.e = round_up(w.acc + parts * kvq::D * sizeof(float), 256);
+    w.sa = round_up(w.e + parts * sizeof(float), 256);
+    w.kv = round_up(w.sa + bh * (size_t)splits * sizeof(float2), 256);
+    w.flags = round_up(w.kv + bh * sizeof(float2), 256);
+    w.gate = round_up(w.flags + bh * (size_t)g, 256);
+    w.total = w.gate + bh;
     return w;
 }
 
@@ -218,7 +227,8 @@ namespace {
 // On success with append, c->length grows by one.
 kvq_status decode_impl(kvq_cache *c, const uint16_t *q, int32_t q_heads, float sm_scale, float tau_k,
                        float tau_v, uint16_t *out, uint8_t *mask_out, void *workspace, size_t ws_bytes,
-                       void *stream, int32_t kernel, int32_t splits, void *split_done, bool append) {
+                       void *stream, int32_t kernel, int32_t splits, void *split_done, bool append,
+                       float *cert = nullptr, float tau_out = 0.0f, uint8_t *recomputed = nullptr) {
     kvq_status st = check_shape(c);
     if (st != KVQ_OK) return st;
     if ((st = check_query(c, q, q_heads, sm_scale, tau_k, tau_v)) != KVQ_OK) return st;
@@ -226,6 +236,8 @@ kvq_status decode_impl(kvq_cache *c, const uint16_t *q, int32_t q_heads, float s
     if (!out) return KVQ_ERR_INVALID_ARG;
     if (!aligned(out, 16)) return KVQ_ERR_ALIGNMENT;
     if (kernel < KVQ_KERNEL_AUTO || kernel > KVQ_KERNEL_MFMA || splits < 0) return KVQ_ERR_INVALID_ARG;
+    const bool certify = cert != nullptr;
+    if (certify && (tau_out != tau_out || !aligned(cert, 4))) return tau_out != tau_out ? KVQ_ERR_INVALID_ARG : KVQ_ERR_ALIGNMENT;
     if (append && c->length >= c->capacity) return KVQ_ERR_CAPACITY;
     const int32_t g = q_heads / c->kv_heads;
     if (!workspace || ws_bytes < kvq_decode_workspace_bytes(c, q_heads)) return KVQ_ERR_WORKSPACE;
@@ -239,6 +251,7 @@ kvq_status decode_impl(kvq_cache *c, const uint16_t *q, int32_t q_heads, float s
     const bool mfma_fits = kvq::mfma_supports(g) && nb <= (int64_t)kvq::MFMA_MAX_BPS * max_splits(c);
     int32_t k = kernel;
     if (k == KVQ_KERNEL_AUTO) k = mfma_fits ? KVQ_KERNEL_MFMA : KVQ_KERNEL_VALU;
+    if (certify && k != KVQ_KERNEL_MFMA) return KVQ_ERR_UNSUPPORTED;  // the certificate is a matrix-core path
     if (k == KVQ_KERNEL_MFMA && !mfma_fits) return KVQ_ERR_UNSUPPORTED;
     const bool mf = k == KVQ_KERNEL_MFMA;
     const int64_t s = nb > 0 ? choose_splits(c, nb, splits, mf ? 1 : 4, mf ? kvq::MFMA_MAX_BPS : kvq::MAX_BPS) : 1;
@@ -272,11 +285,36 @@ kvq_status decode_impl(kvq_cache *c, const uint16_t *q, int32_t q_heads, float s
     a.tau_k = tau_k;
     a.tau_v = tau_v;
     a.t_new = append ? c->length : -1;
+    a.cert_mode = certify ? 1 : 0;
+    a.part_e = reinterpret_cast<float *>((char *)workspace + w.e);
+    a.part_sa = reinterpret_cast<float2 *>((char *)workspace + w.sa);
+    a.part_kv = reinterpret_cast<float2 *>((char *)workspace + w.kv);
+    a.tau_out = tau_out;
+    a.cert = cert;
+    a.flags = recomputed ? recomputed : reinterpret_cast<uint8_t *>((char *)workspace + w.flags);
+    a.gate_out = reinterpret_cast<uint8_t *>((char *)workspace + w.gate);
+    a.gate = nullptr;
+    a.head_gate = nullptr;
 
     hipError_t e = mf ? kvq::launch_decode_mfma(a, c->batch, (hipStream_t)stream)
                       : kvq::launch_decode_valu(a, c->batch, (hipStream_t)stream);
     if (e == hipSuccess && split_done) e = hipEventRecord((hipEvent_t)split_done, (hipStream_t)stream);
-    if (e == hipSuccess) e = kvq::launch_merge(a, c->batch, (hipStream_t)stream);
+    if (e == hipSuccess) e = certify ? kvq::launch_merge_cert(a, c->batch, (hipStream_t)stream)
+                                     : kvq::launch_merge(a, c->batch, (hipStream_t)stream);
+    if (e == hipSuccess && certify && tau_out != __builtin_huge_valf()) {
+        // rung 3: the groups holding a flagged head run again with every
+        // block on FP16 (tolerances 0), and the flagged heads take the result
+        kvq::DecodeArgs r = a;
+        r.tau_k = 0.0f;
+        r.tau_v = 0.0f;
+        r.t_new = -1;
+        r.mask_out = nullptr;
+        r.cert_mode = 0;
+        r.gate = a.gate_out;
+        r.head_gate = a.flags;
+        e = kvq::launch_decode_mfma(r, c->batch, (hipStream_t)stream);
+        if (e == hipSuccess) e = kvq::launch_merge(r, c->batch, (hipStream_t)stream);
+    }
     if (e != hipSuccess) return hip_fail(e);
     if (append) c->length = length;
     return KVQ_OK;
@@ -307,6 +345,15 @@ kvq_status kvq_append_decode_ex(kvq_cache *c, const uint16_t *q, int32_t q_heads
                                 int32_t splits, void *split_done) {
     return decode_impl(c, q, q_heads, sm_scale, tau_k, tau_v, out, mask_out, workspace, ws_bytes, stream,
                        kernel, splits, split_done, true);
+}
+
+kvq_status kvq_decode_attn_cert(kvq_cache *c, const uint16_t *q, int32_t q_heads, float sm_scale, float tau_k,
+                                float tau_v, float tau_out, int32_t append, uint16_t *out, float *cert,
+                                uint8_t *recomputed, uint8_t *mask_out, void *workspace, size_t ws_bytes,
+                                void *stream) {
+    if (!cert) return KVQ_ERR_INVALID_ARG;
+    return decode_impl(c, q, q_heads, sm_scale, tau_k, tau_v, out, mask_out, workspace, ws_bytes, stream,
+                       KVQ_KERNEL_AUTO, 0, nullptr, append != 0, cert, tau_out, recomputed);
 }
 
 kvq_status kvq_append_decode(kvq_cache *c, const uint16_t *q, int32_t q_heads, float sm_scale,

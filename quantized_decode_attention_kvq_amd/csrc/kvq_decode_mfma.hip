@@ -269,12 +269,17 @@ __device__ __forceinline__ void issue_fb(const DecodeArgs &a, int64_t bh, int64_
 struct WaveState {
     float m_run, l_run;
     float4_t acc[8];
+    // certificate only: the attention mass times the block's value error
+    // (online, like l_run), the largest value scale of a value-certified
+    // token and the largest |v| of a value-fallback token (fp16 bits)
+    float e_run;
+    uint32_t smax, amax;
 };
 
-template <typename Mid>
+template <bool CERT, typename Mid>
 __device__ __forceinline__ void process_step(const uint8_t *stage, uint32_t mk, int p_lo, int p_hi,
                                              const uint4 (&qb)[4], float sml2, WaveState &w, int lane,
-                                             Mid &&mid) {
+                                             float eta, Mid &&mid) {
     const int m = lane & 15, g4 = lane >> 4;
     const bool partial = p_lo > 0 || p_hi < 32;  // wave-uniform
 
@@ -347,6 +352,7 @@ __device__ __forceinline__ void process_step(const uint8_t *stage, uint32_t mk, 
         }
     w.m_run = m_new;
     w.l_run = w.l_run * alpha + psum;
+    if (CERT) w.e_run = w.e_run * alpha + psum * eta;  // eta: the block's value error, 0 on value fallback
     if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) w.acc[mt] *= alpha;
@@ -381,6 +387,13 @@ __device__ __forceinline__ void process_step(const uint8_t *stage, uint32_t mk, 
             for (int q = 0; q < 4; ++q)
                 r[q] = ((keep >> q) & 1u ? v[mt][q] : 0u) | (((keep >> (q + 4)) & 1u ? v[mt][q + 4] : 0u) << 16);
             w.acc[mt] = mfma(make_uint4(r[0], r[1], r[2], r[3]), bop, w.acc[mt]);
+            if (CERT) {
+                // |v| of the step's valid values (fp16 bits without the sign
+                // order like the magnitudes; NaN above +Inf)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    w.amax = umax(w.amax, umax(r[q] & 0x7FFFu, (r[q] >> 16) & 0x7FFFu));
+            }
         }
     } else {
         // value codes of channel 16mt + m, positions 8kg .. 8kg+7
@@ -404,6 +417,15 @@ __device__ __forceinline__ void process_step(const uint8_t *stage, uint32_t mk, 
             for (int q = 0; q < 4; ++q) {
                 if (tk0 + q < p_lo || tk0 + q >= p_hi) lo_a[q] = hi_a[q] = 0u;
                 if (tk0 + 4 + q < p_lo || tk0 + 4 + q >= p_hi) lo_b[q] = hi_b[q] = 0u;
+            }
+        }
+        if (CERT) {
+            // largest value scale of the step's valid tokens (non-negative
+            // fp16: bit patterns order like the values)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                w.smax = umax(w.smax, umax(umax(lo_a[q] & 0xFFFFu, lo_a[q] >> 16), umax(hi_a[q] & 0xFFFFu, hi_a[q] >> 16)));
+                w.smax = umax(w.smax, umax(umax(lo_b[q] & 0xFFFFu, lo_b[q] >> 16), umax(hi_b[q] & 0xFFFFu, hi_b[q] >> 16)));
             }
         }
 #pragma unroll
@@ -465,6 +487,17 @@ __device__ __forceinline__ void patch_new_token(uint8_t *stage, uint32_t mk, int
 // cut by its range ends.
 constexpr int TBL = 4 * MFMA_MAX_BPS + 8;
 
+// Round a non-negative float up to an fp16 value (a bound stays a bound).
+__device__ __forceinline__ uint16_t f16_up(float x) {
+    uint32_t h = f2h_rn(x);
+    if (h2f(h) < x) h += 1;
+    return (uint16_t)h;
+}
+
+// CERT: also the per-head output certificate's per-split parts (the
+// mass-weighted value error, the largest certified value scale and
+// fallback |v|, and the largest certified block errors).
+template <bool CERT>
 __global__ __launch_bounds__(NW * 64, NW / 4) void decode_mfma_kernel(DecodeArgs a) {
     // NW waves x NSTAGE stages x 6656 B of ring.  Before the stream starts, the
     // ring from wave 1 on holds the masks of every block of (b, kvh); after it
@@ -476,6 +509,7 @@ __global__ __launch_bounds__(NW * 64, NW / 4) void decode_mfma_kernel(DecodeArgs
     __shared__ int wsum_lds[NW];
     __shared__ int blo_lds, ntbl_lds;
     __shared__ int next_lds;  // next unclaimed step of the share
+    __shared__ uint16_t teta_lds[CERT ? TBL : 1];  // certificate: value error of each listed block (fp16, rounded up; 0 on value fallback)
     uint8_t *maskb = &ring[1][0][0];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -484,6 +518,7 @@ __global__ __launch_bounds__(NW * 64, NW / 4) void decode_mfma_kernel(DecodeArgs
     const int split = blockIdx.x;
     const int64_t kvh = blockIdx.y, b = blockIdx.z;
     const int64_t bh = b * a.hkv + kvh;
+    if (a.gate && !a.gate[bh]) return;  // recompute pass: a group none of whose heads is recomputed
     const int g = a.g;
     const int nb = (int)a.nb;
     constexpr int NT = NW * 64;
@@ -569,7 +604,13 @@ __global__ __launch_bounds__(NW * 64, NW / 4) void decode_mfma_kernel(DecodeArgs
     }
 
     // masks of every block of (b, kvh); mask_out receives this workgroup's
-    // home range of bps blocks
+    // home range of bps blocks.  Certificate: each block's value error
+    // (etab, 0 on value fallback) and, per wave, the largest key and value
+    // errors of the certified blocks (kvw), both in the ring until the
+    // stream starts.
+    float *etab = reinterpret_cast<float *>(&ring[0][0][0] + 40960);  // past maskb's 16 KB
+    float *kvw = etab + MFMA_MAX_BPS * MAX_SPLITS;
+    float kmx = 0.0f, vmx = 0.0f;
     {
         const int64_t h0 = (int64_t)split * a.bps, h1 = h0 + a.bps;
         auto put = [&](int i, float kerr, float verr) {
@@ -583,13 +624,37 @@ __global__ __launch_bounds__(NW * 64, NW / 4) void decode_mfma_kernel(DecodeArgs
             const uint32_t mk = block_mask(a.sm, qn, kerr, verr, a.tau_k, a.tau_v);
             maskb[i] = (uint8_t)mk;
             if (a.mask_out && i >= h0 && i < h1) a.mask_out[bh * a.nb + i] = (uint8_t)mk;
+            if (CERT) {
+                if (!(mk & 1u)) kmx = fmaxf(kmx, kerr);
+                if (!(mk & 2u)) vmx = fmaxf(vmx, verr);
+                etab[i] = (mk & 2u) ? 0.0f : verr;
+            }
         };
 #pragma unroll
         for (int r = 0; r < PF; ++r)
             if (tid + r * NT < nb) put(tid + r * NT, ke[r], ve[r]);
         for (int i = tid + PF * NT; i < nb; i += NT) put(i, a.c.k_err[bh * a.nbc + i], a.c.v_err[bh * a.nbc + i]);
+        if (CERT) {
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                kmx = fmaxf(kmx, __shfl_xor(kmx, o));
+                vmx = fmaxf(vmx, __shfl_xor(vmx, o));
+            }
+            if (lane == 0) {
+                kvw[wave] = kmx;
+                kvw[NW + wave] = vmx;
+            }
+        }
     }
     __syncthreads();
+    if (CERT) {
+        // the largest key and value errors of the certified blocks of (b, kvh)
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            kmx = fmaxf(kmx, kvw[w]);
+            vmx = fmaxf(vmx, kvw[NW + w]);
+        }
+    }
 
     // workgroup 0 of (b, kvh) writes the appended token's tier-1 bytes and
     // its block's statistics (as the append kernel would); no other
@@ -680,6 +745,7 @@ __global__ __launch_bounds__(NW * 64, NW / 4) void decode_mfma_kernel(DecodeArgs
             if (p < r1 && p + w > r0) {
                 toff_lds[i - blo] = (int16_t)(p - r0);
                 tmk_lds[i - blo] = (uint8_t)mk;
+                if (CERT) teta_lds[i - blo] = (mk & 2u) ? (uint16_t)0 : f16_up(etab[i]);
             }
             p += w;
         }
@@ -752,6 +818,9 @@ __global__ __launch_bounds__(NW * 64, NW / 4) void decode_mfma_kernel(DecodeArgs
     WaveState ws;
     ws.m_run = NEG_INF;
     ws.l_run = 0.0f;
+    ws.e_run = 0.0f;
+    ws.smax = 0u;
+    ws.amax = 0u;
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) ws.acc[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
 
@@ -788,7 +857,8 @@ __global__ __launch_bounds__(NW * 64, NW / 4) void decode_mfma_kernel(DecodeArgs
         const int64_t left = a.length - (blk * BLK + (mk ? 8 * sub : 32 * sub));
         const int nvalid = (int)(left < step_len ? (left > 0 ? left : 0) : step_len);
         if (nvalid > 0)
-            process_step(stage, mk, p_lo, p_lo + nvalid, qb, sml2, ws, lane, mid);
+            process_step<CERT>(stage, mk, p_lo, p_lo + nvalid, qb, sml2, ws, lane,
+                               CERT ? h2f(teta_lds[blk - blo]) : 0.0f, mid);
         else
             mid();
         return true;
@@ -816,15 +886,58 @@ __global__ __launch_bounds__(NW * 64, NW / 4) void decode_mfma_kernel(DecodeArgs
             wl[wave][m] = l_run;
         }
     }
+    float *we = reinterpret_cast<float *>(&ring[0][0][0] + NW * 16 * D * 4);  // [NW][16]
+    uint32_t *wsa = reinterpret_cast<uint32_t *>(we + NW * 16);                // [NW][2]
+    if (CERT) {
+        float e_run = ws.e_run;
+        e_run += __shfl_xor(e_run, 16);
+        e_run += __shfl_xor(e_run, 32);
+        uint32_t sm_ = ws.smax, am_ = ws.amax;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            sm_ = umax(sm_, (uint32_t)__shfl_xor((int)sm_, o));
+            am_ = umax(am_, (uint32_t)__shfl_xor((int)am_, o));
+        }
+        if (m < g && g4 == 0) we[wave * 16 + m] = e_run;
+        if (lane == 0) {
+            wsa[2 * wave] = sm_;
+            wsa[2 * wave + 1] = am_;
+        }
+    }
     __syncthreads();
     write_partial(a, bh, split, NW, 16, wm, wl, wacc);
+    if (CERT) {
+        // per head: the split's mass-weighted value error on the scale of its
+        // running maximum (as write_partial scales the running sum)
+        for (int h = tid; h < g; h += NT) {
+            float M = -__builtin_huge_valf();
+            for (int w = 0; w < NW; ++w) M = fmaxf(M, wm[w][h]);
+            float E = 0.0f;
+            if (M != -__builtin_huge_valf())
+                for (int w = 0; w < NW; ++w)
+                    if (wm[w][h] != -__builtin_huge_valf()) E += we[w * 16 + h] * __builtin_amdgcn_exp2f(wm[w][h] - M);
+            a.part_e[(bh * a.splits + split) * g + h] = E;
+        }
+        if (tid == 0) {
+            uint32_t sm_ = 0u, am_ = 0u;
+            for (int w = 0; w < NW; ++w) {
+                sm_ = umax(sm_, wsa[2 * w]);
+                am_ = umax(am_, wsa[2 * w + 1]);
+            }
+            a.part_sa[bh * a.splits + split] = make_float2(h2f(sm_), h2f(am_));
+            if (split == 0) a.part_kv[bh] = make_float2(kmx, vmx);
+        }
+    }
 }
 
 bool mfma_supports(int g) { return g >= 1 && g <= 16; }
 
 hipError_t launch_decode_mfma(const DecodeArgs &a, int batch, hipStream_t s) {
     dim3 grid((unsigned)a.splits, (unsigned)a.hkv, (unsigned)batch);
-    hipLaunchKernelGGL(decode_mfma_kernel, grid, dim3(NW * 64), 0, s, a);
+    if (a.cert_mode)
+        hipLaunchKernelGGL(decode_mfma_kernel<true>, grid, dim3(NW * 64), 0, s, a);
+    else
+        hipLaunchKernelGGL(decode_mfma_kernel<false>, grid, dim3(NW * 64), 0, s, a);
     return hipGetLastError();
 }
 

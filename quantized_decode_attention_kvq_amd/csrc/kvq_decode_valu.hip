@@ -269,6 +269,7 @@ __global__ __launch_bounds__(256) void merge_splits_kernel(DecodeArgs a) {
     __shared__ float2 ml[MAX_SPLITS][16];
     const int64_t kvh = blockIdx.x, b = blockIdx.y;
     const int64_t bh = b * a.hkv + kvh;
+    if (a.gate && !a.gate[bh]) return;  // recompute pass: nothing of this group is recomputed
     const int g = a.g, S = a.splits;
     const float2 *pml = a.part_ml + bh * S * g;
     for (int i = threadIdx.x; i < S * g; i += blockDim.x) ml[i / g][i % g] = pml[i];
@@ -297,7 +298,7 @@ __global__ __launch_bounds__(256) void merge_splits_kernel(DecodeArgs a) {
             for (int k = 0; k < 8; ++k) o += wgt[s + k][h] * v[k];
         }
         for (; s < S; ++s) o += wgt[s][h] * pacc[(int64_t)s * g * D + idx];
-        a.out[((b * a.hq) + kvh * g) * D + idx] = (uint16_t)f2h_rn(o);
+        if (!a.head_gate || a.head_gate[b * a.hq + kvh * g + h]) a.out[((b * a.hq) + kvh * g) * D + idx] = (uint16_t)f2h_rn(o);
     }
 }
 

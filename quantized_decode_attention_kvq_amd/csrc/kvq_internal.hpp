@@ -52,6 +52,19 @@ struct DecodeArgs {
     int32_t splits, bps;  // number of splits and blocks per split
     float sm, tau_k, tau_v;
     int64_t t_new;  // token appended by this launch (fused append), or -1
+    // per-head output certificate (matrix-core kernel with cert_mode set)
+    int32_t cert_mode;
+    float *part_e;          // [B*Hkv][S][G] mass-weighted value error, on the split's running-max scale
+    float2 *part_sa;        // [B*Hkv][S] largest certified value scale, largest fallback |v|
+    float2 *part_kv;        // [B*Hkv] largest certified key error, value error
+    float tau_out;          // heads whose certificate exceeds it are recomputed on FP16
+    float *cert;            // [B][Hq] certificate (written by the certificate merge)
+    uint8_t *flags;         // [B][Hq] 1: the head is recomputed
+    uint8_t *gate_out;      // [B*Hkv] 1: some head of the group is recomputed
+    // recompute pass: only groups with gate[bh] run, only heads with
+    // head_gate[b][h] are written (both null otherwise)
+    const uint8_t *gate;
+    const uint8_t *head_gate;
 };
 
 // Upper limits that size the workspace and LDS tables.
@@ -65,6 +78,8 @@ hipError_t launch_bounds(const BoundsArgs &a, int batch, hipStream_t s);
 hipError_t launch_decode_valu(const DecodeArgs &a, int batch, hipStream_t s);
 hipError_t launch_decode_mfma(const DecodeArgs &a, int batch, hipStream_t s);
 hipError_t launch_merge(const DecodeArgs &a, int batch, hipStream_t s);
+// The merge of a certified decode: outputs, per-head certificates, recompute flags.
+hipError_t launch_merge_cert(const DecodeArgs &a, int batch, hipStream_t s);
 bool mfma_supports(int g);
 
 }  // namespace kvq
