@@ -7,7 +7,8 @@ and the online softmax), then a kernel merging the splits (--unfused: the
 append as its own kernel first).  Inputs are resident in HBM when
 the timed region starts.  Several layers' caches ("replicas") are cycled so
 that consecutive steps never find their KV stream in the 256 MB Infinity
-Cache, as in a real multi-layer decode.
+Cache, as in a real multi-layer decode; by default the steps of those
+layers are captured in one HIP graph, replayed steps / layers times.
 
 Prints one JSON line:
   value      effective KV bandwidth of the step: algorithmic bytes / step time
@@ -18,6 +19,9 @@ Prints one JSON line:
              library records one between the split-K and merge kernels),
              against the 8 TB/s HBM3E peak; traffic from committed rocprofv3
              FETCH_SIZE / WRITE_SIZE runs when they match the sources.
+  certified_step  the same step through kvq_decode_attn_cert: per-head
+             output certificate only, and with the FP16 recompute of the heads
+             above a tau_out that flags about 1% of them (ms per step each).
   cpu_baseline  the CPU oracle (fp64, OpenMP) timed on a bounded sample of
              the same workload, same byte accounting.
 
@@ -62,7 +66,12 @@ def parse():
     p.add_argument("--unfused", action="store_true",
                    help="step as two calls (kvq_quantize_append, kvq_decode_attn) instead of kvq_append_decode")
     p.add_argument("--graph", type=int, default=1,
-                   help="1: replay each layer's step (append + decode) from a captured HIP graph; 0: eager launches")
+                   help="1: replay the steps from captured HIP graphs (the cycled layers' steps in one graph); "
+                        "0: eager launches")
+    p.add_argument("--no-certify", action="store_true",
+                   help="skip timing the step with the per-head output certificate (kvq_decode_attn_cert)")
+    p.add_argument("--recompute-frac", type=float, default=0.01,
+                   help="certified step with recompute: tau_out set so that about this fraction of heads is flagged")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run one 1 GiB device copy (reference kernel for HBM counters)")
     return p.parse_args()
@@ -194,6 +203,98 @@ def bench_quantize(args, w):
     }), flush=True)
 
 
+def timed_steps(args, R, step, stream):
+    """Milliseconds per step over exactly args.steps steps (step(i, stream)
+    launches step i on layer cache i % R), after args.warmup untimed ones.
+    With args.graph, the R layers' steps are captured in one HIP graph
+    (plus one of the first steps % R layers) and replayed; otherwise every
+    step is launched eagerly."""
+    import torch
+
+    for i in range(args.warmup):
+        step(i, stream)
+    torch.cuda.synchronize()
+    if args.graph:
+        side = torch.cuda.Stream()
+
+        def capture(n):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=side):
+                for r in range(n):
+                    step(r, torch.cuda.current_stream())
+            return g
+        full = capture(R)
+        rem = args.steps % R
+        part = capture(rem) if rem else None
+        torch.cuda.synchronize()
+
+        def run_all():
+            for _ in range(args.steps // R):
+                full.replay()
+            if part is not None:
+                part.replay()
+        for _ in range(max(1, args.warmup // R)):
+            full.replay()
+        torch.cuda.synchronize()
+    else:
+        def run_all():
+            for i in range(args.steps):
+                step(i, stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run_all()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / args.steps * 1e3
+
+
+def bench_certified(args, w, caches, ws, q, sm, tau_k, tau_v, ms_plain):
+    """The same step with the per-head output certificate: the certifying
+    decode kernel, the certificate merge and, for heads above tau_out, the
+    gated FP16 recompute.  Timed from captured graphs like the plain step,
+    once with tau_out = inf (certificate only) and once with tau_out set so
+    that about --recompute-frac of the heads are recomputed."""
+    import numpy as np
+    import torch
+
+    import quantized_decode_attention_kvq_amd as kvq
+
+    R = len(caches)
+    out = torch.empty_like(q)
+    cert = torch.empty((w.B, w.Hq), dtype=torch.float32, device=q.device)
+    rec = torch.empty((w.B, w.Hq), dtype=torch.uint8, device=q.device)
+
+    def cstep(i, tau_out, strm):
+        c = caches[i % R]
+        c.length = w.T - 1
+        kvq.kvq_decode_attn_cert(c, q, sm, tau_k, tau_v, tau_out, append=True, out=out, cert=cert,
+                                 recomputed=rec, workspace=ws[i % R], stream=strm)
+
+    stream = torch.cuda.current_stream()
+    cstep(0, float("inf"), stream)
+    torch.cuda.synchronize()
+    cv = np.sort(cert.flatten().cpu().numpy())
+    k = max(1, int(round(args.recompute_frac * cv.size)))
+    tau_out = float(np.float32((cv[cv.size - k - 1] + cv[cv.size - k]) / 2)) if cv.size > k else -1.0
+
+    ms_cert = timed_steps(args, R, lambda i, strm: cstep(i, float("inf"), strm), stream)
+    ms_rec = timed_steps(args, R, lambda i, strm: cstep(i, tau_out, strm), stream)
+    cstep(0, tau_out, stream)
+    torch.cuda.synchronize()
+    r = rec.cpu().numpy()
+    groups = r.reshape(w.B, w.Hkv, w.G).any(axis=2)
+    return {
+        "api": "kvq_decode_attn_cert (append=True)",
+        "ms_per_step_certificate_only": round(ms_cert, 5),
+        "overhead_vs_plain_step": round(ms_cert / ms_plain - 1.0, 4),
+        "tau_out": tau_out,
+        "heads_recomputed_frac": round(float(r.mean()), 5),
+        "kv_groups_recomputed_frac": round(float(groups.mean()), 5),
+        "ms_per_step_with_recompute": round(ms_rec, 5),
+        "certificate_median": float(np.median(cv)),
+        "certificate_max": float(cv[-1]),
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -280,34 +381,11 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # Step launcher of the timed loop: the eager step, or one captured HIP
-    # graph per layer cache holding the same launches (append + decode +
-    # merge), as a serving loop would replay them.
-    run = step
-    if args.graph:
-        graphs = []
-        side = torch.cuda.Stream()
-        for r in range(R):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=side):
-                step(r, strm=torch.cuda.current_stream())
-            graphs.append(g)
-        torch.cuda.synchronize()
-
-        def run(i):
-            graphs[i % R].replay()
-        for i in range(args.warmup):
-            run(i)
-        torch.cuda.synchronize()
-
-    # timed loop: exactly `steps` steps between synchronisations
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        run(i)
-    torch.cuda.synchronize()
-    dt = time.perf_counter() - t0
-    ms_step = dt / args.steps * 1e3
+    # timed loop: exactly `steps` steps between synchronisations, launched
+    # eagerly or replayed from captured HIP graphs (append + decode + merge of
+    # each of the R layers in one graph, as a decoder's per-token graph holds
+    # every layer)
+    ms_step = timed_steps(args, R, lambda i, strm: step(i, strm=strm), stream)
 
     # kernel timing, right after: the same steps launched eagerly with HIP
     # events on the stream before the decode call, between its split-K and
@@ -326,6 +404,10 @@ def main():
     split_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     merge_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
     call_ms = float(np.mean([e[0].elapsed_time(e[2]) for e in evs]))
+
+    # the certificate needs the matrix-core kernel (group sizes up to 16)
+    no_cert = args.no_certify or args.kernel == "valu" or w.G > 16
+    certified = None if no_cert else bench_certified(args, w, caches, ws, q, sm, tau_k, tau_v, ms_step)
 
     if args.calibrate_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -364,7 +446,7 @@ def main():
             "fallback_blocks_value": round(float(((m >> 1) & 1).mean()), 5),
             "tau_k": tau_k if np.isfinite(tau_k) else "inf", "tau_v": tau_v if np.isfinite(tau_v) else "inf",
             "layers_cycled": R,
-            "kernel": args.kernel, "splits": args.splits, "hip_graph": bool(args.graph),
+            "kernel": args.kernel, "splits": args.splits, "hip_graph": bool(args.graph), "steps_per_graph": R if args.graph else None,
             "fused_append": not args.unfused,
             "bytes_per_step": step_bytes,
         },
@@ -384,6 +466,8 @@ def main():
             "eager_ms_per_step_with_events": round(ms_step_events, 5),
         },
     }
+    if certified is not None:
+        line["certified_step"] = certified
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, d, tau_k, tau_v, sm, args.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -60,10 +60,10 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // Workspace layout: [part_ml float2 x B*Hkv*S*G, padded to 256 B]
 //                   [part_acc float x B*Hkv*S*G*128]
 //                   certificate: [part_e float x B*Hkv*S*G] [part_sa float2 x
-//                   B*Hkv*S] [part_kv float2 x B*Hkv] [flags uint8 x B*Hq]
-//                   [gate uint8 x B*Hkv], each padded to 256 B
+//                   B*Hkv*S] [part_kv float2 x B*Hkv] [flags uint8 x B*Hq],
+//                   each padded to 256 B
 struct WsLayout {
-    size_t ml, acc, e, sa, kv, flags, gate, total;
+    size_t ml, acc, e, sa, kv, flags, total;
 };
 
 WsLayout ws_layout(const kvq_cache *c, int32_t g, int64_t splits) {
@@ -76,8 +76,7 @@ WsLayout ws_layout(const kvq_cache *c, int32_t g, int64_t splits) {
     w.sa = round_up(w.e + parts * sizeof(float), 256);
     w.kv = round_up(w.sa + bh * (size_t)splits * sizeof(float2), 256);
     w.flags = round_up(w.kv + bh * sizeof(float2), 256);
-    w.gate = round_up(w.flags + bh * (size_t)g, 256);
-    w.total = w.gate + bh;
+    w.total = w.flags + bh * (size_t)g;
     return w;
 }
 
@@ -264,7 +263,9 @@ kvq_status decode_impl(kvq_cache *c, const uint16_t *q, int32_t q_heads, float s
         append = false;
     }
 
-    const WsLayout w = ws_layout(c, g, s_eff);
+    // offsets for the largest split count, so that passes with different
+    // split counts share the certificate regions
+    const WsLayout w = ws_layout(c, g, max_splits(c));
     kvq::DecodeArgs a;
     a.c = ptrs(c);
     a.q = q;
@@ -292,9 +293,7 @@ kvq_status decode_impl(kvq_cache *c, const uint16_t *q, int32_t q_heads, float s
     a.tau_out = tau_out;
     a.cert = cert;
     a.flags = recomputed ? recomputed : reinterpret_cast<uint8_t *>((char *)workspace + w.flags);
-    a.gate_out = reinterpret_cast<uint8_t *>((char *)workspace + w.gate);
     a.gate = nullptr;
-    a.head_gate = nullptr;
 
     hipError_t e = mf ? kvq::launch_decode_mfma(a, c->batch, (hipStream_t)stream)
                       : kvq::launch_decode_valu(a, c->batch, (hipStream_t)stream);
@@ -304,15 +303,24 @@ kvq_status decode_impl(kvq_cache *c, const uint16_t *q, int32_t q_heads, float s
     if (e == hipSuccess && certify && tau_out != __builtin_huge_valf()) {
         // rung 3: the groups holding a flagged head run again with every
         // block on FP16 (tolerances 0), and the flagged heads take the result
+        // (few groups are expected to hold one: every split count the cache
+        // allows, so that each spreads over many workgroups)
+        const int64_t s_r = nb > 0 ? (nb < max_splits(c) ? nb : max_splits(c)) : 1;
+        const int64_t bps_r = nb > 0 ? (nb + s_r - 1) / s_r : 1;
         kvq::DecodeArgs r = a;
+        r.splits = (int32_t)(nb > 0 ? (nb + bps_r - 1) / bps_r : 1);
+        r.bps = (int32_t)bps_r;
         r.tau_k = 0.0f;
         r.tau_v = 0.0f;
         r.t_new = -1;
         r.mask_out = nullptr;
         r.cert_mode = 0;
-        r.gate = a.gate_out;
-        r.head_gate = a.flags;
-        e = kvq::launch_decode_mfma(r, c->batch, (hipStream_t)stream);
+        r.gate = a.flags;
+        const int64_t nbh = (int64_t)c->batch * c->kv_heads;
+        int64_t slots = (device_cus() + r.splits - 1) / r.splits;  // about one workgroup per CU
+        if (slots > nbh) slots = nbh;
+        if (slots < 1) slots = 1;
+        e = kvq::launch_decode_mfma_gated(r, c->batch, (int)slots, (hipStream_t)stream);
         if (e == hipSuccess) e = kvq::launch_merge(r, c->batch, (hipStream_t)stream);
     }
     if (e != hipSuccess) return hip_fail(e);

@@ -26,85 +26,106 @@ namespace kvq {
 
 namespace {
 
+// One workgroup per query head h of (b, kvh).  The output merge is the
+// split merge's (every wave forms M and L; wave w sums the splits w, w + 4,
+// ..., lane l holds channels 2l and 2l + 1); wave 1 then gathers the
+// certificate's parts of the splits (two per lane, summed in double).
 __global__ __launch_bounds__(256) void merge_cert_kernel(DecodeArgs a) {
-    __shared__ float wgt[MAX_SPLITS][16];
-    __shared__ float2 ml[MAX_SPLITS][16];
-    __shared__ float qn_lds[16];
-    __shared__ uint8_t flag_lds[16];
-    const int64_t kvh = blockIdx.x, b = blockIdx.y;
+    __shared__ float2 red[4][64];
+    __shared__ float qn_lds;
+    const int h = blockIdx.x;
+    const int64_t kvh = blockIdx.y, b = blockIdx.z;
     const int64_t bh = b * a.hkv + kvh;
     const int g = a.g, S = a.splits;
-    const int tid = threadIdx.x;
-    const float2 *pml = a.part_ml + bh * S * g;
-    for (int i = tid; i < S * g; i += blockDim.x) ml[i / g][i % g] = pml[i];
-    {
-        // per-head query norm: 16-lane group h holds head h's 128 channels
-        const int h = tid >> 4, l16 = tid & 15;
+    const int64_t head = b * a.hq + kvh * g + h;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    constexpr float NEG_INF = -__builtin_huge_valf();
+    if (wave == 0) {
+        // query norm of head h: lanes 0-15 hold its 128 channels (the other
+        // lane groups take part with zeros)
         uint4 raw = make_uint4(0u, 0u, 0u, 0u);
-        if (h < g) raw = *reinterpret_cast<const uint4 *>(a.q + ((b * a.hq) + kvh * g + h) * D + 8 * l16);
-        const float n = qnorm16(raw);  // all 16 lanes of the group take part
-        if (l16 == 0 && h < g) qn_lds[h] = n;
+        if (lane < 16) raw = *reinterpret_cast<const uint4 *>(a.q + head * D + 8 * lane);
+        const float n = qnorm16(raw);
+        if (lane == 0) qn_lds = n;
     }
+    const float2 *pml = a.part_ml + bh * S * g + h;  // split s at pml[s * g]
+    const float2 e0 = lane < S ? pml[lane * g] : make_float2(NEG_INF, 0.0f);
+    const float2 e1 = lane + 64 < S ? pml[(lane + 64) * g] : make_float2(NEG_INF, 0.0f);
+    float M = fmaxf(e0.x, e1.x);
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
+    float L = 0.0f;
+    if (e0.x != NEG_INF) L += e0.y * __builtin_amdgcn_exp2f(e0.x - M);
+    if (e1.x != NEG_INF) L += e1.y * __builtin_amdgcn_exp2f(e1.x - M);
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) L += __shfl_xor(L, o);
+    const float *pacc = a.part_acc + (bh * S * g + h) * D + 2 * lane;  // split s at pacc[s * g * D]
+    float2 acc = make_float2(0.0f, 0.0f);
+#pragma unroll 8
+    for (int s = wave; s < S; s += 4) {
+        const float m_s = pml[s * g].x;
+        const float w = (L > 0.0f && m_s != NEG_INF) ? __builtin_amdgcn_exp2f(m_s - M) / L : 0.0f;
+        const float2 v = *reinterpret_cast<const float2 *>(pacc + (int64_t)s * g * D);
+        acc.x += w * v.x;
+        acc.y += w * v.y;
+    }
+    red[wave][lane] = acc;
     __syncthreads();
-    for (int i = tid; i < S * g; i += blockDim.x) {
-        const int s = i / g, h = i % g;
-        float M = -__builtin_huge_valf();
-        for (int r = 0; r < S; ++r) M = fmaxf(M, ml[r][h].x);
-        float L = 0.0f;
-        for (int r = 0; r < S; ++r)
-            if (ml[r][h].x != -__builtin_huge_valf()) L += ml[r][h].y * __builtin_amdgcn_exp2f(ml[r][h].x - M);
-        const float m_s = ml[s][h].x;
-        wgt[s][h] = (L > 0.0f && m_s != -__builtin_huge_valf()) ? __builtin_amdgcn_exp2f(m_s - M) / L : 0.0f;
-    }
-    if (tid < g) {
-        const int h = tid;
-        float M = -__builtin_huge_valf();
-        for (int r = 0; r < S; ++r) M = fmaxf(M, ml[r][h].x);
-        double L = 0.0, E = 0.0;
-        float smax = 0.0f, amax = 0.0f;
-        for (int r = 0; r < S; ++r) {
-            if (ml[r][h].x != -__builtin_huge_valf()) {
-                const double f = (double)__builtin_amdgcn_exp2f(ml[r][h].x - M);
-                L += (double)ml[r][h].y * f;
-                E += (double)a.part_e[(bh * S + r) * g + h] * f;
-            }
-            const float2 sa = a.part_sa[bh * S + r];
-            smax = fmaxf(smax, sa.x);
-            amax = (sa.y != sa.y || sa.y > amax) ? sa.y : amax;  // a NaN value keeps the certificate NaN
+    if (wave == 0) {
+        float2 o = red[0][lane];
+#pragma unroll
+        for (int w = 1; w < 4; ++w) {
+            o.x += red[w][lane].x;
+            o.y += red[w][lane].y;
         }
-        const float2 kv = a.part_kv[bh];
-        const double e_val = L > 0.0 ? E / L : 0.0;
-        const double delta = (double)key_bound(a.sm, qn_lds[h], kv.x);
-        const double r1 = 7.0 * (double)smax + (double)kv.y;
-        const double range = 2.0 * ((double)amax != (double)amax || (double)amax > r1 ? (double)amax : r1);
-        const double c = tanh(0.5 * delta) * range + e_val;
-        float cf = (float)c;
-        if ((double)cf < c) cf = __uint_as_float(__float_as_uint(cf) + 1u);  // c >= 0: the next float up
-        const int64_t oh = b * a.hq + kvh * g + h;
-        a.cert[oh] = cf;
-        const uint8_t fl = cf > a.tau_out ? 1 : 0;
-        a.flags[oh] = fl;
-        flag_lds[h] = fl;
-    }
-    __syncthreads();
-    if (tid == 0) {
-        uint8_t any = 0;
-        for (int h = 0; h < g; ++h) any |= flag_lds[h];
-        a.gate_out[bh] = any;
-    }
-    const float *pacc = a.part_acc + bh * S * g * D;
-    for (int idx = tid; idx < g * D; idx += blockDim.x) {
-        const int h = idx / D;
-        float o = 0.0f;
-        for (int s = 0; s < S; ++s) o += wgt[s][h] * pacc[(int64_t)s * g * D + idx];
-        a.out[((b * a.hq) + kvh * g) * D + idx] = (uint16_t)f2h_rn(o);
+        const uint32_t pair = (uint32_t)f2h_rn(o.x) | ((uint32_t)f2h_rn(o.y) << 16);
+        *reinterpret_cast<uint32_t *>(a.out + head * D + 2 * lane) = pair;
+    } else if (wave == 1) {
+        // L and E in double over the splits with a valid token, the
+        // largest value scale and fallback |v| over all splits
+        double Ld = 0.0, E = 0.0;
+        float smax = 0.0f, amax = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int r = lane + 64 * k;
+            if (r < S) {
+                const float2 e = k ? e1 : e0;
+                if (e.x != NEG_INF) {
+                    const double f = (double)__builtin_amdgcn_exp2f(e.x - M);
+                    Ld += (double)e.y * f;
+                    E += (double)a.part_e[(bh * S + r) * g + h] * f;
+                }
+                const float2 sa = a.part_sa[bh * S + r];
+                smax = fmaxf(smax, sa.x);
+                amax = max_keep_nan(amax, sa.y);  // a NaN value keeps the certificate NaN
+            }
+        }
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            Ld += __shfl_xor(Ld, o);
+            E += __shfl_xor(E, o);
+            smax = fmaxf(smax, __shfl_xor(smax, o));
+            amax = max_keep_nan(amax, __shfl_xor(amax, o));
+        }
+        if (lane == 0) {
+            const float2 kv = a.part_kv[bh];
+            const double e_val = Ld > 0.0 ? E / Ld : 0.0;
+            const double delta = (double)key_bound(a.sm, qn_lds, kv.x);
+            const double r1 = 7.0 * (double)smax + (double)kv.y;
+            const double range = 2.0 * ((double)amax != (double)amax || (double)amax > r1 ? (double)amax : r1);
+            const double c = tanh(0.5 * delta) * range + e_val;
+            float cf = (float)c;
+            if ((double)cf < c) cf = __uint_as_float(__float_as_uint(cf) + 1u);  // c >= 0: the next float up
+            a.cert[head] = cf;
+            a.flags[head] = cf > a.tau_out ? 1 : 0;
+        }
     }
 }
 
 }  // namespace
 
 hipError_t launch_merge_cert(const DecodeArgs &a, int batch, hipStream_t s) {
-    hipLaunchKernelGGL(merge_cert_kernel, dim3((unsigned)a.hkv, (unsigned)batch), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(merge_cert_kernel, dim3((unsigned)a.g, (unsigned)a.hkv, (unsigned)batch), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

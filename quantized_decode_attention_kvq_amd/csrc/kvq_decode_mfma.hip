@@ -498,7 +498,8 @@ __device__ __forceinline__ uint16_t f16_up(float x) {
 // mass-weighted value error, the largest certified value scale and
 // fallback |v|, and the largest certified block errors).
 template <bool CERT>
-__global__ __launch_bounds__(NW * 64, NW / 4) void decode_mfma_kernel(DecodeArgs a) {
+__device__ __forceinline__ void decode_group(const DecodeArgs &a, const int split, const int64_t kvh,
+                                             const int64_t b) {
     // NW waves x NSTAGE stages x 6656 B of ring.  Before the stream starts, the
     // ring from wave 1 on holds the masks of every block of (b, kvh); after it
     // ends, the ring holds the wave merge.
@@ -515,10 +516,7 @@ __global__ __launch_bounds__(NW * 64, NW / 4) void decode_mfma_kernel(DecodeArgs
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept scalar
     const int m = lane & 15, g4 = lane >> 4;                    // MFMA row/column index and k-group
-    const int split = blockIdx.x;
-    const int64_t kvh = blockIdx.y, b = blockIdx.z;
     const int64_t bh = b * a.hkv + kvh;
-    if (a.gate && !a.gate[bh]) return;  // recompute pass: a group none of whose heads is recomputed
     const int g = a.g;
     const int nb = (int)a.nb;
     constexpr int NT = NW * 64;
@@ -930,6 +928,59 @@ __global__ __launch_bounds__(NW * 64, NW / 4) void decode_mfma_kernel(DecodeArgs
     }
 }
 
+template <bool CERT>
+__global__ __launch_bounds__(NW * 64, NW / 4) void decode_mfma_kernel(DecodeArgs a) {
+    decode_group<CERT>(a, blockIdx.x, blockIdx.y, blockIdx.z);
+}
+
+// Index of the rank-th group i in [0, n) (in index order) with a set byte
+// among flags[i*g, i*g + g), or -1: a count over chunks of NT groups, with
+// each wave's ballot and the per-wave totals in wcnt.  Every thread returns
+// the same value.
+__device__ int64_t nth_set(const uint8_t *flags, const int g, const int64_t n, const int rank, int *wcnt,
+                           int64_t *pick) {
+    constexpr int NT = NW * 64;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    __syncthreads();  // earlier readers of pick and wcnt are done
+    if (tid == 0) *pick = -1;
+    int base = 0;
+    for (int64_t c0 = 0; c0 < n && base <= rank; c0 += NT) {
+        const int64_t i = c0 + tid;
+        bool f = false;
+        if (i < n)
+            for (int k = 0; k < g; ++k) f = f || flags[i * g + k] != 0;
+        const uint64_t bal = __ballot(f);
+        if (lane == 0) wcnt[wave] = __popcll(bal);
+        __syncthreads();
+        int before = 0, tot = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            const int v = wcnt[w];
+            before += w < wave ? v : 0;
+            tot += v;
+        }
+        if (f && base + before + __popcll(bal & ((1ull << lane) - 1ull)) == rank) *pick = i;
+        base += tot;
+        __syncthreads();  // wcnt is rewritten by the next chunk; pick is final
+    }
+    __syncthreads();
+    return *pick;
+}
+
+// Recompute pass over the (b, kvh) groups holding a flagged head: grid
+// (splits, slots), slot y taking the set groups of rank y, y + slots, ...
+// Few groups are expected, and their count is known only on the device, so
+// a small grid spreads them over the chip instead of a grid over every group.
+__global__ __launch_bounds__(NW * 64, NW / 4) void decode_mfma_gated_kernel(DecodeArgs a, int64_t nbh) {
+    __shared__ int wcnt[NW];
+    __shared__ int64_t pick;
+    for (int rank = blockIdx.y;; rank += gridDim.y) {
+        const int64_t bh = nth_set(a.gate, a.g, nbh, rank, wcnt, &pick);
+        if (bh < 0) break;
+        decode_group<false>(a, blockIdx.x, bh % a.hkv, bh / a.hkv);
+    }
+}
+
 bool mfma_supports(int g) { return g >= 1 && g <= 16; }
 
 hipError_t launch_decode_mfma(const DecodeArgs &a, int batch, hipStream_t s) {
@@ -938,6 +989,12 @@ hipError_t launch_decode_mfma(const DecodeArgs &a, int batch, hipStream_t s) {
         hipLaunchKernelGGL(decode_mfma_kernel<true>, grid, dim3(NW * 64), 0, s, a);
     else
         hipLaunchKernelGGL(decode_mfma_kernel<false>, grid, dim3(NW * 64), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_mfma_gated(const DecodeArgs &a, int batch, int slots, hipStream_t s) {
+    dim3 grid((unsigned)a.splits, (unsigned)slots, 1);
+    hipLaunchKernelGGL(decode_mfma_gated_kernel, grid, dim3(NW * 64), 0, s, a, (int64_t)batch * a.hkv);
     return hipGetLastError();
 }
 

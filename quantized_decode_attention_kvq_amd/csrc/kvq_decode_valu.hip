@@ -259,51 +259,62 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
 
 // ------------------------------------------------------------ split merge
 
-// Log-sum-exp merge of the splits of one (b, kvh), in log2 units: M = max m_s,
-// L = sum l_s 2^(m_s - M), out = sum acc_s 2^(m_s - M) / L, written as fp16.
-// The per-(split, head) weights 2^(m_s - M) / L are formed once in LDS; the
-// accumulators are then summed with coalesced loads, several splits in
-// flight per thread.  No split holding a valid token (length 0) gives 0.
+static_assert(MAX_SPLITS <= 128, "the split merge covers at most 128 splits (two per lane)");
+
+// Split merge of head h of (b, kvh): with M = max_s m_s and
+// L = sum_s l_s 2^(m_s - M), out = sum_s 2^(m_s - M) acc_s / L.  One
+// workgroup per head; wave w sums the splits w, w + 4, ..., lane l holds
+// channels 2l and 2l + 1, and the four waves' sums meet in LDS.  With no
+// valid token in any split (length 0) the output is 0.
 __global__ __launch_bounds__(256) void merge_splits_kernel(DecodeArgs a) {
-    __shared__ float wgt[MAX_SPLITS][16];
-    __shared__ float2 ml[MAX_SPLITS][16];
-    const int64_t kvh = blockIdx.x, b = blockIdx.y;
+    __shared__ float2 red[4][64];
+    const int h = blockIdx.x;
+    const int64_t kvh = blockIdx.y, b = blockIdx.z;
     const int64_t bh = b * a.hkv + kvh;
-    if (a.gate && !a.gate[bh]) return;  // recompute pass: nothing of this group is recomputed
     const int g = a.g, S = a.splits;
-    const float2 *pml = a.part_ml + bh * S * g;
-    for (int i = threadIdx.x; i < S * g; i += blockDim.x) ml[i / g][i % g] = pml[i];
-    __syncthreads();
-    for (int i = threadIdx.x; i < S * g; i += blockDim.x) {
-        const int s = i / g, h = i % g;
-        float M = -__builtin_huge_valf();
-        for (int r = 0; r < S; ++r) M = fmaxf(M, ml[r][h].x);
-        float L = 0.0f;
-        for (int r = 0; r < S; ++r)
-            if (ml[r][h].x != -__builtin_huge_valf()) L += ml[r][h].y * __builtin_amdgcn_exp2f(ml[r][h].x - M);
-        const float m_s = ml[s][h].x;
-        wgt[s][h] = (L > 0.0f && m_s != -__builtin_huge_valf()) ? __builtin_amdgcn_exp2f(m_s - M) / L : 0.0f;
+    const int64_t head = b * a.hq + kvh * g + h;
+    if (a.gate && !a.gate[head]) return;  // recompute pass: only the recomputed heads
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const float2 *pml = a.part_ml + bh * S * g + h;  // split s at pml[s * g]
+    constexpr float NEG_INF = -__builtin_huge_valf();
+    // M and L over the splits (at most 128: lanes l and l + 64)
+    const float2 e0 = lane < S ? pml[lane * g] : make_float2(NEG_INF, 0.0f);
+    const float2 e1 = lane + 64 < S ? pml[(lane + 64) * g] : make_float2(NEG_INF, 0.0f);
+    float M = fmaxf(e0.x, e1.x);
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
+    float L = 0.0f;
+    if (e0.x != NEG_INF) L += e0.y * __builtin_amdgcn_exp2f(e0.x - M);
+    if (e1.x != NEG_INF) L += e1.y * __builtin_amdgcn_exp2f(e1.x - M);
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) L += __shfl_xor(L, o);
+    const float *pacc = a.part_acc + (bh * S * g + h) * D + 2 * lane;  // split s at pacc[s * g * D]
+    float2 acc = make_float2(0.0f, 0.0f);
+#pragma unroll 8
+    for (int s = wave; s < S; s += 4) {
+        const float m_s = pml[s * g].x;
+        const float w = (L > 0.0f && m_s != NEG_INF) ? __builtin_amdgcn_exp2f(m_s - M) / L : 0.0f;
+        const float2 v = *reinterpret_cast<const float2 *>(pacc + (int64_t)s * g * D);
+        acc.x += w * v.x;
+        acc.y += w * v.y;
     }
+    red[wave][lane] = acc;
     __syncthreads();
-    const float *pacc = a.part_acc + bh * S * g * D;
-    for (int idx = threadIdx.x; idx < g * D; idx += blockDim.x) {
-        const int h = idx / D;
-        float o = 0.0f;
-        int s = 0;
-        for (; s + 8 <= S; s += 8) {
-            float v[8];
+    if (wave == 0) {
+        float2 o = red[0][lane];
 #pragma unroll
-            for (int k = 0; k < 8; ++k) v[k] = pacc[(int64_t)(s + k) * g * D + idx];
-#pragma unroll
-            for (int k = 0; k < 8; ++k) o += wgt[s + k][h] * v[k];
+        for (int w = 1; w < 4; ++w) {
+            o.x += red[w][lane].x;
+            o.y += red[w][lane].y;
         }
-        for (; s < S; ++s) o += wgt[s][h] * pacc[(int64_t)s * g * D + idx];
-        if (!a.head_gate || a.head_gate[b * a.hq + kvh * g + h]) a.out[((b * a.hq) + kvh * g) * D + idx] = (uint16_t)f2h_rn(o);
+        const uint32_t pair = (uint32_t)f2h_rn(o.x) | ((uint32_t)f2h_rn(o.y) << 16);
+        *reinterpret_cast<uint32_t *>(a.out + head * D + 2 * lane) = pair;
     }
 }
 
 hipError_t launch_merge(const DecodeArgs &a, int batch, hipStream_t s) {
-    hipLaunchKernelGGL(merge_splits_kernel, dim3((unsigned)a.hkv, (unsigned)batch), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(merge_splits_kernel, dim3((unsigned)a.g, (unsigned)a.hkv, (unsigned)batch), dim3(256), 0, s,
+                       a);
     return hipGetLastError();
 }
 

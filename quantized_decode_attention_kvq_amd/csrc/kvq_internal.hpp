@@ -60,11 +60,9 @@ struct DecodeArgs {
     float tau_out;          // heads whose certificate exceeds it are recomputed on FP16
     float *cert;            // [B][Hq] certificate (written by the certificate merge)
     uint8_t *flags;         // [B][Hq] 1: the head is recomputed
-    uint8_t *gate_out;      // [B*Hkv] 1: some head of the group is recomputed
-    // recompute pass: only groups with gate[bh] run, only heads with
-    // head_gate[b][h] are written (both null otherwise)
+    // recompute pass: per-head flags [B*Hq]; only groups holding a flagged
+    // head run and only flagged heads are written (null otherwise)
     const uint8_t *gate;
-    const uint8_t *head_gate;
 };
 
 // Upper limits that size the workspace and LDS tables.
@@ -77,6 +75,9 @@ hipError_t launch_bounds(const BoundsArgs &a, int batch, hipStream_t s);
 // The split-K kernels (the cross-split merge is launched separately).
 hipError_t launch_decode_valu(const DecodeArgs &a, int batch, hipStream_t s);
 hipError_t launch_decode_mfma(const DecodeArgs &a, int batch, hipStream_t s);
+// recompute pass: only the (b, kvh) groups holding a head with a.gate set,
+// on a grid of (a.splits, slots) workgroups
+hipError_t launch_decode_mfma_gated(const DecodeArgs &a, int batch, int slots, hipStream_t s);
 hipError_t launch_merge(const DecodeArgs &a, int batch, hipStream_t s);
 // The merge of a certified decode: outputs, per-head certificates, recompute flags.
 hipError_t launch_merge_cert(const DecodeArgs &a, int batch, hipStream_t s);
