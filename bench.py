@@ -72,6 +72,8 @@ def parse():
                    help="skip timing the step with the per-head output certificate (kvq_decode_attn_cert)")
     p.add_argument("--recompute-frac", type=float, default=0.01,
                    help="certified step with recompute: tau_out set so that about this fraction of heads is flagged")
+    p.add_argument("--tier2", default="device", choices=["device", "host"],
+                   help="FP16 originals in HBM, or in pinned host memory read in place over the host link")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run one 1 GiB device copy (reference kernel for HBM counters)")
     return p.parse_args()
@@ -326,9 +328,14 @@ def main():
     R = args.replicas or int(max(2, np.ceil(2e9 / tier1)))
     caches = []
     for r in range(R):
-        k16 = d["k16"] if r == 0 else d["k16"].clone()
-        v16 = d["v16"] if r == 0 else d["v16"].clone()
-        c = kvq.KVCache(w.B, w.Hkv, w.cap, device=dev, k16=k16, v16=v16)
+        if args.tier2 == "host":
+            c = kvq.KVCache(w.B, w.Hkv, w.cap, device=dev, tier2="host")
+            c.k16.copy_(d["k16"])
+            c.v16.copy_(d["v16"])
+        else:
+            k16 = d["k16"] if r == 0 else d["k16"].clone()
+            v16 = d["v16"] if r == 0 else d["v16"].clone()
+            c = kvq.KVCache(w.B, w.Hkv, w.cap, device=dev, k16=k16, v16=v16)
         kvq.kvq_quantize_append(c, w.T - 1)  # prefill; the step appends token T-1
         caches.append(c)
     q = d["q"].contiguous()
@@ -448,6 +455,7 @@ def main():
             "layers_cycled": R,
             "kernel": args.kernel, "splits": args.splits, "hip_graph": bool(args.graph), "steps_per_graph": R if args.graph else None,
             "fused_append": not args.unfused,
+            "tier2": args.tier2,
             "bytes_per_step": step_bytes,
         },
         "roofline": {
@@ -468,6 +476,12 @@ def main():
     }
     if certified is not None:
         line["certified_step"] = certified
+    if args.tier2 == "host":
+        # bytes each step reads from host memory: fallback tiles and the
+        # appended rows (the rest of the step reads tier 1 in HBM)
+        host_bytes = int(((m & 1) != 0).sum() + ((m & 2) != 0).sum()) * 16384 + w.B * w.Hkv * 512
+        line["tier2_host"] = {"bytes_per_step": host_bytes,
+                              "host_link_gbs": round(host_bytes / (ms_step * 1e-3) / 1e9, 2)}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, d, tau_k, tau_v, sm, args.cpu_seconds)
     print(json.dumps(line), flush=True)

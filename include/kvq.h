@@ -40,9 +40,10 @@
  *               k~ = bit0 ? fp16 original : s*c and v~ = bit1 ? fp16 original
  *               : s*c.  Output fp16.  length 0 gives a zero output.
  *
- * Memory layout (all device memory, caller-allocated, head-major so that each
- * 64-token block of one (batch, KV head) is contiguous).  cap = capacity in
- * tokens, a multiple of 64; NBc = cap/64.
+ * Memory layout (device memory, caller-allocated, head-major so that each
+ * 64-token block of one (batch, KV head) is contiguous; tier 2 may instead be
+ * pinned host memory, see kvq_tier2_location).  cap = capacity in tokens, a
+ * multiple of 64; NBc = cap/64.
  *   k16, v16   uint16 (fp16 bits) [B][Hkv][cap][128]  FP16 originals (tier 2)
  *   k_codes    int8               [B][Hkv][cap][128]
  *   k_scales   uint16 (fp16)      [B][Hkv][cap]
@@ -93,7 +94,8 @@ typedef enum {
 } kvq_status;
 
 /* A quantized KV cache for one attention layer.  The struct is host memory;
- * every pointer in it is device memory owned by the caller. */
+ * every pointer in it is owned by the caller: device memory, except that
+ * k16/v16 may be pinned host memory the device reads (kvq_tier2_location). */
 typedef struct kvq_cache {
     int32_t batch;        /* B */
     int32_t kv_heads;     /* Hkv */
@@ -117,6 +119,19 @@ typedef struct kvq_cache {
  * v_codes, v_scales, k_err, v_err, for the shape fields of *c (pointers and
  * length are ignored).  Host only. */
 kvq_status kvq_cache_bytes(const kvq_cache *c, size_t bytes_out[6]);
+
+/* Where tier 2 lives (Methodology 1 keeps the FP16 originals in pinned
+ * system RAM, as the ground truth that fallback pages in).  *where_out = 0
+ * when k16 and v16 are both device memory of the current device; 1 when both
+ * are pinned host memory that the current device reads at the same address.
+ * With 1, every kernel reads tier 2 in place over the host link (zero-copy:
+ * the fused append's new rows, the bulk append's rows and every fallback
+ * tile), with no staging copy.  Call it once when the cache is set up, before
+ * any other entry point touches a host tier 2.  Host only, enqueues nothing.
+ * Errors: INVALID_ARG for null pointers, a mix of the two kinds, pageable or
+ * unknown host memory, another device's memory, or host memory the device
+ * sees at another address; HIP when the attribute query itself fails. */
+kvq_status kvq_tier2_location(const kvq_cache *c, int32_t *where_out);
 
 /* Quantize-on-append (Methodology 1: tier-1 codes, scales and per-block error
  * annotations derived from the FP16 originals).  Quantizes tokens

@@ -52,7 +52,7 @@ class _Cache(ctypes.Structure):
 _lib = None
 EXPORTS = ("kvq_cache_bytes", "kvq_quantize_append", "kvq_bounds", "kvq_decode_workspace_bytes",
            "kvq_decode_attn", "kvq_decode_attn_ex", "kvq_append_decode", "kvq_append_decode_ex",
-           "kvq_decode_attn_cert", "kvq_status_str", "kvq_last_hip_error")
+           "kvq_decode_attn_cert", "kvq_tier2_location", "kvq_status_str", "kvq_last_hip_error")
 
 
 def lib_path():
@@ -86,6 +86,8 @@ def lib():
         L.kvq_append_decode_ex.restype = ctypes.c_int
         L.kvq_decode_attn_cert.argtypes = [CP, P, i32, f32, f32, f32, f32, i32, P, P, P, P, P, sz, P]
         L.kvq_decode_attn_cert.restype = ctypes.c_int
+        L.kvq_tier2_location.argtypes = [CP, ctypes.POINTER(i32)]
+        L.kvq_tier2_location.restype = ctypes.c_int
         L.kvq_status_str.argtypes = [ctypes.c_int]
         L.kvq_status_str.restype = ctypes.c_char_p
         L.kvq_last_hip_error.argtypes = []
@@ -118,21 +120,30 @@ class KVCache:
         v_codes    uint8 [B][Hkv][cap/64][128][32]
         v_scales   fp16  [B][Hkv][cap][4]
         k_err, v_err float32 [B][Hkv][cap/64]
-    `length` is host-side and advanced by kvq_quantize_append."""
+    `length` is host-side and advanced by kvq_quantize_append.
+    tier2="host" keeps k16/v16 in pinned host memory that the kernels read
+    in place (zero-copy over the host link), checked by kvq_tier2_location."""
 
-    def __init__(self, batch, kv_heads, capacity, device="cuda", k16=None, v16=None):
+    def __init__(self, batch, kv_heads, capacity, device="cuda", k16=None, v16=None, tier2="device"):
         if capacity % BLK:
             raise ValueError("capacity must be a multiple of 64")
         dev = torch.device(device)
         if dev.type == "cuda" and dev.index is None:
             dev = torch.device("cuda", torch.cuda.current_device())
+        if tier2 not in ("device", "host"):
+            raise ValueError("tier2 must be 'device' or 'host'")
         shape = (batch, kv_heads, capacity, D)
         self.batch, self.kv_heads, self.capacity, self.length = batch, kv_heads, capacity, 0
-        self.k16 = k16 if k16 is not None else torch.zeros(shape, dtype=torch.float16, device=dev)
-        self.v16 = v16 if v16 is not None else torch.zeros(shape, dtype=torch.float16, device=dev)
+        self.tier2 = tier2
+        host = tier2 == "host"
+        t2dev = torch.device("cpu") if host else dev
+        self.k16 = k16 if k16 is not None else torch.zeros(shape, dtype=torch.float16, device=t2dev, pin_memory=host)
+        self.v16 = v16 if v16 is not None else torch.zeros(shape, dtype=torch.float16, device=t2dev, pin_memory=host)
         for t in (self.k16, self.v16):
-            if t.shape != shape or t.dtype != torch.float16 or not t.is_contiguous() or t.device != dev:
-                raise ValueError(f"tier-2 tensors must be contiguous fp16 {shape} on {dev}")
+            placed = (t.device.type == "cpu" and t.is_pinned()) if host else t.device == dev
+            if t.shape != shape or t.dtype != torch.float16 or not t.is_contiguous() or not placed:
+                where = "pinned host memory" if host else str(dev)
+                raise ValueError(f"tier-2 tensors must be contiguous fp16 {shape} in {where}")
         nbc = capacity // BLK
         self.k_codes = torch.empty(shape, dtype=torch.int8, device=dev)
         self.k_scales = torch.empty((batch, kv_heads, capacity), dtype=torch.float16, device=dev)
@@ -140,6 +151,11 @@ class KVCache:
         self.v_scales = torch.empty((batch, kv_heads, capacity, D // VG), dtype=torch.float16, device=dev)
         self.k_err = torch.zeros((batch, kv_heads, nbc), dtype=torch.float32, device=dev)
         self.v_err = torch.zeros((batch, kv_heads, nbc), dtype=torch.float32, device=dev)
+        if host:
+            with torch.cuda.device(dev):
+                where = kvq_tier2_location(self)
+            if where != 1:
+                raise ValueError("tier 2 is not host memory the device reads in place")
 
     @property
     def nblocks(self):
@@ -155,6 +171,14 @@ class KVCache:
         out = (ctypes.c_size_t * 6)()
         _check("kvq_cache_bytes", lib().kvq_cache_bytes(ctypes.byref(self.c_struct()), out))
         return list(out)
+
+
+def kvq_tier2_location(cache: KVCache) -> int:
+    """0 if the cache's tier 2 is device memory, 1 if it is pinned host memory
+    the device reads in place (raises KvqError otherwise)."""
+    where = ctypes.c_int32(-1)
+    _check("kvq_tier2_location", lib().kvq_tier2_location(ctypes.byref(cache.c_struct()), ctypes.byref(where)))
+    return int(where.value)
 
 
 def kvq_quantize_append(cache: KVCache, n_new: int, stream=None):
@@ -196,7 +220,7 @@ def make_workspace(cache: KVCache, q_heads: int, device=None):
     n = kvq_decode_workspace_bytes(cache, q_heads)
     if n == 0:
         raise ValueError("invalid cache shape or q_heads")
-    return torch.zeros(n, dtype=torch.uint8, device=device or cache.k16.device)
+    return torch.zeros(n, dtype=torch.uint8, device=device or cache.k_codes.device)
 
 
 def kvq_decode_attn(cache: KVCache, q, sm_scale=DEFAULT_SM_SCALE, tau_k=0.0, tau_v=0.0, out=None,

@@ -142,6 +142,42 @@ const char *kvq_status_str(kvq_status s) {
 
 int kvq_last_hip_error(void) { return g_last_hip_error; }
 
+// Kind of the memory at p for the current device: 0 device memory, 1 pinned
+// host memory mapped at the same address, -1 anything else; -2 (with *err
+// set) when the query fails for another reason.
+static int tier2_kind(const void *p, hipError_t *err) {
+    hipPointerAttribute_t at;
+    const hipError_t e = hipPointerGetAttributes(&at, p);
+    if (e == hipErrorInvalidValue) {  // memory HIP does not know (pageable)
+        (void)hipGetLastError();
+        return -1;
+    }
+    if (e != hipSuccess) {
+        *err = e;
+        return -2;
+    }
+    int dev = 0;
+    const hipError_t ed = hipGetDevice(&dev);
+    if (ed != hipSuccess) {
+        *err = ed;
+        return -2;
+    }
+    if (at.type == hipMemoryTypeDevice && at.device == dev) return 0;
+    if (at.type == hipMemoryTypeHost && at.devicePointer == p) return 1;
+    return -1;
+}
+
+kvq_status kvq_tier2_location(const kvq_cache *c, int32_t *where_out) {
+    if (!c || !where_out || !c->k16 || !c->v16) return KVQ_ERR_INVALID_ARG;
+    hipError_t err = hipSuccess;
+    const int kk = tier2_kind(c->k16, &err);
+    const int kv = kk == -2 ? -2 : tier2_kind(c->v16, &err);
+    if (kk == -2 || kv == -2) return hip_fail(err);
+    if (kk < 0 || kv < 0 || kk != kv) return KVQ_ERR_INVALID_ARG;
+    *where_out = kk;
+    return KVQ_OK;
+}
+
 kvq_status kvq_cache_bytes(const kvq_cache *c, size_t bytes_out[6]) {
     kvq_status st = check_shape(c);
     if (st != KVQ_OK) return st;

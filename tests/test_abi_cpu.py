@@ -104,3 +104,12 @@ def test_status_strings():
     for s in (OK, INVALID, UNSUPPORTED, CAPACITY, ALIGNMENT, WORKSPACE, -6):
         assert L().kvq_status_str(s)
     assert L().kvq_last_hip_error() == 0
+
+
+@pytest.mark.parametrize("field", ["k16", "v16"])
+def test_tier2_location_rejects_null_pointers(field):
+    where = ctypes.c_int32(7)
+    assert L().kvq_tier2_location(ctypes.byref(cache(**{field: None})), ctypes.byref(where)) == INVALID
+    assert where.value == 7
+    assert L().kvq_tier2_location(None, ctypes.byref(where)) == INVALID
+    assert L().kvq_tier2_location(ctypes.byref(cache()), None) == INVALID
