@@ -63,6 +63,9 @@ def lib():
         L.kvqo_certificate.argtypes = [i32, i32, i32, i64, i64, P, f32, f32, f32, ctypes.c_double,
                                        P, P, P, P, P, P, P, P, P, P, P, P, P]
         L.kvqo_certificate.restype = None
+        dbl = ctypes.c_double
+        L.kvqo_adaptive.argtypes = [i32, i32, i32, i64, i64, P, f32, f32, f32, dbl, dbl, dbl, dbl] + [P] * 20
+        L.kvqo_adaptive.restype = None
         _lib = L
     return _lib
 
@@ -211,6 +214,38 @@ class Cache:
                                _p(self.k_scales), _p(self.v_codes), _p(self.v_scales), _p(self.k_err),
                                _p(self.v_err), _p(r["out"]), _p(r["cert"]), _p(r["e_key"]),
                                _p(r["e_val"]), _p(r["recomputed"]))
+        return r
+
+
+    def adaptive(self, q, sm, tau_k, tau_v, tau_cov, tau_vc=float("inf"), tau_rank=1.0, tau_out=float("inf")):
+        """Adaptive precision with the ranking check and rungs 1-3 (see
+        kvqo_adaptive): dict of out, cert, e_key, e_val, recomputed (as
+        certificate), masks (uint8 [B][Hkv][NB], bounds OR promotions), lhat
+        and lfp (fp64 [B][Hq][NB], natural-log block masses from the INT8 and
+        FP16 keys), kstar (int32 [B][Hq]), ndisc and npairs (int64 [B][Hq])
+        and inconsistent (uint8 [B][Hq])."""
+        q = _c(q, np.float16)
+        B, Hq, d = q.shape
+        assert B == self.B and d == D and Hq % self.Hkv == 0
+        nb = (self.length + BLK - 1) // BLK
+        r = {k: np.zeros((B, Hq), np.float64) for k in ("cert", "e_key", "e_val")}
+        r["out"] = np.zeros((B, Hq, D), np.float64)
+        r["recomputed"] = np.zeros((B, Hq), np.uint8)
+        r["masks"] = np.zeros((B, self.Hkv, max(nb, 1)), np.uint8)
+        r["lhat"] = np.zeros((B, Hq, max(nb, 1)), np.float64)
+        r["lfp"] = np.zeros((B, Hq, max(nb, 1)), np.float64)
+        r["kstar"] = np.zeros((B, Hq), np.int32)
+        r["ndisc"] = np.zeros((B, Hq), np.int64)
+        r["npairs"] = np.zeros((B, Hq), np.int64)
+        r["inconsistent"] = np.zeros((B, Hq), np.uint8)
+        lib().kvqo_adaptive(B, Hq, self.Hkv, self.cap, self.length, _p(q), sm, tau_k, tau_v, float(tau_cov),
+                            float(tau_vc), float(tau_rank), float(tau_out), _p(self.k16), _p(self.v16),
+                            _p(self.k_codes), _p(self.k_scales), _p(self.v_codes), _p(self.v_scales),
+                            _p(self.k_err), _p(self.v_err), _p(r["out"]), _p(r["cert"]), _p(r["e_key"]),
+                            _p(r["e_val"]), _p(r["recomputed"]), _p(r["masks"]), _p(r["lhat"]), _p(r["lfp"]),
+                            _p(r["kstar"]), _p(r["ndisc"]), _p(r["npairs"]), _p(r["inconsistent"]))
+        for k in ("masks", "lhat", "lfp"):
+            r[k] = r[k][..., :nb]
         return r
 
 

@@ -457,6 +457,13 @@ void kvqo_attention(int B, int Hq, int Hkv, int64_t cap, int64_t length, const u
  * values: its output is o and recomputed[h] = 1.
  * out, cert, e_key, e_val: double [B][Hq](x128 for out); recomputed uint8
  * [B][Hq].  length == 0 gives zeros. */
+static void certify_masked(int B, int Hq, int Hkv, int64_t cap, int64_t length, const uint16_t *q,
+                           float sm, const uint8_t *m, double tau_out, const uint8_t *force,
+                           const uint16_t *k16, const uint16_t *v16, const int8_t *k_codes,
+                           const uint16_t *k_scales, const uint8_t *v_codes, const uint16_t *v_scales,
+                           const float *k_err, const float *v_err, double *out, double *cert,
+                           double *e_key, double *e_val, uint8_t *recomputed);
+
 void kvqo_certificate(int B, int Hq, int Hkv, int64_t cap, int64_t length, const uint16_t *q,
                       float sm, float tau_k, float tau_v, double tau_out, const uint16_t *k16,
                       const uint16_t *v16, const int8_t *k_codes, const uint16_t *k_scales,
@@ -464,10 +471,26 @@ void kvqo_certificate(int B, int Hq, int Hkv, int64_t cap, int64_t length, const
                       const float *v_err, double *out, double *cert, double *e_key, double *e_val,
                       uint8_t *recomputed)
 {
-    int G = Hq / Hkv;
     int64_t nblk = (length + BLK - 1) / BLK;
     uint8_t *m = (uint8_t *)malloc((size_t)B * Hkv * (size_t)(nblk ? nblk : 1));
     kvqo_bounds(B, Hq, Hkv, cap, length, q, sm, tau_k, tau_v, k_err, v_err, NULL, NULL, m);
+    certify_masked(B, Hq, Hkv, cap, length, q, sm, m, tau_out, NULL, k16, v16, k_codes, k_scales,
+                   v_codes, v_scales, k_err, v_err, out, cert, e_key, e_val, recomputed);
+    free(m);
+}
+
+/* The decode over the fallback masks m ([B][Hkv][nblk]), its certificate,
+ * and the FP16 recompute of the heads whose certificate exceeds tau_out or
+ * whose force[b][h] is set (force may be NULL). */
+static void certify_masked(int B, int Hq, int Hkv, int64_t cap, int64_t length, const uint16_t *q,
+                           float sm, const uint8_t *m, double tau_out, const uint8_t *force,
+                           const uint16_t *k16, const uint16_t *v16, const int8_t *k_codes,
+                           const uint16_t *k_scales, const uint8_t *v_codes, const uint16_t *v_scales,
+                           const float *k_err, const float *v_err, double *out, double *cert,
+                           double *e_key, double *e_val, uint8_t *recomputed)
+{
+    int G = Hq / Hkv;
+    int64_t nblk = (length + BLK - 1) / BLK;
 
 #pragma omp parallel for collapse(2) schedule(dynamic)
     for (int b = 0; b < B; ++b)
@@ -566,7 +589,7 @@ void kvqo_certificate(int B, int Hq, int Hkv, int64_t cap, int64_t length, const
             e_key[oi] = ek;
             e_val[oi] = ev;
             cert[oi] = ek + ev;
-            if (cert[oi] > tau_out) {
+            if (cert[oi] > tau_out || (force && force[oi])) {
                 recomputed[oi] = 1;
                 for (int j = 0; j < D; ++j)
                     o[j] = od[j];
@@ -574,5 +597,192 @@ void kvqo_certificate(int B, int Hq, int Hkv, int64_t cap, int64_t length, const
             free(logit);
             free(dlogit);
         }
-    free(m);
+}
+
+/* -------------------------------------------------------- adaptive precision */
+
+/* Block log-masses of one (b, query head) over blocks [0, nblk):
+ * l[i] = ln sum_{t in block i, t < length} exp(sm * q . k_t), with k_t the
+ * dequantized INT8 key s_t * c_t (fp16 == 0) or the FP16 original
+ * (fp16 == 1).  A log-sum-exp per block, shifted by the block's largest
+ * logit. */
+static void block_logmass(int b, int h, int Hkv, int64_t cap, int64_t length, const double *qv, float sm,
+                          int fp16, const uint16_t *k16, const int8_t *k_codes, const uint16_t *k_scales,
+                          double *l)
+{
+    int64_t nblk = (length + BLK - 1) / BLK;
+    double lg[BLK];
+    for (int64_t i = 0; i < nblk; ++i) {
+        int64_t t0 = i * BLK, t1 = t0 + BLK < length ? t0 + BLK : length;
+        double mx = -INFINITY;
+        for (int64_t t = t0; t < t1; ++t) {
+            size_t r = row_index(b, h, t, Hkv, cap);
+            double s = kvqo_f16_to_f64(k_scales[r]);
+            double acc = 0.0;
+            for (int j = 0; j < D; ++j) {
+                double k = fp16 ? kvqo_f16_to_f64(k16[r * D + j]) : s * (double)k_codes[r * D + j];
+                acc += qv[j] * k;
+            }
+            lg[t - t0] = (double)sm * acc;
+            if (lg[t - t0] > mx)
+                mx = lg[t - t0];
+        }
+        double sum = 0.0;
+        for (int64_t t = t0; t < t1; ++t)
+            sum += exp(lg[t - t0] - mx);
+        l[i] = mx + log(sum);
+    }
+}
+
+static const double *g_sort_keys; /* qsort has no context argument */
+static int by_mass_desc(const void *a, const void *b)
+{
+    double x = g_sort_keys[*(const int64_t *)a], y = g_sort_keys[*(const int64_t *)b];
+    if (x > y)
+        return -1;
+    if (x < y)
+        return 1;
+    return (*(const int64_t *)a > *(const int64_t *)b) - (*(const int64_t *)a < *(const int64_t *)b);
+}
+
+/* Adaptive precision and the fallback ladder ("Runtime-Certified Bounded-Error
+ * Quantized Attention", technical summary, Methodology 3: "Adaptive Top-K
+ * Selection", "Ranking-Consistency Check" and rungs 1-3 of the "Four-Rung
+ * Fallback Ladder"; Key Contributions, "Adaptive Precision").  The page gives
+ * the steps and names tau_cov (its example: 99.5%); the readings below fix
+ * what it leaves open.  For every (b, query head h):
+ *   scoring pass  lhat_i = ln sum_{t in block i} exp(sm * q_h . khat_t) over the
+ *                 dequantized INT8 keys of every block; masses
+ *                 mhat_i = exp(lhat_i - LSE), LSE = ln sum_i exp(lhat_i).
+ *   rung 1        K* = the smallest k whose k largest masses sum to at least
+ *                 tau_cov (0 when tau_cov <= 0; every block when no k does);
+ *                 the head promotes the blocks whose mass is at least the
+ *                 K*-th largest (blocks tied with it are all promoted).  The
+ *                 key tile of a block is promoted when any head of its KV
+ *                 group promotes it.
+ *   rung 2        the value tile of a block is promoted when, for some head
+ *                 of its group, mhat_i * v_err_i > tau_vc.
+ *   masks         the bound masks (kvqo_bounds) OR these promotions.
+ *   ranking check over the head's own promoted blocks P, the FP16 log-masses
+ *                 l_i (the same sum over the FP16 keys); the discordant share
+ *                 disc = #{i < j in P : (lhat_i - lhat_j) * (l_i - l_j) < 0}
+ *                 / (|P| (|P| - 1) / 2), 0 when |P| < 2; the ranking is
+ *                 inconsistent when disc > tau_rank.
+ *   rung 3        the decode over the masks with its certificate
+ *                 (kvqo_certificate's terms); heads whose ranking is
+ *                 inconsistent or whose certificate exceeds tau_out are
+ *                 recomputed on FP16.
+ * Outputs: out, cert, e_key, e_val, recomputed as kvqo_certificate;
+ * masks uint8 [B][Hkv][nblk]; lhat, lfp double [B][Hq][nblk] (lfp for every
+ * block); kstar int32 [B][Hq] (blocks the head promotes, ties included);
+ * ndisc int64 [B][Hq] (discordant pairs);
+ * npairs int64 [B][Hq]; inconsistent uint8 [B][Hq]. */
+void kvqo_adaptive(int B, int Hq, int Hkv, int64_t cap, int64_t length, const uint16_t *q, float sm,
+                   float tau_k, float tau_v, double tau_cov, double tau_vc, double tau_rank, double tau_out,
+                   const uint16_t *k16, const uint16_t *v16, const int8_t *k_codes, const uint16_t *k_scales,
+                   const uint8_t *v_codes, const uint16_t *v_scales, const float *k_err, const float *v_err,
+                   double *out, double *cert, double *e_key, double *e_val, uint8_t *recomputed,
+                   uint8_t *masks, double *lhat, double *lfp, int32_t *kstar, int64_t *ndisc,
+                   int64_t *npairs, uint8_t *inconsistent)
+{
+    int G = Hq / Hkv;
+    int64_t nblk = (length + BLK - 1) / BLK;
+    size_t nb1 = (size_t)(nblk ? nblk : 1);
+    uint8_t *prom = (uint8_t *)calloc((size_t)B * Hq * nb1, 1); /* each head's own promotions */
+    kvqo_bounds(B, Hq, Hkv, cap, length, q, sm, tau_k, tau_v, k_err, v_err, NULL, NULL, masks);
+
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int b = 0; b < B; ++b)
+        for (int hq = 0; hq < Hq; ++hq) {
+            int h = hq / G;
+            size_t oi = (size_t)b * Hq + hq;
+            double qv[D];
+            for (int j = 0; j < D; ++j)
+                qv[j] = kvqo_f16_to_f64(q[oi * D + j]);
+            double *lh = lhat + oi * nb1, *lf = lfp + oi * nb1;
+            uint8_t *ph = prom + oi * nb1;
+            block_logmass(b, h, Hkv, cap, length, qv, sm, 0, k16, k_codes, k_scales, lh);
+            block_logmass(b, h, Hkv, cap, length, qv, sm, 1, k16, k_codes, k_scales, lf);
+            kstar[oi] = 0;
+            ndisc[oi] = npairs[oi] = 0;
+            inconsistent[oi] = 0;
+            if (nblk == 0)
+                continue;
+            /* masses of the scoring pass */
+            double mx = -INFINITY, tot = 0.0;
+            for (int64_t i = 0; i < nblk; ++i)
+                if (lh[i] > mx)
+                    mx = lh[i];
+            for (int64_t i = 0; i < nblk; ++i)
+                tot += exp(lh[i] - mx);
+            double lse = mx + log(tot);
+            double *mh = (double *)malloc(sizeof(double) * (size_t)nblk);
+            int64_t *ord = (int64_t *)malloc(sizeof(int64_t) * (size_t)nblk);
+            for (int64_t i = 0; i < nblk; ++i) {
+                mh[i] = exp(lh[i] - lse);
+                ord[i] = i;
+            }
+            /* rung 1: the smallest top set covering tau_cov, ties included */
+            int64_t k = 0;
+            if (tau_cov > 0.0) {
+#pragma omp critical(kvqo_sort)
+                {
+                    g_sort_keys = mh;
+                    qsort(ord, (size_t)nblk, sizeof(int64_t), by_mass_desc);
+                }
+                double cum = 0.0;
+                k = nblk;
+                for (int64_t r = 0; r < nblk; ++r) {
+                    cum += mh[ord[r]];
+                    if (cum >= tau_cov) {
+                        k = r + 1;
+                        break;
+                    }
+                }
+            }
+            if (k > 0) {
+                double theta = mh[ord[k - 1]];
+                for (int64_t i = 0; i < nblk; ++i) {
+                    ph[i] = mh[i] >= theta;
+                    kstar[oi] += ph[i];
+                }
+            }
+            /* ranking check over the head's promoted blocks */
+            int64_t nd = 0, np = 0;
+            for (int64_t i = 0; i < nblk; ++i) {
+                if (!ph[i])
+                    continue;
+                for (int64_t j = i + 1; j < nblk; ++j) {
+                    if (!ph[j])
+                        continue;
+                    ++np;
+                    if ((lh[i] - lh[j]) * (lf[i] - lf[j]) < 0.0)
+                        ++nd;
+                }
+            }
+            ndisc[oi] = nd;
+            npairs[oi] = np;
+            inconsistent[oi] = np > 0 && (double)nd > tau_rank * (double)np;
+            /* rung 2 marks go to the group's masks below; keep mh in prom's
+             * place via the value flag bit 1 */
+            for (int64_t i = 0; i < nblk; ++i) {
+                size_t si = blk_index(b, h, i, Hkv, cap);
+                if (mh[i] * (double)v_err[si] > tau_vc)
+                    ph[i] |= 2;
+            }
+            free(mh);
+            free(ord);
+        }
+    /* the group's union of its heads' promotions into the masks */
+    for (int b = 0; b < B; ++b)
+        for (int hq = 0; hq < Hq; ++hq) {
+            int h = hq / G;
+            const uint8_t *ph = prom + ((size_t)b * Hq + hq) * nb1;
+            uint8_t *mk = masks + ((size_t)b * Hkv + h) * (size_t)nblk;
+            for (int64_t i = 0; i < nblk; ++i)
+                mk[i] |= ph[i];
+        }
+    free(prom);
+    certify_masked(B, Hq, Hkv, cap, length, q, sm, masks, tau_out, inconsistent, k16, v16, k_codes, k_scales,
+                   v_codes, v_scales, k_err, v_err, out, cert, e_key, e_val, recomputed);
 }
