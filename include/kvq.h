@@ -216,6 +216,49 @@ kvq_status kvq_decode_attn_cert(kvq_cache *c, const uint16_t *q, int32_t q_heads
                                 float *cert, uint8_t *recomputed, uint8_t *mask_out, void *workspace,
                                 size_t ws_bytes, void *stream);
 
+/* Workspace of kvq_decode_attn_adaptive: the decode workspace plus the
+ * scoring pass's block log-masses, the promotions and the FP16 step
+ * statistics (about 4*q_heads*(1 + 16*capacity/64) bytes per sequence more).
+ * 0 on an invalid shape. */
+size_t kvq_adaptive_workspace_bytes(const kvq_cache *c, int32_t q_heads);
+
+/* Adaptive precision with the fallback ladder ("Runtime-Certified Bounded-
+ * Error Quantized Attention", technical summary, Methodology 3: "Adaptive
+ * Top-K Selection", "Ranking-Consistency Check" and rungs 1-3 of the
+ * fallback ladder; Key Contributions "Adaptive Precision").  As
+ * kvq_decode_attn_cert (cert required; recomputed may be NULL; append as
+ * there), with these steps before the decode, for every query head h:
+ *   scoring  a pass over the INT8 keys of every block gives the block's
+ *            log-mass lhat_i = log sum_{t in block i} exp(sm * q_h . k^_t),
+ *            and its mass m_i (the share of sum_i exp(lhat_i)).
+ *   rung 1   the head promotes the blocks whose mass is at least the K*-th
+ *            largest, K* the smallest count whose largest masses sum to
+ *            tau_cov (none for tau_cov == 0; every block when no count gets
+ *            there, e.g. tau_cov > 1); a block's key tile is read as FP16 when
+ *            any head of its KV group promotes it.  kstar [B][q_heads] (int32,
+ *            may be NULL) receives the count each head promotes.
+ *   rung 2   a block's value tile is read as FP16 when m_i * v_err_i >
+ *            tau_vc for some head of the group (+INFINITY: never).
+ *   masks    the bound masks OR these promotions (mask_out receives them).
+ *   check    over the head's own promoted blocks, the pairs whose INT8 and
+ *            FP16 block log-masses are ordered oppositely (the FP16 ones
+ *            from the decode's FP16 key tiles) are counted into ndisc
+ *            [B][q_heads] (int32, may be NULL); a head with more than
+ *            tau_rank * (pairs) of them is inconsistent (tau_rank >= 1: never).
+ *   rung 3   heads that are inconsistent or whose certificate (over the masks
+ *            above) exceeds tau_out are recomputed over the FP16 keys and
+ *            values (recomputed[h] = 1).
+ * The masses and the ranking are evaluated in fp32, so near-ties may fall
+ * either way.  Matrix-core path only; at most 8192 blocks (524,288 tokens)
+ * per sequence.  Errors: as kvq_decode_attn_cert; also INVALID_ARG for NaN
+ * or negative tau_cov, tau_vc or tau_rank, WORKSPACE below
+ * kvq_adaptive_workspace_bytes, UNSUPPORTED past 8192 blocks. */
+kvq_status kvq_decode_attn_adaptive(kvq_cache *c, const uint16_t *q, int32_t q_heads, float sm_scale,
+                                    float tau_k, float tau_v, float tau_cov, float tau_vc, float tau_rank,
+                                    float tau_out, int32_t append, uint16_t *out, float *cert,
+                                    uint8_t *recomputed, int32_t *kstar, int32_t *ndisc, uint8_t *mask_out,
+                                    void *workspace, size_t ws_bytes, void *stream);
+
 /* Decode kernel selection and timing, for measurement.  kvq_decode_attn and
  * kvq_append_decode use KVQ_KERNEL_AUTO; the _ex forms let a benchmark force a variant and a
  * split count (0 = automatic), and, when split_done is a hipEvent_t (passed

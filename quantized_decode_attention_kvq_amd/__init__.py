@@ -52,7 +52,8 @@ class _Cache(ctypes.Structure):
 _lib = None
 EXPORTS = ("kvq_cache_bytes", "kvq_quantize_append", "kvq_bounds", "kvq_decode_workspace_bytes",
            "kvq_decode_attn", "kvq_decode_attn_ex", "kvq_append_decode", "kvq_append_decode_ex",
-           "kvq_decode_attn_cert", "kvq_tier2_location", "kvq_status_str", "kvq_last_hip_error")
+           "kvq_decode_attn_cert", "kvq_adaptive_workspace_bytes", "kvq_decode_attn_adaptive",
+           "kvq_tier2_location", "kvq_status_str", "kvq_last_hip_error")
 
 
 def lib_path():
@@ -86,6 +87,11 @@ def lib():
         L.kvq_append_decode_ex.restype = ctypes.c_int
         L.kvq_decode_attn_cert.argtypes = [CP, P, i32, f32, f32, f32, f32, i32, P, P, P, P, P, sz, P]
         L.kvq_decode_attn_cert.restype = ctypes.c_int
+        L.kvq_adaptive_workspace_bytes.argtypes = [CP, i32]
+        L.kvq_adaptive_workspace_bytes.restype = sz
+        L.kvq_decode_attn_adaptive.argtypes = [CP, P, i32, f32, f32, f32, f32, f32, f32, f32, i32,
+                                               P, P, P, P, P, P, P, sz, P]
+        L.kvq_decode_attn_adaptive.restype = ctypes.c_int
         L.kvq_tier2_location.argtypes = [CP, ctypes.POINTER(i32)]
         L.kvq_tier2_location.restype = ctypes.c_int
         L.kvq_status_str.argtypes = [ctypes.c_int]
@@ -173,6 +179,41 @@ class KVCache:
         return list(out)
 
 
+def kvq_decode_attn_adaptive(cache: KVCache, q, sm_scale=DEFAULT_SM_SCALE, tau_k=0.0, tau_v=0.0, tau_cov=0.995,
+                             tau_vc=float("inf"), tau_rank=1.0, tau_out=float("inf"), append=False, out=None,
+                             cert=None, recomputed=None, kstar=None, ndisc=None, mask_out=None, workspace=None,
+                             stream=None):
+    """Adaptive precision with the fallback ladder (see include/kvq.h):
+    INT8 scoring pass, top-K* promotion covering tau_cov of the estimated
+    mass, value promotion above tau_vc, the certified decode, the ranking
+    check (inconsistent above tau_rank) and the FP16 recompute of
+    inconsistent heads and of heads whose certificate exceeds tau_out.
+    Returns dict(out, cert, recomputed, kstar, ndisc)."""
+    _check_q(cache, q)
+    B, Hq = q.shape[0], q.shape[1]
+    dev = q.device
+    if out is None:
+        out = torch.empty_like(q)
+    if cert is None:
+        cert = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    if recomputed is None:
+        recomputed = torch.empty((B, Hq), dtype=torch.uint8, device=dev)
+    if kstar is None:
+        kstar = torch.empty((B, Hq), dtype=torch.int32, device=dev)
+    if ndisc is None:
+        ndisc = torch.empty((B, Hq), dtype=torch.int32, device=dev)
+    if workspace is None:
+        workspace = make_workspace(cache, Hq, dev, adaptive=True)
+    c = cache.c_struct()
+    st = lib().kvq_decode_attn_adaptive(ctypes.byref(c), _ptr(q), Hq, sm_scale, tau_k, tau_v, tau_cov, tau_vc,
+                                        tau_rank, tau_out, 1 if append else 0, _ptr(out), _ptr(cert),
+                                        _ptr(recomputed), _ptr(kstar), _ptr(ndisc), _ptr(mask_out),
+                                        _ptr(workspace), workspace.numel(), _stream(stream))
+    _check("kvq_decode_attn_adaptive", st)
+    cache.length = int(c.length)
+    return dict(out=out, cert=cert, recomputed=recomputed, kstar=kstar, ndisc=ndisc)
+
+
 def kvq_tier2_location(cache: KVCache) -> int:
     """0 if the cache's tier 2 is device memory, 1 if it is pinned host memory
     the device reads in place (raises KvqError otherwise)."""
@@ -215,9 +256,14 @@ def kvq_decode_workspace_bytes(cache: KVCache, q_heads: int) -> int:
     return int(lib().kvq_decode_workspace_bytes(ctypes.byref(cache.c_struct()), int(q_heads)))
 
 
-def make_workspace(cache: KVCache, q_heads: int, device=None):
-    """A zero-filled workspace for kvq_decode_attn (reusable across calls)."""
-    n = kvq_decode_workspace_bytes(cache, q_heads)
+def kvq_adaptive_workspace_bytes(cache: KVCache, q_heads: int) -> int:
+    return int(lib().kvq_adaptive_workspace_bytes(ctypes.byref(cache.c_struct()), int(q_heads)))
+
+
+def make_workspace(cache: KVCache, q_heads: int, device=None, adaptive=False):
+    """A zero-filled workspace for the decode entry points (reusable across
+    calls); adaptive=True sizes it for kvq_decode_attn_adaptive too."""
+    n = (kvq_adaptive_workspace_bytes if adaptive else kvq_decode_workspace_bytes)(cache, q_heads)
     if n == 0:
         raise ValueError("invalid cache shape or q_heads")
     return torch.zeros(n, dtype=torch.uint8, device=device or cache.k_codes.device)

@@ -8,7 +8,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkvq.so")
-SOURCES = ["kvq_api.hip", "kvq_quantize.hip", "kvq_decode_valu.hip", "kvq_decode_mfma.hip", "kvq_certify.hip"]
+SOURCES = ["kvq_api.hip", "kvq_quantize.hip", "kvq_decode_valu.hip", "kvq_decode_mfma.hip", "kvq_certify.hip", "kvq_adaptive.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

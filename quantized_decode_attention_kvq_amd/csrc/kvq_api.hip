@@ -80,6 +80,25 @@ WsLayout ws_layout(const kvq_cache *c, int32_t g, int64_t splits) {
     return w;
 }
 
+// Adaptive workspace: the decode workspace, then [lhat float x B*Hq*NBc]
+// [phead uint8 x B*Hq*NBc] [promote uint8 x B*Hkv*NBc] [step statistics
+// float2 x B*Hkv*NBc*8*G], each padded to 256 B.
+struct AdaptLayout {
+    size_t lhat, phead, promote, step, total;
+};
+
+AdaptLayout adapt_layout(const kvq_cache *c, int32_t q_heads, size_t base) {
+    const size_t nbc = (size_t)(c->capacity / kvq::BLK);
+    const size_t bq = (size_t)c->batch * (size_t)q_heads, bh = (size_t)c->batch * (size_t)c->kv_heads;
+    AdaptLayout w;
+    w.lhat = round_up(base, 256);
+    w.phead = round_up(w.lhat + bq * nbc * sizeof(float), 256);
+    w.promote = round_up(w.phead + bq * nbc, 256);
+    w.step = round_up(w.promote + bh * nbc, 256);
+    w.total = w.step + bq * nbc * 8 * sizeof(float2);
+    return w;
+}
+
 int64_t max_splits(const kvq_cache *c) {
     const int64_t nbc = c->capacity / kvq::BLK;
     int64_t s = nbc < kvq::MAX_SPLITS ? nbc : kvq::MAX_SPLITS;
@@ -252,18 +271,33 @@ size_t kvq_decode_workspace_bytes(const kvq_cache *c, int32_t q_heads) {
     return ws_layout(c, q_heads / c->kv_heads, max_splits(c)).total;
 }
 
+size_t kvq_adaptive_workspace_bytes(const kvq_cache *c, int32_t q_heads) {
+    const size_t base = kvq_decode_workspace_bytes(c, q_heads);
+    return base ? adapt_layout(c, q_heads, base).total : 0;
+}
+
 }  // extern "C"
 
 namespace {
 
+// Options of the adaptive-precision decode (kvq_decode_attn_adaptive).
+struct AdaptOpts {
+    float tau_cov, tau_vc, tau_rank;
+    int32_t *kstar, *ndisc;
+};
+
+bool bad_tol(float t) { return t != t || t < 0.0f; }
+
 // Decode over the cache's tokens; with append, token `length` (already in
 // k16/v16) is first quantized into tier 1 and joins the decode: fused into
-// the matrix-core kernel, or as an append launch before the VALU kernel.
-// On success with append, c->length grows by one.
+// the matrix-core kernel, or as an append launch before the VALU kernel (and
+// before the scoring pass of the adaptive decode).  On success with append,
+// c->length grows by one.
 kvq_status decode_impl(kvq_cache *c, const uint16_t *q, int32_t q_heads, float sm_scale, float tau_k,
                        float tau_v, uint16_t *out, uint8_t *mask_out, void *workspace, size_t ws_bytes,
                        void *stream, int32_t kernel, int32_t splits, void *split_done, bool append,
-                       float *cert = nullptr, float tau_out = 0.0f, uint8_t *recomputed = nullptr) {
+                       float *cert = nullptr, float tau_out = 0.0f, uint8_t *recomputed = nullptr,
+                       const AdaptOpts *ad = nullptr) {
     kvq_status st = check_shape(c);
     if (st != KVQ_OK) return st;
     if ((st = check_query(c, q, q_heads, sm_scale, tau_k, tau_v)) != KVQ_OK) return st;
@@ -277,6 +311,15 @@ kvq_status decode_impl(kvq_cache *c, const uint16_t *q, int32_t q_heads, float s
     const int32_t g = q_heads / c->kv_heads;
     if (!workspace || ws_bytes < kvq_decode_workspace_bytes(c, q_heads)) return KVQ_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return KVQ_ERR_ALIGNMENT;
+    if (ad) {
+        if (!certify || bad_tol(ad->tau_cov) || bad_tol(ad->tau_vc) || bad_tol(ad->tau_rank))
+            return KVQ_ERR_INVALID_ARG;
+        if ((ad->kstar && !aligned(ad->kstar, 4)) || (ad->ndisc && !aligned(ad->ndisc, 4))) return KVQ_ERR_ALIGNMENT;
+        if (ws_bytes < kvq_adaptive_workspace_bytes(c, q_heads)) return KVQ_ERR_WORKSPACE;
+        const int64_t len1 = c->length + (append ? 1 : 0);
+        if ((len1 + kvq::BLK - 1) / kvq::BLK > kvq::ADAPT_MAX_NB) return KVQ_ERR_UNSUPPORTED;
+        if (kernel == KVQ_KERNEL_VALU) return KVQ_ERR_UNSUPPORTED;
+    }
 
     const int64_t length = c->length + (append ? 1 : 0);  // tokens the decode attends to
     const int64_t nb = (length + kvq::BLK - 1) / kvq::BLK;
@@ -293,8 +336,9 @@ kvq_status decode_impl(kvq_cache *c, const uint16_t *q, int32_t q_heads, float s
     const int64_t bps = nb > 0 ? (nb + s - 1) / s : 1;
     const int64_t s_eff = nb > 0 ? (nb + bps - 1) / bps : 1;
 
-    if (append && !mf) {
-        // no fused path in the VALU kernel: append first
+    if (append && (!mf || ad)) {
+        // no fused path in the VALU kernel, and the adaptive scoring pass
+        // reads the new token's codes: append first
         if ((st = kvq_quantize_append(c, 1, stream)) != KVQ_OK) return st;
         append = false;
     }
@@ -330,13 +374,51 @@ kvq_status decode_impl(kvq_cache *c, const uint16_t *q, int32_t q_heads, float s
     a.cert = cert;
     a.flags = recomputed ? recomputed : reinterpret_cast<uint8_t *>((char *)workspace + w.flags);
     a.gate = nullptr;
+    a.promote = nullptr;
+    a.step_ml = nullptr;
 
-    hipError_t e = mf ? kvq::launch_decode_mfma(a, c->batch, (hipStream_t)stream)
-                      : kvq::launch_decode_valu(a, c->batch, (hipStream_t)stream);
+    hipError_t e = hipSuccess;
+    kvq::AdaptArgs aa;
+    if (ad) {
+        // rungs 1-2: INT8 scoring pass and selection, then the decode with the
+        // promoted tiles and the FP16 step statistics of the ranking check
+        const AdaptLayout al = adapt_layout(c, q_heads, kvq_decode_workspace_bytes(c, q_heads));
+        aa.c = a.c;
+        aa.q = q;
+        aa.lhat = reinterpret_cast<float *>((char *)workspace + al.lhat);
+        aa.phead = reinterpret_cast<uint8_t *>((char *)workspace + al.phead);
+        aa.promote = reinterpret_cast<uint8_t *>((char *)workspace + al.promote);
+        aa.kstar = ad->kstar;
+        aa.step_ml = reinterpret_cast<float2 *>((char *)workspace + al.step);
+        aa.flags = a.flags;
+        aa.ndisc = ad->ndisc;
+        aa.cap = c->capacity;
+        aa.length = length;
+        aa.nbc = nbc;
+        aa.nb = nb;
+        aa.hkv = c->kv_heads;
+        aa.hq = q_heads;
+        aa.g = g;
+        aa.sm = sm_scale;
+        aa.tau_cov = ad->tau_cov;
+        aa.tau_vc = ad->tau_vc;
+        aa.tau_rank = ad->tau_rank;
+        if (nb > 0) e = kvq::launch_score(aa, c->batch, (hipStream_t)stream);
+        if (e == hipSuccess) e = kvq::launch_select(aa, c->batch, (hipStream_t)stream);
+        a.promote = aa.promote;
+        a.step_ml = const_cast<float2 *>(aa.step_ml);
+    }
+    if (e == hipSuccess)
+        e = mf ? kvq::launch_decode_mfma(a, c->batch, (hipStream_t)stream)
+               : kvq::launch_decode_valu(a, c->batch, (hipStream_t)stream);
     if (e == hipSuccess && split_done) e = hipEventRecord((hipEvent_t)split_done, (hipStream_t)stream);
     if (e == hipSuccess) e = certify ? kvq::launch_merge_cert(a, c->batch, (hipStream_t)stream)
                                      : kvq::launch_merge(a, c->batch, (hipStream_t)stream);
-    if (e == hipSuccess && certify && tau_out != __builtin_huge_valf()) {
+    // the ranking check flags inconsistent heads for rung 3 (after the
+    // certificate's flags are written)
+    if (e == hipSuccess && ad) e = kvq::launch_check(aa, c->batch, (hipStream_t)stream);
+    const bool rung3 = certify && (tau_out != __builtin_huge_valf() || (ad && ad->tau_rank < 1.0f));
+    if (e == hipSuccess && rung3) {
         // rung 3: the groups holding a flagged head run again with every
         // block on FP16 (tolerances 0), and the flagged heads take the result
         // (few groups are expected to hold one: every split count the cache
@@ -352,6 +434,8 @@ kvq_status decode_impl(kvq_cache *c, const uint16_t *q, int32_t q_heads, float s
         r.mask_out = nullptr;
         r.cert_mode = 0;
         r.gate = a.flags;
+        r.promote = nullptr;
+        r.step_ml = nullptr;
         const int64_t nbh = (int64_t)c->batch * c->kv_heads;
         int64_t slots = (device_cus() + r.splits - 1) / r.splits;  // about one workgroup per CU
         if (slots > nbh) slots = nbh;
@@ -398,6 +482,17 @@ kvq_status kvq_decode_attn_cert(kvq_cache *c, const uint16_t *q, int32_t q_heads
     if (!cert) return KVQ_ERR_INVALID_ARG;
     return decode_impl(c, q, q_heads, sm_scale, tau_k, tau_v, out, mask_out, workspace, ws_bytes, stream,
                        KVQ_KERNEL_AUTO, 0, nullptr, append != 0, cert, tau_out, recomputed);
+}
+
+kvq_status kvq_decode_attn_adaptive(kvq_cache *c, const uint16_t *q, int32_t q_heads, float sm_scale,
+                                    float tau_k, float tau_v, float tau_cov, float tau_vc, float tau_rank,
+                                    float tau_out, int32_t append, uint16_t *out, float *cert,
+                                    uint8_t *recomputed, int32_t *kstar, int32_t *ndisc, uint8_t *mask_out,
+                                    void *workspace, size_t ws_bytes, void *stream) {
+    if (!cert) return KVQ_ERR_INVALID_ARG;
+    const AdaptOpts ad{tau_cov, tau_vc, tau_rank, kstar, ndisc};
+    return decode_impl(c, q, q_heads, sm_scale, tau_k, tau_v, out, mask_out, workspace, ws_bytes, stream,
+                       KVQ_KERNEL_AUTO, 0, nullptr, append != 0, cert, tau_out, recomputed, &ad);
 }
 
 kvq_status kvq_append_decode(kvq_cache *c, const uint16_t *q, int32_t q_heads, float sm_scale,

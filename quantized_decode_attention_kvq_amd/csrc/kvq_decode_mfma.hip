@@ -52,39 +52,15 @@
 // is ever waited on while later steps are in flight.
 // Waves and splits are merged by log-sum-exp in a second kernel.
 #include "kvq_decode_common.hpp"
+#include "kvq_mfma.hpp"
 #include "kvq_quant_row.hpp"
 
 namespace kvq {
-
-typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
-typedef float float4_t __attribute__((ext_vector_type(4)));
-typedef float float2_t __attribute__((ext_vector_type(2)));
 
 namespace {
 
 constexpr int NW = 8;  // waves per workgroup (one workgroup per CU, NW/4 waves per SIMD)
 constexpr float NEG_INF = -__builtin_huge_valf();
-
-__device__ __forceinline__ float4_t mfma(uint4 a, uint4 b, float4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a),
-                                                  __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
-}
-
-// 4 int8 codes -> 2 x fp16 pairs (exact): offset code u = c + 128 under the
-// fp16 exponent of 1024 reads as 1024 + u; minus 1152 leaves c.
-__device__ __forceinline__ uint2 i8x4_to_h4(uint32_t x) {
-    const uint32_t u = x ^ 0x80808080u;
-    const half2_t bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
-    const half2_t lo = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u)) + bias;
-    const half2_t hi = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u)) + bias;
-    return make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
-}
-
-// 8 int8 codes (two dwords) -> the 8 fp16 k-slots of one A operand.
-__device__ __forceinline__ uint4 i8x8_to_h8(uint32_t x0, uint32_t x1) {
-    const uint2 a = i8x4_to_h4(x0), b = i8x4_to_h4(x1);
-    return make_uint4(a.x, a.y, b.x, b.y);
-}
 
 // 8 int4 codes (one dword, nibble k = token k) -> fp16 pairs (n_p, n_{p+4}),
 // p = 0..3.  A two's-complement nibble n with bit 3 flipped is the offset code
@@ -266,6 +242,9 @@ __device__ __forceinline__ void issue_fb(const DecodeArgs &a, int64_t bh, int64_
 // log2 units (sm * log2(e) folded into the per-token key factor) so the
 // softmax uses exp2.  State: m_run / l_run of head m (this lane's column; l as
 // this lane's share of the 8-position groups) and the P.V accumulators.
+// RANK: a step of FP16 keys also writes, per head, its largest score and the
+// sum of exp2(score - that) over its valid tokens to rank_out[head] (the FP16
+// block masses of the ranking check).
 struct WaveState {
     float m_run, l_run;
     float4_t acc[8];
@@ -276,10 +255,10 @@ struct WaveState {
     uint32_t smax, amax;
 };
 
-template <bool CERT, typename Mid>
+template <bool CERT, bool RANK, typename Mid>
 __device__ __forceinline__ void process_step(const uint8_t *stage, uint32_t mk, int p_lo, int p_hi,
                                              const uint4 (&qb)[4], float sml2, WaveState &w, int lane,
-                                             float eta, Mid &&mid) {
+                                             float eta, float2 *rank_out, int g, Mid &&mid) {
     const int m = lane & 15, g4 = lane >> 4;
     const bool partial = p_lo > 0 || p_hi < 32;  // wave-uniform
 
@@ -338,6 +317,16 @@ __device__ __forceinline__ void process_step(const uint8_t *stage, uint32_t mk, 
 #pragma unroll
         for (int i = 0; i < 4; ++i) bmax = fmaxf(bmax, sc[e][i]);
     bmax = max_across_rows(bmax);
+    if (RANK && (mk & 1u) && rank_out) {
+        float es = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) es += (sc[e][i] == NEG_INF) ? 0.0f : __builtin_amdgcn_exp2f(sc[e][i] - bmax);
+        es += __shfl_xor(es, 16);
+        es += __shfl_xor(es, 32);
+        if (g4 == 0 && m < g) rank_out[m] = make_float2(bmax, es);
+    }
     const float m_new = fmaxf(w.m_run, bmax);
     // a step with no finite score so far leaves m_new at -inf
     const float alpha = (m_new == NEG_INF) ? 1.0f : __builtin_amdgcn_exp2f(w.m_run - m_new);
@@ -497,7 +486,7 @@ __device__ __forceinline__ uint16_t f16_up(float x) {
 // CERT: also the per-head output certificate's per-split parts (the
 // mass-weighted value error, the largest certified value scale and
 // fallback |v|, and the largest certified block errors).
-template <bool CERT>
+template <bool CERT, bool RANK>
 __device__ __forceinline__ void decode_group(const DecodeArgs &a, const int split, const int64_t kvh,
                                              const int64_t b) {
     // NW waves x NSTAGE stages x 6656 B of ring.  Before the stream starts, the
@@ -619,7 +608,8 @@ __device__ __forceinline__ void decode_group(const DecodeArgs &a, const int spli
                 kerr = p_new > 0 ? fmaxf(rq.kerr, kerr) : rq.kerr;
                 verr = p_new > 0 ? fmaxf(rq.verr, verr) : rq.verr;
             }
-            const uint32_t mk = block_mask(a.sm, qn, kerr, verr, a.tau_k, a.tau_v);
+            uint32_t mk = block_mask(a.sm, qn, kerr, verr, a.tau_k, a.tau_v);
+            if (a.promote) mk |= a.promote[bh * a.nbc + i];  // adaptive precision: promoted tiles
             maskb[i] = (uint8_t)mk;
             if (a.mask_out && i >= h0 && i < h1) a.mask_out[bh * a.nb + i] = (uint8_t)mk;
             if (CERT) {
@@ -855,8 +845,9 @@ __device__ __forceinline__ void decode_group(const DecodeArgs &a, const int spli
         const int64_t left = a.length - (blk * BLK + (mk ? 8 * sub : 32 * sub));
         const int nvalid = (int)(left < step_len ? (left > 0 ? left : 0) : step_len);
         if (nvalid > 0)
-            process_step<CERT>(stage, mk, p_lo, p_lo + nvalid, qb, sml2, ws, lane,
-                               CERT ? h2f(teta_lds[blk - blo]) : 0.0f, mid);
+            process_step<CERT, RANK>(stage, mk, p_lo, p_lo + nvalid, qb, sml2, ws, lane,
+                                     CERT ? h2f(teta_lds[blk - blo]) : 0.0f,
+                                     RANK ? a.step_ml + ((bh * a.nbc + blk) * 8 + sub) * g : nullptr, g, mid);
         else
             mid();
         return true;
@@ -928,9 +919,9 @@ __device__ __forceinline__ void decode_group(const DecodeArgs &a, const int spli
     }
 }
 
-template <bool CERT>
+template <bool CERT, bool RANK>
 __global__ __launch_bounds__(NW * 64, NW / 4) void decode_mfma_kernel(DecodeArgs a) {
-    decode_group<CERT>(a, blockIdx.x, blockIdx.y, blockIdx.z);
+    decode_group<CERT, RANK>(a, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
 // Index of the rank-th group i in [0, n) (in index order) with a set byte
@@ -977,7 +968,7 @@ __global__ __launch_bounds__(NW * 64, NW / 4) void decode_mfma_gated_kernel(Deco
     for (int rank = blockIdx.y;; rank += gridDim.y) {
         const int64_t bh = nth_set(a.gate, a.g, nbh, rank, wcnt, &pick);
         if (bh < 0) break;
-        decode_group<false>(a, blockIdx.x, bh % a.hkv, bh / a.hkv);
+        decode_group<false, false>(a, blockIdx.x, bh % a.hkv, bh / a.hkv);
     }
 }
 
@@ -985,10 +976,12 @@ bool mfma_supports(int g) { return g >= 1 && g <= 16; }
 
 hipError_t launch_decode_mfma(const DecodeArgs &a, int batch, hipStream_t s) {
     dim3 grid((unsigned)a.splits, (unsigned)a.hkv, (unsigned)batch);
-    if (a.cert_mode)
-        hipLaunchKernelGGL(decode_mfma_kernel<true>, grid, dim3(NW * 64), 0, s, a);
+    if (a.cert_mode && a.step_ml)
+        hipLaunchKernelGGL((decode_mfma_kernel<true, true>), grid, dim3(NW * 64), 0, s, a);
+    else if (a.cert_mode)
+        hipLaunchKernelGGL((decode_mfma_kernel<true, false>), grid, dim3(NW * 64), 0, s, a);
     else
-        hipLaunchKernelGGL(decode_mfma_kernel<false>, grid, dim3(NW * 64), 0, s, a);
+        hipLaunchKernelGGL((decode_mfma_kernel<false, false>), grid, dim3(NW * 64), 0, s, a);
     return hipGetLastError();
 }
 

@@ -63,12 +63,35 @@ struct DecodeArgs {
     // recompute pass: per-head flags [B*Hq]; only groups holding a flagged
     // head run and only flagged heads are written (null otherwise)
     const uint8_t *gate;
+    // adaptive precision (null otherwise): promoted tiles per (b, kvh,
+    // block) [B*Hkv][nbc] (bit 0 key, bit 1 value), OR-ed into the bound
+    // masks; with the certificate, per FP16 key step its per-head largest
+    // score and exp2-sum, [B*Hkv][nbc][8][G] (log2 units)
+    const uint8_t *promote;
+    float2 *step_ml;
+};
+
+// Adaptive precision (scoring pass, top-K* selection, ranking check).
+struct AdaptArgs {
+    CachePtrs c;
+    const uint16_t *q;
+    float *lhat;             // [B][Hq][nbc] INT8 block log-masses (log2 units)
+    uint8_t *phead;          // [B][Hq][nbc] 1: the head promotes the block's keys
+    uint8_t *promote;        // [B][Hkv][nbc] bit 0 key, bit 1 value promotion (union over the group)
+    int32_t *kstar;          // [B][Hq] blocks each head promotes, or null
+    const float2 *step_ml;   // [B*Hkv][nbc][8][G] FP16 step statistics from the decode
+    uint8_t *flags;          // [B][Hq] recompute flags, set for inconsistent rankings
+    int32_t *ndisc;          // [B][Hq] discordant pairs, or null
+    int64_t cap, length, nbc, nb;
+    int32_t hkv, hq, g;
+    float sm, tau_cov, tau_vc, tau_rank;
 };
 
 // Upper limits that size the workspace and LDS tables.
 constexpr int MAX_SPLITS = 128;
 constexpr int MAX_BPS = 1024;  // blocks per split (mask table in LDS)
 constexpr int MFMA_MAX_BPS = 128;  // blocks per split of the matrix-core kernel (block table in LDS)
+constexpr int ADAPT_MAX_NB = 8192;  // blocks per sequence of the adaptive path (LDS arrays)
 
 hipError_t launch_append(const AppendArgs &a, int batch, int64_t nblk, hipStream_t s);
 hipError_t launch_bounds(const BoundsArgs &a, int batch, hipStream_t s);
@@ -82,5 +105,11 @@ hipError_t launch_merge(const DecodeArgs &a, int batch, hipStream_t s);
 // The merge of a certified decode: outputs, per-head certificates, recompute flags.
 hipError_t launch_merge_cert(const DecodeArgs &a, int batch, hipStream_t s);
 bool mfma_supports(int g);
+
+// adaptive precision: INT8 scoring pass (a.nb > 0), selection and the
+// ranking check
+hipError_t launch_score(const AdaptArgs &a, int batch, hipStream_t s);
+hipError_t launch_select(const AdaptArgs &a, int batch, hipStream_t s);
+hipError_t launch_check(const AdaptArgs &a, int batch, hipStream_t s);
 
 }  // namespace kvq

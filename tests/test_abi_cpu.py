@@ -113,3 +113,24 @@ def test_tier2_location_rejects_null_pointers(field):
     assert where.value == 7
     assert L().kvq_tier2_location(None, ctypes.byref(where)) == INVALID
     assert L().kvq_tier2_location(ctypes.byref(cache()), None) == INVALID
+
+
+def _adaptive(c, ws_bytes, cert=FAKE, tau_cov=0.9, tau_vc=math.inf, tau_rank=0.5, kstar=None):
+    return L().kvq_decode_attn_adaptive(ctypes.byref(c), FAKE, 8, 0.1, 0.0, 0.0, tau_cov, tau_vc, tau_rank,
+                                        math.inf, 0, FAKE, cert, None, kstar, None, None, FAKE, ws_bytes, None)
+
+
+def test_adaptive_validation():
+    c = cache(length=100)
+    base = L().kvq_decode_workspace_bytes(ctypes.byref(c), 8)
+    need = L().kvq_adaptive_workspace_bytes(ctypes.byref(c), 8)
+    assert need > base > 0
+    assert L().kvq_adaptive_workspace_bytes(ctypes.byref(c), 7) == 0
+    assert _adaptive(c, need - 1) == WORKSPACE
+    assert _adaptive(c, need, cert=None) == INVALID
+    for kw in (dict(tau_cov=math.nan), dict(tau_cov=-0.5), dict(tau_vc=math.nan), dict(tau_rank=-1.0)):
+        assert _adaptive(c, need, **kw) == INVALID, kw
+    assert _adaptive(c, need, kstar=FAKE + 2) == ALIGNMENT
+    # more than 8192 blocks per sequence
+    big = cache(B=1, H=1, cap=8194 * 64, length=8193 * 64 + 1)
+    assert _adaptive(big, L().kvq_adaptive_workspace_bytes(ctypes.byref(big), 8)) == UNSUPPORTED
