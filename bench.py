@@ -19,6 +19,9 @@ Prints one JSON line:
              library records one between the split-K and merge kernels),
              against the 8 TB/s HBM3E peak; traffic from committed rocprofv3
              FETCH_SIZE / WRITE_SIZE runs when they match the sources.
+  adaptive_step  the same step through kvq_decode_attn_adaptive (INT8
+             scoring pass, top-K* promotion covering tau_cov, ranking check,
+             recompute of inconsistent heads), with the promoted shares.
   certified_step  the same step through kvq_decode_attn_cert: per-head
              output certificate only, and with the FP16 recompute of the heads
              above a tau_out that flags about 1% of them (ms per step each).
@@ -72,6 +75,11 @@ def parse():
                    help="skip timing the step with the per-head output certificate (kvq_decode_attn_cert)")
     p.add_argument("--recompute-frac", type=float, default=0.01,
                    help="certified step with recompute: tau_out set so that about this fraction of heads is flagged")
+    p.add_argument("--no-adaptive", action="store_true",
+                   help="skip timing the adaptive-precision step (kvq_decode_attn_adaptive)")
+    p.add_argument("--tau-cov", type=float, default=0.995, help="adaptive step: coverage of the INT8 mass")
+    p.add_argument("--tau-rank", type=float, default=0.1, help="adaptive step: discordant share that flags a head")
+    p.add_argument("--tau-vc", type=float, default=float("inf"), help="adaptive step: value-promotion threshold")
     p.add_argument("--tier2", default="device", choices=["device", "host"],
                    help="FP16 originals in HBM, or in pinned host memory read in place over the host link")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -297,6 +305,52 @@ def bench_certified(args, w, caches, ws, q, sm, tau_k, tau_v, ms_plain):
     }
 
 
+def bench_adaptive(args, w, caches, q, sm, tau_k, tau_v, ms_plain):
+    """The same step through kvq_decode_attn_adaptive (append, INT8 scoring
+    pass, selection, certifying decode with the promoted tiles, certificate
+    merge, ranking check, gated FP16 recompute), timed like the plain step."""
+    import numpy as np
+    import torch
+
+    import quantized_decode_attention_kvq_amd as kvq
+
+    R = len(caches)
+    out = torch.empty_like(q)
+    cert = torch.empty((w.B, w.Hq), dtype=torch.float32, device=q.device)
+    rec = torch.empty((w.B, w.Hq), dtype=torch.uint8, device=q.device)
+    kstar = torch.empty((w.B, w.Hq), dtype=torch.int32, device=q.device)
+    ndisc = torch.empty((w.B, w.Hq), dtype=torch.int32, device=q.device)
+    mask = torch.empty((w.B, w.Hkv, (w.T + 63) // 64), dtype=torch.uint8, device=q.device)
+    wsa = [kvq.make_workspace(c, w.Hq, adaptive=True) for c in caches]
+
+    def astep(i, strm, mask_out=None):
+        c = caches[i % R]
+        c.length = w.T - 1
+        kvq.kvq_decode_attn_adaptive(c, q, sm, tau_k, tau_v, args.tau_cov, args.tau_vc, args.tau_rank,
+                                     append=True, out=out, cert=cert, recomputed=rec, kstar=kstar, ndisc=ndisc,
+                                     mask_out=mask_out, workspace=wsa[i % R], stream=strm)
+
+    stream = torch.cuda.current_stream()
+    astep(0, stream, mask)
+    torch.cuda.synchronize()
+    m = mask.cpu().numpy()
+    ks = kstar.cpu().numpy()
+    r = rec.cpu().numpy()
+    ms = timed_steps(args, R, lambda i, strm: astep(i, strm), stream)
+    nb = m.shape[-1]
+    return {
+        "api": "kvq_decode_attn_adaptive (append=True)",
+        "tau_cov": args.tau_cov, "tau_rank": args.tau_rank,
+        "tau_vc": args.tau_vc if np.isfinite(args.tau_vc) else "inf",
+        "ms_per_step": round(ms, 5),
+        "overhead_vs_plain_step": round(ms / ms_plain - 1.0, 4),
+        "kstar_mean_frac": round(float(ks.mean()) / nb, 5),
+        "key_fp16_blocks_frac": round(float((m & 1).mean()), 5),
+        "value_fp16_blocks_frac": round(float(((m >> 1) & 1).mean()), 5),
+        "heads_recomputed_frac": round(float(r.mean()), 5),
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -415,6 +469,8 @@ def main():
     # the certificate needs the matrix-core kernel (group sizes up to 16)
     no_cert = args.no_certify or args.kernel == "valu" or w.G > 16
     certified = None if no_cert else bench_certified(args, w, caches, ws, q, sm, tau_k, tau_v, ms_step)
+    adaptive = None if (no_cert or args.no_adaptive or (w.T + 63) // 64 > 8192) else \
+        bench_adaptive(args, w, caches, q, sm, tau_k, tau_v, ms_step)
 
     if args.calibrate_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -476,6 +532,8 @@ def main():
     }
     if certified is not None:
         line["certified_step"] = certified
+    if adaptive is not None:
+        line["adaptive_step"] = adaptive
     if args.tier2 == "host":
         # bytes each step reads from host memory: fallback tiles and the
         # appended rows (the rest of the step reads tier 1 in HBM)

@@ -111,15 +111,18 @@ __device__ __forceinline__ int half_row(int e, int m) { return 8 * (m >> 2) + 4 
 //   [6400, 6656)  value scales: dword t < 32 = groups (0,1) of token t,
 //                 dword 32 + t = groups (2,3)
 constexpr int ST_K = 0, ST_V = 4096, ST_KS = 6144, ST_VS = 6400, ST_BYTES = 6656;
-// A fallback step (tokens 8j .. 8j+7 of a block, inside half u = j/4 at
-// positions 8(j%4) .. 8(j%4)+7) uses the same stage: a part served from the
-// codes is copied exactly as for half u (only the step's positions are used);
-// a part served from FP16 rows takes
-//   keys   [0, 2048): chunk e (1 KB), lane (s, dg, r) = lane 16s + 4dg + r:
-//          token 4e + r of the step, channels [32dg + 8s, +8);
-//   values [4096, 6144): the step's 8 rows, row-major [8][128];
-// and the copies are padded up to 8 with dwords of the block's statistics
-// into a region the step leaves unused.
+// A fallback step uses the same stage.  Keys alone falling back: tokens
+// 16j .. 16j+15 of the block (half u = j/2, positions 16(j%2) .. +15), with
+//   keys   [0, 4096): chunk c (1 KB), lane (s, dg, r) = lane 16s + 4dg + r:
+//          token 4c + r of the step, channels [32dg + 8s, +8);
+// and the value codes and scales of half u as for a certified half.  Other
+// fallback masks: tokens 8j .. 8j+7 (half u = j/4, positions 8(j%4) .. +7),
+// a part served from the codes copied exactly as for half u (only the step's
+// positions are used), a part served from FP16 rows taking
+//   keys   [0, 2048): chunk e as above, token 4e + r of the step;
+//   values [4096, 6144): the step's 8 rows, row-major [8][128].
+// The copies are padded up to 8 with dwords of the block's statistics into a
+// region the step leaves unused.
 constexpr int FB_K16 = 0, FB_V16 = 4096;
 constexpr int NSTAGE = 3;  // LDS stages per wave
 // With three stages the copies of step k+2 are issued in the middle of step k;
@@ -196,15 +199,32 @@ __device__ __forceinline__ void issue_half(const DecodeArgs &a, int64_t bh, int6
     issue_values(a, bh, blk, row0, u, stage, lane);
 }
 
-// Issues the 8 copies of fallback step j (tokens 8j .. 8j+7) of block `blk`
-// with fallback mask mk (nonzero).  Every source address lies inside the block.
+// Steps of a block by its fallback mask: two certified halves, four 16-token
+// steps of FP16 keys with value codes, or eight 8-token steps otherwise.
+__device__ __forceinline__ int steps_of(uint32_t mk) { return mk == 0u ? 2 : (mk == 1u ? 4 : 8); }
+
+// Issues the 8 copies of fallback step j of block `blk` with fallback mask
+// mk (nonzero): tokens 16j .. 16j+15 when only the keys fall back (FP16 key
+// rows in the four 1 KB chunks: chunk c, lane (r, dg, st) holds token 4c + r,
+// channels 32dg + 8st .. +8; the value codes and scales of half j >> 1),
+// tokens 8j .. 8j+7 otherwise.  Every source address lies inside the block.
 __device__ __forceinline__ void issue_fb(const DecodeArgs &a, int64_t bh, int64_t blk, int j,
                                          uint32_t mk, uint32_t stage, int lane_) {
     const int lane = opaque_lane(lane_);
     const int64_t row0 = bh * a.cap + blk * BLK;  // first token of the block
-    const int64_t rs = row0 + 8 * j;              // first token of the step
-    const int u = j >> 2;
     const float *pad = a.c.k_err + bh * a.nbc + blk;
+    if (mk == 1u) {
+        const int64_t rk = row0 + 16 * j;
+        const int r = lane & 3, dg = (lane >> 2) & 3, st = lane >> 4;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            dma16(stage + FB_K16 + 1024 * c, a.c.k16 + rk * D, (uint32_t)(2 * ((4 * c + r) * D + 32 * dg + 8 * st)));
+        issue_values(a, bh, blk, row0, j >> 1, stage, lane);
+        dma4(stage + ST_KS, pad, 0u);  // padding into the unused key-scale region
+        return;
+    }
+    const int64_t rs = row0 + 8 * j;  // first token of the step
+    const int u = j >> 2;
     if (mk & 1u) {
         const int r = lane & 3, dg = (lane >> 2) & 3, st = lane >> 4;
 #pragma unroll
@@ -221,13 +241,9 @@ __device__ __forceinline__ void issue_fb(const DecodeArgs &a, int64_t bh, int64_
     } else {
         issue_values(a, bh, blk, row0, u, stage, lane);
     }
-    // padding: K16 + value codes (5 copies) -> 3 into the unused key-code
-    // region; K16 + V16 (4) -> 4 there; key codes + V16 (7) -> 1 into the
-    // unused value-scale region
-    if ((mk & 1u) && !(mk & 2u)) {
-#pragma unroll
-        for (int i = 0; i < 3; ++i) dma4(stage + 2048 + 256 * i, pad, 0u);
-    } else if (mk & 1u) {
+    // padding: K16 + V16 (4 copies) -> 4 into the unused key-code region; key
+    // codes + V16 (7) -> 1 into the unused value-scale region
+    if (mk & 1u) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) dma4(stage + 2048 + 256 * i, pad, 0u);
     } else {
@@ -265,14 +281,20 @@ __device__ __forceinline__ void process_step(const uint8_t *stage, uint32_t mk, 
     // ---------------- Q.K^T: S^T[position][head] for the 2 subtiles
     float4_t sc[2];
     if (mk & 1u) {
-        // FP16 key rows: subtile e row r holds token 4e + (r & 3) of the step
-        // (the rows of group p_lo/8 are the step's positions; others masked)
+        // FP16 key rows.  8-token step (both parts FP16): subtile e row r
+        // holds token 4e + (r & 3) of the step (the rows of group p_lo/8 are
+        // the step's positions; others masked).  16-token step (keys only):
+        // row r of subtile e holds token 8((r >> 2) & 1) + 4e + (r & 3), from
+        // chunk 2((r >> 2) & 1) + e, so that result row 4g + i is position
+        // 8g + 4e + i of the half for g = p_lo/8, p_lo/8 + 1.
+        const int hsel = (mk & 2u) ? 0 : ((m >> 2) & 1);
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
             float4_t c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int st = 0; st < 4; ++st)
-                c = mfma(*reinterpret_cast<const uint4 *>(stage + FB_K16 + 1024 * e + 16 * (16 * st + 4 * g4 + (m & 3))),
+                c = mfma(*reinterpret_cast<const uint4 *>(stage + FB_K16 + 1024 * (2 * hsel + e) +
+                                                          16 * (16 * st + 4 * g4 + (m & 3))),
                          qb[st], c);
             sc[e] = c * sml2;
         }
@@ -325,7 +347,11 @@ __device__ __forceinline__ void process_step(const uint8_t *stage, uint32_t mk, 
             for (int i = 0; i < 4; ++i) es += (sc[e][i] == NEG_INF) ? 0.0f : __builtin_amdgcn_exp2f(sc[e][i] - bmax);
         es += __shfl_xor(es, 16);
         es += __shfl_xor(es, 32);
-        if (g4 == 0 && m < g) rank_out[m] = make_float2(bmax, es);
+        if (g4 == 0 && m < g) {
+            rank_out[m] = make_float2(bmax, es);
+            // a 16-token step fills two 8-token statistics slots
+            if (!(mk & 2u)) rank_out[g + m] = make_float2(NEG_INF, 0.0f);
+        }
     }
     const float m_new = fmaxf(w.m_run, bmax);
     // a step with no finite score so far leaves m_new at -inf
@@ -686,14 +712,15 @@ __device__ __forceinline__ void decode_group(const DecodeArgs &a, const int spli
         }
     }
 
-    // Work of (b, kvh) in steps: 2 per certified block (its halves), 8 per
-    // fallback block (its 8-token steps).  Split s takes steps [r0, r1) of the
+    // Work of (b, kvh) in steps: 2 per certified block (its halves), 4 per
+    // block whose keys alone fall back (16-token steps), 8 per other fallback
+    // block (8-token steps).  Split s takes steps [r0, r1) of the
     // sequence in block order, so splits carry equal work however the
     // fallback blocks fall.  Thread t sums the contiguous blocks [t*c, t*c+c).
     const int c = (nb + NT - 1) / NT;
     const int i0 = tid * c < nb ? tid * c : nb, i1 = i0 + c < nb ? i0 + c : nb;
     int mysum = 0;
-    for (int i = i0; i < i1; ++i) mysum += maskb[i] ? 8 : 2;
+    for (int i = i0; i < i1; ++i) mysum += steps_of(maskb[i]);
     int incl = mysum;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -716,7 +743,7 @@ __device__ __forceinline__ void decode_group(const DecodeArgs &a, const int spli
     {
         int p = excl;
         for (int i = i0; i < i1; ++i) {
-            const int w = maskb[i] ? 8 : 2;
+            const int w = steps_of(maskb[i]);
             if (p <= r0 && r0 < p + w) blo_lds = i;
             if (p <= r1 - 1 && r1 - 1 < p + w) ntbl_lds = i;  // last block, made a count below
             p += w;
@@ -729,7 +756,7 @@ __device__ __forceinline__ void decode_group(const DecodeArgs &a, const int spli
         int p = excl;
         for (int i = i0; i < i1; ++i) {
             const uint32_t mk = maskb[i];
-            const int w = mk ? 8 : 2;
+            const int w = steps_of(mk);
             if (p < r1 && p + w > r0) {
                 toff_lds[i - blo] = (int16_t)(p - r0);
                 tmk_lds[i - blo] = (uint8_t)mk;
@@ -837,17 +864,20 @@ __device__ __forceinline__ void decode_group(const DecodeArgs &a, const int spli
         uint32_t mk;
         find(pwin, t, blk, sub, mk);
         uint8_t *stage = &ring[wave][s][0];
-        if (blk == blk_new && (mk ? (p_new >> 3) == sub : (p_new >> 5) == sub))
+        // tokens of the step: 32 (certified half), 16 (keys only) or 8
+        const int step_len = BLK / steps_of(mk);
+        if (blk == blk_new && p_new / step_len == sub)
             patch_new_token(stage, mk, p_new & 31, nk_lds, nv_lds, nks_lds, nvs_lds, lane);
         // positions [p_lo, p_hi) of the half: the valid tokens of the step
-        const int step_len = mk ? 8 : 32;
-        const int p_lo = mk ? 8 * (sub & 3) : 0;
-        const int64_t left = a.length - (blk * BLK + (mk ? 8 * sub : 32 * sub));
+        const int p_lo = (step_len * sub) & 31;
+        const int64_t left = a.length - (blk * BLK + step_len * sub);
         const int nvalid = (int)(left < step_len ? (left > 0 ? left : 0) : step_len);
         if (nvalid > 0)
             process_step<CERT, RANK>(stage, mk, p_lo, p_lo + nvalid, qb, sml2, ws, lane,
                                      CERT ? h2f(teta_lds[blk - blo]) : 0.0f,
-                                     RANK ? a.step_ml + ((bh * a.nbc + blk) * 8 + sub) * g : nullptr, g, mid);
+                                     RANK ? a.step_ml + ((bh * a.nbc + blk) * 8 + sub * (8 / steps_of(mk))) * g
+                                          : nullptr,
+                                     g, mid);
         else
             mid();
         return true;

@@ -16,6 +16,11 @@ Workloads (their shapes follow Llama-3-style GQA decode):
     stress_fallback  B16 Hq32 Hkv8  T8192   10% of 64-token blocks get one K and
                                             one V element scaled x50
     bulk_quantize    B1  Hkv8  1,048,576 new tokens, 3 K outlier channels x20
+    llama3_8b_32k_niah  the llama3_8b_32k shape and structure plus 8 needle
+                     tokens per (batch, KV head) at seeded positions, whose
+                     keys point along the sum of the group's queries with
+                     staggered strengths (a retrieval-shaped attention
+                     pattern standing in for needle-in-a-haystack prompts)
 """
 from dataclasses import dataclass, replace
 
@@ -40,6 +45,8 @@ class Workload:
     spike_block_frac: float = 0.0  # fraction of 64-token blocks with one x`spike` K and V element
     spike_scale: float = 1.0
     fallback_frac: float = 0.0     # target share of blocks falling back, per bound
+    needles: int = 0               # needle tokens per (batch, KV head)
+    needle_dot: float = 0.0        # smallest q_h . k of the strongest needle over the group's heads
 
     @property
     def G(self):
@@ -64,6 +71,9 @@ WORKLOADS = {
                                 spike_scale=50.0, fallback_frac=0.10),
     "bulk_quantize": Workload("bulk_quantize", 1, 8, 8, 1048576, 1005, k_outlier_channels=3,
                               k_outlier_scale=20.0),
+    "llama3_8b_32k_niah": Workload("llama3_8b_32k_niah", 8, 32, 8, 32768, 1006, k_outlier_channels=4,
+                                   k_outlier_scale=15.0, fallback_frac=0.01, needles=8,
+                                   needle_dot=226.0),
 }
 
 
@@ -113,5 +123,20 @@ def make(w: Workload, device="cpu"):
                     t = blocks * BLK + torch.randint(0, BLK, (n,), generator=g, device=device)
                     j = torch.randint(0, D, (n,), generator=g, device=device)
                     dst[b, h, t, j] *= w.spike_scale
+
+    if w.needles:
+        # needle i of a (b, kvh): key along u, the unit sum of the group's
+        # queries, scaled so that its smallest dot product with them is
+        # needle_dot * (1 - i / (4 * needles))
+        G = Hq // Hkv
+        for b in range(B):
+            for h in range(Hkv):
+                qg = q[b, h * G:(h + 1) * G]
+                u = qg.sum(0)
+                u = u / u.norm()
+                dmin = float((qg @ u).min().clamp(min=1e-3))
+                tok = torch.randperm(T, generator=g, device=device)[: w.needles]
+                for i in range(w.needles):
+                    k[b, h, tok[i]] = u * (w.needle_dot * (1 - i / (4 * w.needles)) / dmin)
 
     return dict(q=q.half(), k16=k.half(), v16=v.half())
