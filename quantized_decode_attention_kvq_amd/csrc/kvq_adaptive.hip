@@ -21,9 +21,10 @@
 //   check       over the head's own promoted blocks, the share of pairs the
 //               INT8 and FP16 block log-masses order oppositely; above
 //               tau_rank the head is flagged for the FP16 recompute.
-// The FP16 block log-masses come from the certifying decode, which writes
-// each FP16 key step's per-head largest score and exp2-sum (no second read of
-// the keys).
+// The ranking check itself runs in the certificate merge (kvq_certify.hip),
+// on the FP16 block log-masses from the certifying decode, which writes each
+// FP16 key step's per-head largest score and exp2-sum (no second read of the
+// keys).
 #include "kvq_decode_common.hpp"
 #include "kvq_mfma.hpp"
 
@@ -32,13 +33,8 @@ namespace kvq {
 namespace {
 
 constexpr float NEG_INF = -__builtin_huge_valf();
-constexpr int BPW = 4;  // blocks per wave of the scoring pass
-
-__device__ __forceinline__ int wave_sum_int(int v) {
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o);
-    return v;
-}
+constexpr int BPW = 1;        // blocks per wave of the scoring pass (more waves in flight beat fewer, longer ones)
+constexpr int SEL_REGS = 16;  // masses per lane held in registers by the selection
 
 // Scoring pass.  Grid (ceil(nb / (4 * BPW)), Hkv, B), 4 waves; wave w of
 // workgroup x scores blocks (4x + w) * BPW .. +BPW - 1.  Per 16-token tile,
@@ -120,27 +116,59 @@ __global__ __launch_bounds__(256) void select_kernel(AdaptArgs a) {
     for (int hl = wave; hl < g; hl += 4) {
         const int64_t head = b * a.hq + kvh * g + hl;
         const float *lh = a.lhat + head * a.nbc;
-        float mx = NEG_INF;
-        for (int i = lane; i < nb; i += 64) mx = fmaxf(mx, lh[i]);
-        mx = wave_max(mx);
-        float tot = 0.0f;
-        for (int i = lane; i < nb; i += 64) {
-            const float v = __builtin_amdgcn_exp2f(lh[i] - mx);
-            ms[i] = v;
-            tot += v;
+        const bool in_regs = nb <= 64 * SEL_REGS;
+        // the lane's masses in registers when they fit (every load issued
+        // before the first is used; 0 past nb, never counted as every probe
+        // is above 0), else in LDS
+        float mr[SEL_REGS];
+        float mx = NEG_INF, tot = 0.0f;
+        if (in_regs) {
+#pragma unroll
+            for (int k = 0; k < SEL_REGS; ++k) mr[k] = lane + 64 * k < nb ? lh[lane + 64 * k] : NEG_INF;
+#pragma unroll
+            for (int k = 0; k < SEL_REGS; ++k) mx = fmaxf(mx, mr[k]);
+            mx = wave_total_max(mx);
+#pragma unroll
+            for (int k = 0; k < SEL_REGS; ++k) {
+                mr[k] = mr[k] == NEG_INF ? 0.0f : __builtin_amdgcn_exp2f(mr[k] - mx);
+                tot += mr[k];
+            }
+        } else {
+#pragma unroll 8
+            for (int i = lane; i < nb; i += 64) mx = fmaxf(mx, lh[i]);
+            mx = wave_total_max(mx);
+#pragma unroll 8
+            for (int i = lane; i < nb; i += 64) {
+                const float v = __builtin_amdgcn_exp2f(lh[i] - mx);
+                ms[i] = v;
+                tot += v;
+            }
         }
-        tot = wave_sum(tot);
+        tot = wave_total_sum(tot);
         const float target = a.tau_cov * tot;
         const bool none = !(a.tau_cov > 0.0f);
         const bool all = !none && !(target <= tot);  // out of reach (or NaN): every block
         uint32_t lo = 0u, hi = 0x7F800000u;            // F(lo) >= target > F(hi)
-        if (!none && !all) {
+        if (!none && !all && in_regs) {
             while (hi - lo > 1u) {
                 const uint32_t mid = lo + (hi - lo) / 2u;
                 float f = 0.0f;
+#pragma unroll
+                for (int k = 0; k < SEL_REGS; ++k) f += __float_as_uint(mr[k]) >= mid ? mr[k] : 0.0f;
+                f = wave_total_sum(f);
+                if (f >= target)
+                    lo = mid;
+                else
+                    hi = mid;
+            }
+        } else if (!none && !all) {
+            while (hi - lo > 1u) {
+                const uint32_t mid = lo + (hi - lo) / 2u;
+                float f = 0.0f;
+#pragma unroll 8
                 for (int i = lane; i < nb; i += 64)
                     if (__float_as_uint(ms[i]) >= mid) f += ms[i];
-                f = wave_sum(f);
+                f = wave_total_sum(f);
                 if (f >= target)
                     lo = mid;
                 else
@@ -148,95 +176,30 @@ __global__ __launch_bounds__(256) void select_kernel(AdaptArgs a) {
             }
         }
         int cnt = 0;
-        for (int i = lane; i < nb; i += 64) {
-            const bool pk = !none && (all || __float_as_uint(ms[i]) >= lo);
-            const bool pv = (ms[i] / tot) * a.c.v_err[bh * a.nbc + i] > a.tau_vc;
+        auto mark = [&](int i, float mi, float ve) {
+            const bool pk = !none && (all || __float_as_uint(mi) >= lo);
+            const bool pv = (mi / tot) * ve > a.tau_vc;
             a.phead[head * a.nbc + i] = pk ? 1 : 0;
             cnt += pk ? 1 : 0;
             const uint32_t bits = (pk ? 1u : 0u) | (pv ? 2u : 0u);
             if (bits) atomicOr(&uni[i >> 2], bits << (8 * (i & 3)));
+        };
+        if (in_regs) {
+            float ve[SEL_REGS];
+#pragma unroll
+            for (int k = 0; k < SEL_REGS; ++k) ve[k] = lane + 64 * k < nb ? a.c.v_err[bh * a.nbc + lane + 64 * k] : 0.0f;
+#pragma unroll
+            for (int k = 0; k < SEL_REGS; ++k)
+                if (lane + 64 * k < nb) mark(lane + 64 * k, mr[k], ve[k]);
+        } else {
+#pragma unroll 8
+            for (int i = lane; i < nb; i += 64) mark(i, ms[i], a.c.v_err[bh * a.nbc + i]);
         }
-        cnt = wave_sum_int(cnt);
+        cnt = wave_total_sum_int(cnt);
         if (lane == 0 && a.kstar) a.kstar[head] = cnt;
     }
     __syncthreads();
     for (int i = threadIdx.x; i < nb; i += 256) a.promote[bh * a.nbc + i] = (uint8_t)(uni[i >> 2] >> (8 * (i & 3)));
-}
-
-// FP16 block log-mass (log2 units) of block i for head hl of (b, kvh), from
-// the decode's per-step statistics of the block's valid 8-token steps.
-__device__ float fp16_block_logmass(const AdaptArgs &a, int64_t bh, int64_t i, int hl) {
-    const int64_t left = a.length - i * BLK;
-    const int nst = left >= BLK ? 8 : (int)((left + 7) / 8);
-    const float2 *st = a.step_ml + (bh * a.nbc + i) * 8 * a.g + hl;
-    float L[8], M = NEG_INF;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        L[k] = NEG_INF;
-        if (k < nst) {
-            const float2 p = st[k * a.g];
-            if (p.y > 0.0f) L[k] = p.x + __log2f(p.y);
-        }
-        M = fmaxf(M, L[k]);
-    }
-    if (M == NEG_INF) return NEG_INF;
-    float s = 0.0f;
-#pragma unroll
-    for (int k = 0; k < 8; ++k)
-        if (L[k] != NEG_INF) s += __builtin_amdgcn_exp2f(L[k] - M);
-    return M + __log2f(s);
-}
-
-// Ranking check.  Grid (Hq, B), 4 waves: the head's promoted blocks are
-// compacted into LDS (INT8 and FP16 log-masses), then every pair is compared.
-__global__ __launch_bounds__(256) void check_kernel(AdaptArgs a) {
-    __shared__ float pa[ADAPT_MAX_NB], pf[ADAPT_MAX_NB];
-    __shared__ int wcnt[4];
-    __shared__ unsigned wred[4];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t h = blockIdx.x, b = blockIdx.y;
-    const int g = a.g;
-    const int64_t kvh = h / g, hl = h % g;
-    const int64_t bh = b * a.hkv + kvh, head = b * a.hq + h;
-    const uint8_t *ph = a.phead + head * a.nbc;
-    const float *lh = a.lhat + head * a.nbc;
-    int n = 0;
-    for (int64_t c0 = 0; c0 < a.nb; c0 += 256) {
-        const int64_t i = c0 + tid;
-        const bool f = i < a.nb && ph[i] != 0;
-        const uint64_t bal = __ballot(f);
-        if (lane == 0) wcnt[wave] = __popcll(bal);
-        __syncthreads();
-        int before = 0, tot = 0;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const int v = wcnt[w];
-            before += w < wave ? v : 0;
-            tot += v;
-        }
-        if (f) {
-            const int pos = n + before + __popcll(bal & ((1ull << lane) - 1ull));
-            pa[pos] = lh[i];
-            pf[pos] = fp16_block_logmass(a, bh, i, (int)hl);
-        }
-        n += tot;
-        __syncthreads();
-    }
-    unsigned cnt = 0u;
-    for (int i = tid; i < n; i += 256) {
-        const float ai = pa[i], fi = pf[i];
-        for (int j = i + 1; j < n; ++j) cnt += ((ai - pa[j]) * (fi - pf[j]) < 0.0f) ? 1u : 0u;
-    }
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) cnt += (unsigned)__shfl_xor((int)cnt, o);
-    if (lane == 0) wred[wave] = cnt;
-    __syncthreads();
-    if (tid == 0) {
-        const unsigned nd = wred[0] + wred[1] + wred[2] + wred[3];
-        const double np = (double)n * (double)(n - 1) / 2.0;
-        if (a.ndisc) a.ndisc[head] = (int32_t)nd;
-        if (np > 0.0 && (double)nd > (double)a.tau_rank * np) a.flags[head] = 1;
-    }
 }
 
 }  // namespace
@@ -249,11 +212,6 @@ hipError_t launch_score(const AdaptArgs &a, int batch, hipStream_t s) {
 
 hipError_t launch_select(const AdaptArgs &a, int batch, hipStream_t s) {
     hipLaunchKernelGGL(select_kernel, dim3((unsigned)a.hkv, (unsigned)batch), dim3(256), 0, s, a);
-    return hipGetLastError();
-}
-
-hipError_t launch_check(const AdaptArgs &a, int batch, hipStream_t s) {
-    hipLaunchKernelGGL(check_kernel, dim3((unsigned)a.hq, (unsigned)batch), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

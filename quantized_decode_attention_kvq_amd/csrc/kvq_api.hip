@@ -376,6 +376,10 @@ kvq_status decode_impl(kvq_cache *c, const uint16_t *q, int32_t q_heads, float s
     a.gate = nullptr;
     a.promote = nullptr;
     a.step_ml = nullptr;
+    a.phead = nullptr;
+    a.lhat = nullptr;
+    a.ndisc = nullptr;
+    a.tau_rank = 1.0f;
 
     hipError_t e = hipSuccess;
     kvq::AdaptArgs aa;
@@ -389,9 +393,6 @@ kvq_status decode_impl(kvq_cache *c, const uint16_t *q, int32_t q_heads, float s
         aa.phead = reinterpret_cast<uint8_t *>((char *)workspace + al.phead);
         aa.promote = reinterpret_cast<uint8_t *>((char *)workspace + al.promote);
         aa.kstar = ad->kstar;
-        aa.step_ml = reinterpret_cast<float2 *>((char *)workspace + al.step);
-        aa.flags = a.flags;
-        aa.ndisc = ad->ndisc;
         aa.cap = c->capacity;
         aa.length = length;
         aa.nbc = nbc;
@@ -402,11 +403,14 @@ kvq_status decode_impl(kvq_cache *c, const uint16_t *q, int32_t q_heads, float s
         aa.sm = sm_scale;
         aa.tau_cov = ad->tau_cov;
         aa.tau_vc = ad->tau_vc;
-        aa.tau_rank = ad->tau_rank;
         if (nb > 0) e = kvq::launch_score(aa, c->batch, (hipStream_t)stream);
         if (e == hipSuccess) e = kvq::launch_select(aa, c->batch, (hipStream_t)stream);
         a.promote = aa.promote;
-        a.step_ml = const_cast<float2 *>(aa.step_ml);
+        a.step_ml = reinterpret_cast<float2 *>((char *)workspace + al.step);
+        a.phead = aa.phead;
+        a.lhat = aa.lhat;
+        a.ndisc = ad->ndisc;
+        a.tau_rank = ad->tau_rank;
     }
     if (e == hipSuccess)
         e = mf ? kvq::launch_decode_mfma(a, c->batch, (hipStream_t)stream)
@@ -414,9 +418,6 @@ kvq_status decode_impl(kvq_cache *c, const uint16_t *q, int32_t q_heads, float s
     if (e == hipSuccess && split_done) e = hipEventRecord((hipEvent_t)split_done, (hipStream_t)stream);
     if (e == hipSuccess) e = certify ? kvq::launch_merge_cert(a, c->batch, (hipStream_t)stream)
                                      : kvq::launch_merge(a, c->batch, (hipStream_t)stream);
-    // the ranking check flags inconsistent heads for rung 3 (after the
-    // certificate's flags are written)
-    if (e == hipSuccess && ad) e = kvq::launch_check(aa, c->batch, (hipStream_t)stream);
     const bool rung3 = certify && (tau_out != __builtin_huge_valf() || (ad && ad->tau_rank < 1.0f));
     if (e == hipSuccess && rung3) {
         // rung 3: the groups holding a flagged head run again with every

@@ -26,13 +26,141 @@ namespace kvq {
 
 namespace {
 
+// FP16 block log-mass (log2 units) of block i < nb for head hl of group bh,
+// from the decode's statistics of the block's valid 8-token slots (a
+// 16-token step fills its first slot and empties the second).  The loads
+// are unconditional (slots past the valid ones re-read the last valid one)
+// so that they issue together.
+__device__ __forceinline__ float fp16_block_logmass(const DecodeArgs &a, int64_t bh, int64_t i, int hl) {
+    constexpr float NEG_INF = -__builtin_huge_valf();
+    const int64_t left = a.length - i * BLK;
+    const int nst = left >= BLK ? 8 : (int)((left + 7) / 8);
+    const float2 *st = a.step_ml + (bh * a.nbc + i) * 8 * a.g + hl;
+    float2 p[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) p[k] = st[(k < nst ? k : nst - 1) * a.g];
+    float L[8], M = NEG_INF;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        L[k] = (k < nst && p[k].y > 0.0f) ? p[k].x + __log2f(p[k].y) : NEG_INF;
+        M = fmaxf(M, L[k]);
+    }
+    if (M == NEG_INF) return NEG_INF;
+    float s = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+        if (L[k] != NEG_INF) s += __builtin_amdgcn_exp2f(L[k] - M);
+    return M + __log2f(s);
+}
+
+// Ranking-consistency check of one head (Methodology 3): its promoted blocks
+// are compacted into LDS with their INT8 and FP16 log-masses, every pair is
+// compared, and the head is inconsistent when the pairs ordered oppositely
+// exceed tau_rank of all pairs.  All 256 threads take part; every thread
+// returns the result.
+__device__ bool ranking_inconsistent(const DecodeArgs &a, int64_t bh, int64_t head, int hl, float *pa, float *pf,
+                                     int *wcnt, int *bcast) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (a.nb == 0) {  // uniform: no barrier is skipped by part of the workgroup
+        if (tid == 0 && a.ndisc) a.ndisc[head] = 0;
+        return false;
+    }
+    const uint8_t *ph = a.phead + head * a.nbc;
+    const float *lh = a.lhat + head * a.nbc;
+    // thread t takes blocks [t*K, t*K + K): count its promoted blocks, scan
+    // the counts over the workgroup, then write the entries (pair order is
+    // irrelevant to the count)
+    const int nb = (int)a.nb, K = (nb + 255) / 256;
+    const int i0 = tid * K < nb ? tid * K : nb, i1 = i0 + K < nb ? i0 + K : nb;
+    // up to KR blocks per thread: every load issued at once (the log-masses
+    // of blocks that turn out not promoted are simply unused)
+    constexpr int KR = 4;
+    bool fr[KR];
+    float ar[KR], fpr[KR];
+    int mine = 0;
+    if (K <= KR) {
+#pragma unroll
+        for (int k = 0; k < KR; ++k) {
+            // unconditional loads at a clamped, in-range block
+            const int i = i0 + k < nb ? i0 + k : nb - 1;
+            fr[k] = i0 + k < i1 && ph[i] != 0;
+            ar[k] = lh[i];
+            fpr[k] = fp16_block_logmass(a, bh, i, hl);
+        }
+#pragma unroll
+        for (int k = 0; k < KR; ++k) mine += fr[k] ? 1 : 0;
+    } else {
+        for (int i = i0; i < i1; ++i) mine += ph[i] != 0;
+    }
+    const int incl = wave_incl_scan_int(mine);
+    if (lane == 63) wcnt[wave] = incl;
+    __syncthreads();
+    int pos = incl - mine, n = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        pos += w < wave ? wcnt[w] : 0;
+        n += wcnt[w];
+    }
+    if (K <= KR) {
+#pragma unroll
+        for (int k = 0; k < KR; ++k)
+            if (fr[k]) {
+                pa[pos] = ar[k];
+                pf[pos] = fpr[k];
+                ++pos;
+            }
+    } else {
+        for (int i = i0; i < i1; ++i)
+            if (ph[i] != 0) {
+                pa[pos] = lh[i];
+                pf[pos] = fp16_block_logmass(a, bh, i, hl);
+                ++pos;
+            }
+    }
+    __syncthreads();
+    int cnt = 0;
+    for (int i = tid; i < n; i += 256) {
+        const float ai = pa[i], fi = pf[i];
+        int j = i + 1;
+        for (; j + 8 <= n; j += 8) {
+            float aj[8], fj[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                aj[u] = pa[j + u];
+                fj[u] = pf[j + u];
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) cnt += ((ai - aj[u]) * (fi - fj[u]) < 0.0f) ? 1 : 0;
+        }
+        for (; j < n; ++j) cnt += ((ai - pa[j]) * (fi - pf[j]) < 0.0f) ? 1 : 0;
+    }
+    cnt = wave_total_sum_int(cnt);
+    __syncthreads();  // every thread has read wcnt
+    if (lane == 0) wcnt[wave] = cnt;
+    __syncthreads();
+    if (tid == 0) {
+        const int nd = wcnt[0] + wcnt[1] + wcnt[2] + wcnt[3];
+        const double np = (double)n * (double)(n - 1) / 2.0;
+        if (a.ndisc) a.ndisc[head] = nd;
+        *bcast = np > 0.0 && (double)nd > (double)a.tau_rank * np ? 1 : 0;
+    }
+    __syncthreads();
+    return *bcast != 0;
+}
+
 // One workgroup per query head h of (b, kvh).  The output merge is the
 // split merge's (every wave forms M and L; wave w sums the splits w, w + 4,
 // ..., lane l holds channels 2l and 2l + 1); wave 1 then gathers the
-// certificate's parts of the splits (two per lane, summed in double).
+// certificate's parts of the splits (two per lane, summed in double).  RANK
+// (adaptive decode): the head's ranking check runs first, and an
+// inconsistent head is flagged for the recompute like one whose certificate
+// exceeds tau_out.
+template <bool RANK>
 __global__ __launch_bounds__(256) void merge_cert_kernel(DecodeArgs a) {
     __shared__ float2 red[4][64];
     __shared__ float qn_lds;
+    __shared__ float pa[RANK ? ADAPT_MAX_NB : 1], pf[RANK ? ADAPT_MAX_NB : 1];
+    __shared__ int wcnt[4], bcast;
     const int h = blockIdx.x;
     const int64_t kvh = blockIdx.y, b = blockIdx.z;
     const int64_t bh = b * a.hkv + kvh;
@@ -71,6 +199,7 @@ __global__ __launch_bounds__(256) void merge_cert_kernel(DecodeArgs a) {
     }
     red[wave][lane] = acc;
     __syncthreads();
+    const bool inconsistent = RANK && ranking_inconsistent(a, bh, head, h, pa, pf, wcnt, &bcast);
     if (wave == 0) {
         float2 o = red[0][lane];
 #pragma unroll
@@ -117,7 +246,7 @@ __global__ __launch_bounds__(256) void merge_cert_kernel(DecodeArgs a) {
             float cf = (float)c;
             if ((double)cf < c) cf = __uint_as_float(__float_as_uint(cf) + 1u);  // c >= 0: the next float up
             a.cert[head] = cf;
-            a.flags[head] = cf > a.tau_out ? 1 : 0;
+            a.flags[head] = (cf > a.tau_out || inconsistent) ? 1 : 0;
         }
     }
 }
@@ -125,7 +254,11 @@ __global__ __launch_bounds__(256) void merge_cert_kernel(DecodeArgs a) {
 }  // namespace
 
 hipError_t launch_merge_cert(const DecodeArgs &a, int batch, hipStream_t s) {
-    hipLaunchKernelGGL(merge_cert_kernel, dim3((unsigned)a.g, (unsigned)a.hkv, (unsigned)batch), dim3(256), 0, s, a);
+    const dim3 grid((unsigned)a.g, (unsigned)a.hkv, (unsigned)batch);
+    if (a.step_ml)
+        hipLaunchKernelGGL(merge_cert_kernel<true>, grid, dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL(merge_cert_kernel<false>, grid, dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

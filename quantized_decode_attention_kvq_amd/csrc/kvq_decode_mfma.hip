@@ -97,6 +97,14 @@ __device__ __forceinline__ float max_across_rows(float v) {
     return fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
 }
 
+// Sum over the four 16-lane rows, with the same row-swap permutes.
+__device__ __forceinline__ float sum_across_rows(float v) {
+    const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+    const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
+}
+
 // Row (token) of the half held by MFMA row m of Q.K^T subtile e.
 __device__ __forceinline__ int half_row(int e, int m) { return 8 * (m >> 2) + 4 * e + (m & 3); }
 
@@ -345,8 +353,7 @@ __device__ __forceinline__ void process_step(const uint8_t *stage, uint32_t mk, 
         for (int e = 0; e < 2; ++e)
 #pragma unroll
             for (int i = 0; i < 4; ++i) es += (sc[e][i] == NEG_INF) ? 0.0f : __builtin_amdgcn_exp2f(sc[e][i] - bmax);
-        es += __shfl_xor(es, 16);
-        es += __shfl_xor(es, 32);
+        es = sum_across_rows(es);
         if (g4 == 0 && m < g) {
             rank_out[m] = make_float2(bmax, es);
             // a 16-token step fills two 8-token statistics slots

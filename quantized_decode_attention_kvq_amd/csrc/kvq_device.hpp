@@ -64,6 +64,49 @@ __device__ __forceinline__ float qnorm16(const uint4 raw) {
     return (float)__dsqrt_rn(tree128(sq));
 }
 
+// Wave-wide totals in every lane, on DPP moves (no LDS round trip): inclusive
+// scans inside each 16-lane row (row shifts by 1, 2, 4, 8; lanes shifted in
+// from outside the row read the identity), then the row totals carried up by
+// the broadcasts of lane 15 (into rows 1 and 3) and lane 31 (into rows 2 and
+// 3); lane 63 ends with the total, read back as a wave-uniform value.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_from(int identity, int v) {
+    return __builtin_amdgcn_update_dpp(identity, v, CTRL, ROWS, 0xF, false);
+}
+__device__ __forceinline__ float wave_total_sum(float v) {
+    constexpr int Z = 0;  // bits of 0.0f
+    v += __int_as_float(dpp_from<0x111, 0xF>(Z, __float_as_int(v)));
+    v += __int_as_float(dpp_from<0x112, 0xF>(Z, __float_as_int(v)));
+    v += __int_as_float(dpp_from<0x114, 0xF>(Z, __float_as_int(v)));
+    v += __int_as_float(dpp_from<0x118, 0xF>(Z, __float_as_int(v)));
+    v += __int_as_float(dpp_from<0x142, 0xA>(Z, __float_as_int(v)));
+    v += __int_as_float(dpp_from<0x143, 0xC>(Z, __float_as_int(v)));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+__device__ __forceinline__ float wave_total_max(float v) {
+    constexpr int NI = (int)0xFF800000u;  // bits of -inf
+    v = fmaxf(v, __int_as_float(dpp_from<0x111, 0xF>(NI, __float_as_int(v))));
+    v = fmaxf(v, __int_as_float(dpp_from<0x112, 0xF>(NI, __float_as_int(v))));
+    v = fmaxf(v, __int_as_float(dpp_from<0x114, 0xF>(NI, __float_as_int(v))));
+    v = fmaxf(v, __int_as_float(dpp_from<0x118, 0xF>(NI, __float_as_int(v))));
+    v = fmaxf(v, __int_as_float(dpp_from<0x142, 0xA>(NI, __float_as_int(v))));
+    v = fmaxf(v, __int_as_float(dpp_from<0x143, 0xC>(NI, __float_as_int(v))));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+// Inclusive prefix sum over the lanes (the same moves), per lane.
+__device__ __forceinline__ int wave_incl_scan_int(int v) {
+    v += dpp_from<0x111, 0xF>(0, v);
+    v += dpp_from<0x112, 0xF>(0, v);
+    v += dpp_from<0x114, 0xF>(0, v);
+    v += dpp_from<0x118, 0xF>(0, v);
+    v += dpp_from<0x142, 0xA>(0, v);
+    v += dpp_from<0x143, 0xC>(0, v);
+    return v;
+}
+__device__ __forceinline__ int wave_total_sum_int(int v) {
+    return __builtin_amdgcn_readlane(wave_incl_scan_int(v), 63);
+}
+
 // Max of two non-negative-or-NaN floats that keeps NaN (as an unsigned
 // compare of the bit patterns, NaN > +Inf > finite >= 0).
 __device__ __forceinline__ float max_keep_nan(float a, float b) {

@@ -66,9 +66,16 @@ struct DecodeArgs {
     // adaptive precision (null otherwise): promoted tiles per (b, kvh,
     // block) [B*Hkv][nbc] (bit 0 key, bit 1 value), OR-ed into the bound
     // masks; with the certificate, per FP16 key step its per-head largest
-    // score and exp2-sum, [B*Hkv][nbc][8][G] (log2 units)
+    // score and exp2-sum, [B*Hkv][nbc][8][G] (log2 units), and for the
+    // ranking check in the certificate merge each head's own key promotions
+    // [B][Hq][nbc], its INT8 block log-masses [B][Hq][nbc], the discordant
+    // pair counts [B][Hq] (or null) and tau_rank
     const uint8_t *promote;
     float2 *step_ml;
+    const uint8_t *phead;
+    const float *lhat;
+    int32_t *ndisc;
+    float tau_rank;
 };
 
 // Adaptive precision (scoring pass, top-K* selection, ranking check).
@@ -79,12 +86,9 @@ struct AdaptArgs {
     uint8_t *phead;          // [B][Hq][nbc] 1: the head promotes the block's keys
     uint8_t *promote;        // [B][Hkv][nbc] bit 0 key, bit 1 value promotion (union over the group)
     int32_t *kstar;          // [B][Hq] blocks each head promotes, or null
-    const float2 *step_ml;   // [B*Hkv][nbc][8][G] FP16 step statistics from the decode
-    uint8_t *flags;          // [B][Hq] recompute flags, set for inconsistent rankings
-    int32_t *ndisc;          // [B][Hq] discordant pairs, or null
     int64_t cap, length, nbc, nb;
     int32_t hkv, hq, g;
-    float sm, tau_cov, tau_vc, tau_rank;
+    float sm, tau_cov, tau_vc;
 };
 
 // Upper limits that size the workspace and LDS tables.
@@ -106,10 +110,9 @@ hipError_t launch_merge(const DecodeArgs &a, int batch, hipStream_t s);
 hipError_t launch_merge_cert(const DecodeArgs &a, int batch, hipStream_t s);
 bool mfma_supports(int g);
 
-// adaptive precision: INT8 scoring pass (a.nb > 0), selection and the
-// ranking check
+// adaptive precision: INT8 scoring pass (a.nb > 0) and selection (the
+// ranking check runs in the certificate merge when a.step_ml is set)
 hipError_t launch_score(const AdaptArgs &a, int batch, hipStream_t s);
 hipError_t launch_select(const AdaptArgs &a, int batch, hipStream_t s);
-hipError_t launch_check(const AdaptArgs &a, int batch, hipStream_t s);
 
 }  // namespace kvq

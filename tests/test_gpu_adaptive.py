@@ -177,3 +177,4 @@ def test_empty_cache():
     torch.cuda.synchronize()
     assert not g["out"].float().cpu().numpy().any()
     assert not g["kstar"].cpu().numpy().any() and not g["recomputed"].cpu().numpy().any()
+    assert not g["ndisc"].cpu().numpy().any()
