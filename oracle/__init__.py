@@ -53,18 +53,20 @@ def lib():
         L.kvqo_quant_k_row.restype = None
         L.kvqo_quant_v_row.argtypes = [P, P, P, P]
         L.kvqo_quant_v_row.restype = None
-        L.kvqo_quantize_cache.argtypes = [i32, i32, i64, i64, P, P, P, P, P, P, P, P]
+        L.kvqo_quantize_cache.argtypes = [i32, i32, i64, i64, P, P, P, P, P, P, P, P, i32]
         L.kvqo_quantize_cache.restype = None
         L.kvqo_bounds.argtypes = [i32, i32, i32, i64, i64, P, f32, f32, f32, P, P, P, P, P]
         L.kvqo_bounds.restype = None
         L.kvqo_attention.argtypes = [i32, i32, i32, i64, i64, P, f32, f32, f32,
-                                     P, P, P, P, P, P, P, P, P, P]
+                                     P, P, P, P, P, P, P, P, P, P, i32]
         L.kvqo_attention.restype = None
         L.kvqo_certificate.argtypes = [i32, i32, i32, i64, i64, P, f32, f32, f32, ctypes.c_double,
-                                       P, P, P, P, P, P, P, P, P, P, P, P, P]
+                                       P, P, P, P, P, P, P, P, P, P, P, P, P, i32]
         L.kvqo_certificate.restype = None
         dbl = ctypes.c_double
-        L.kvqo_adaptive.argtypes = [i32, i32, i32, i64, i64, P, f32, f32, f32, dbl, dbl, dbl, dbl] + [P] * 20
+        L.kvqo_adaptive.argtypes = [i32, i32, i32, i64, i64, P, f32, f32, f32, dbl, dbl, dbl, dbl] + [P] * 20 + [i32]
+        L.kvqo_quant_k_row_rot.argtypes = [P, P, P, P]
+        L.kvqo_quant_k_row_rot.restype = None
         L.kvqo_adaptive.restype = None
         _lib = L
     return _lib
@@ -139,14 +141,17 @@ def quant_v_row(x):
 # ----------------------------------------------------------------- cache
 
 class Cache:
-    """The oracle's own quantized cache (tier 1) for fp16 tier-2 arrays."""
+    """The oracle's own quantized cache (tier 1) for fp16 tier-2 arrays.
+    key_rotation: the keys are quantized after the Hadamard rotation
+    (kvqo_quant_k_row_rot) and read back through its inverse."""
 
-    def __init__(self, k16, v16, length):
+    def __init__(self, k16, v16, length, key_rotation=False):
         k16 = _c(k16, np.float16)
         v16 = _c(v16, np.float16)
         B, Hkv, cap, d = k16.shape
         assert d == D and cap % BLK == 0 and v16.shape == k16.shape and 0 <= length <= cap
         self.B, self.Hkv, self.cap, self.length = B, Hkv, cap, int(length)
+        self.key_rotation = bool(key_rotation)
         self.k16, self.v16 = k16, v16
         nb = cap // BLK
         self.k_codes = np.zeros((B, Hkv, cap, D), np.int8)
@@ -157,7 +162,7 @@ class Cache:
         self.v_err = np.zeros((B, Hkv, nb), np.float32)
         lib().kvqo_quantize_cache(B, Hkv, cap, self.length, _p(k16), _p(v16), _p(self.k_codes),
                                   _p(self.k_scales), _p(self.v_codes), _p(self.v_scales),
-                                  _p(self.k_err), _p(self.v_err))
+                                  _p(self.k_err), _p(self.v_err), int(self.key_rotation))
 
     @property
     def nblocks(self):
@@ -195,7 +200,7 @@ class Cache:
         lib().kvqo_attention(B, Hq, self.Hkv, self.cap, self.length, _p(q), sm, tau_k, tau_v,
                              _p(self.k16), _p(self.v16), _p(self.k_codes), _p(self.k_scales),
                              _p(self.v_codes), _p(self.v_scales), _p(self.k_err), _p(self.v_err),
-                             _p(out), _p(mask))
+                             _p(out), _p(mask), int(self.key_rotation))
         return out, mask[:, :, : self.nblocks]
 
 
@@ -213,7 +218,7 @@ class Cache:
                                float(tau_out), _p(self.k16), _p(self.v16), _p(self.k_codes),
                                _p(self.k_scales), _p(self.v_codes), _p(self.v_scales), _p(self.k_err),
                                _p(self.v_err), _p(r["out"]), _p(r["cert"]), _p(r["e_key"]),
-                               _p(r["e_val"]), _p(r["recomputed"]))
+                               _p(r["e_val"]), _p(r["recomputed"]), int(self.key_rotation))
         return r
 
 
@@ -243,7 +248,8 @@ class Cache:
                             _p(self.k_codes), _p(self.k_scales), _p(self.v_codes), _p(self.v_scales),
                             _p(self.k_err), _p(self.v_err), _p(r["out"]), _p(r["cert"]), _p(r["e_key"]),
                             _p(r["e_val"]), _p(r["recomputed"]), _p(r["masks"]), _p(r["lhat"]), _p(r["lfp"]),
-                            _p(r["kstar"]), _p(r["ndisc"]), _p(r["npairs"]), _p(r["inconsistent"]))
+                            _p(r["kstar"]), _p(r["ndisc"]), _p(r["npairs"]), _p(r["inconsistent"]),
+                            int(self.key_rotation))
         for k in ("masks", "lhat", "lfp"):
             r[k] = r[k][..., :nb]
         return r

@@ -199,6 +199,86 @@ void kvqo_quant_k_row(const uint16_t *x16, int8_t *codes, uint16_t *scale, float
     *err = (float)sqrt(kvqo_tree128(sq));
 }
 
+/* Walsh-Hadamard transform of 128 values in place, Sylvester order:
+ * out_j = sum_i (-1)^popcount(i & j) in_i, by butterflies at strides 1 .. 64.
+ * Exact in fp64 for the rows below (every partial sum fits the significand),
+ * so the order of the butterflies does not matter. */
+static void wht128(double *x)
+{
+    for (int h = 1; h < D; h <<= 1)
+        for (int i = 0; i < D; i += 2 * h)
+            for (int j = i; j < i + h; ++j) {
+                double a = x[j], b = x[j + h];
+                x[j] = a + b;
+                x[j + h] = a - b;
+            }
+}
+
+/* Quantize one key row with the Hadamard rotation (outlier-aware codec: the
+ * Walsh-Hadamard transform applied before scalar quantization in the KQV
+ * scheme of "Statistical Inference and Quality Measures of KV Cache
+ * Quantisations Inspired by TurboQuant", technical summary, quantisation
+ * schemes, whose results credit it with robustness to heavy tails; read here
+ * as a rotation of the keys alone, the values keeping their codec).  u = H k / 16 (exact in fp64: k's
+ * values are multiples of 2^-24 below 2^16, so the sums fit 47 bits); the
+ * key codec on u: s = f16(f32(max|u|) / 127), c = clamp(RNE(u / s), -127,
+ * 127) with the quotient in fp64 (u is a multiple of 2^-28, so a quotient
+ * that is not a half-integer lies at least 2^-43 from one, well beyond its
+ * fp64 rounding); e = u - s c (exact).  The decode's key is k~ = H (s c) / 8,
+ * so ||k - k~|| = sqrt(128) ||e|| / 8 = sqrt(2) ||e||, and the row's error is
+ * f32(sqrt(2 * T128(e^2))). */
+void kvqo_quant_k_row_rot(const uint16_t *x16, int8_t *codes, uint16_t *scale, float *err)
+{
+    double u[D];
+    int finite = 1;
+    for (int j = 0; j < D; ++j) {
+        u[j] = kvqo_f16_to_f64(x16[j]);
+        if (!isfinite(u[j]))
+            finite = 0;
+    }
+    if (!finite) {
+        memset(codes, 0, D);
+        *scale = 0;
+        *err = INFINITY;
+        return;
+    }
+    wht128(u);
+    double a = 0.0;
+    for (int j = 0; j < D; ++j) {
+        u[j] /= 16.0;
+        if (fabs(u[j]) > a)
+            a = fabs(u[j]);
+    }
+    uint16_t sh = kvqo_f32_to_f16((float)a / 127.0f);
+    double s = kvqo_f16_to_f64(sh);
+    double sq[D];
+    for (int j = 0; j < D; ++j) {
+        int c = (s == 0.0) ? 0 : clampi((int)rint(u[j] / s), -127, 127);
+        double e = u[j] - s * (double)c;
+        codes[j] = (int8_t)c;
+        sq[j] = e * e;
+    }
+    *scale = sh;
+    *err = (float)sqrt(2.0 * kvqo_tree128(sq));
+}
+
+/* The key the decode uses for a row of codes: s c, or with the rotation
+ * H (s c) / 8 = s (H c) / 8 (H c is an integer below 2^14: exact). */
+static void dequant_key_row(const int8_t *codes, uint16_t scale, int key_rot, double *out)
+{
+    double s = kvqo_f16_to_f64(scale);
+    if (!key_rot) {
+        for (int j = 0; j < D; ++j)
+            out[j] = s * (double)codes[j];
+        return;
+    }
+    for (int j = 0; j < D; ++j)
+        out[j] = (double)codes[j];
+    wht128(out);
+    for (int j = 0; j < D; ++j)
+        out[j] = s * out[j] / 8.0;
+}
+
 /* Quantize one value row: 4 groups of 32 channels.  Writes 128 int4 codes as
  * ints in [-7, 7], 4 scales, and returns the row's max |v - v^|. */
 void kvqo_quant_v_row(const uint16_t *x16, int8_t *codes, uint16_t *scales, float *err)
@@ -262,7 +342,7 @@ static size_t v_byte(int b, int h, int64_t t, int j, int Hkv, int64_t cap, int *
  * defined; other blocks are left untouched. */
 void kvqo_quantize_cache(int B, int Hkv, int64_t cap, int64_t length, const uint16_t *k16,
                          const uint16_t *v16, int8_t *k_codes, uint16_t *k_scales, uint8_t *v_codes,
-                         uint16_t *v_scales, float *k_err, float *v_err)
+                         uint16_t *v_scales, float *k_err, float *v_err, int key_rot)
 {
     int64_t nblk = (length + BLK - 1) / BLK;
 #pragma omp parallel for collapse(3) schedule(dynamic)
@@ -276,7 +356,10 @@ void kvqo_quantize_cache(int B, int Hkv, int64_t cap, int64_t length, const uint
                 for (int64_t t = blk * BLK; t < length && t < (blk + 1) * BLK; ++t) {
                     size_t r = row_index(b, h, t, Hkv, cap);
                     float ke, ve;
-                    kvqo_quant_k_row(k16 + r * D, k_codes + r * D, k_scales + r, &ke);
+                    if (key_rot)
+                        kvqo_quant_k_row_rot(k16 + r * D, k_codes + r * D, k_scales + r, &ke);
+                    else
+                        kvqo_quant_k_row(k16 + r * D, k_codes + r * D, k_scales + r, &ke);
                     int8_t vc[D];
                     kvqo_quant_v_row(v16 + r * D, vc, v_scales + r * (D / VG), &ve);
                     for (int j = 0; j < D; ++j) {
@@ -365,7 +448,7 @@ void kvqo_attention(int B, int Hq, int Hkv, int64_t cap, int64_t length, const u
                     float tau_k, float tau_v, const uint16_t *k16, const uint16_t *v16,
                     const int8_t *k_codes, const uint16_t *k_scales, const uint8_t *v_codes,
                     const uint16_t *v_scales, const float *k_err, const float *v_err, double *out,
-                    uint8_t *mask)
+                    uint8_t *mask, int key_rot)
 {
     int G = Hq / Hkv;
     int64_t nblk = (length + BLK - 1) / BLK;
@@ -389,10 +472,12 @@ void kvqo_attention(int B, int Hq, int Hkv, int64_t cap, int64_t length, const u
             for (int64_t t = 0; t < length; ++t) {
                 size_t r = row_index(b, h, t, Hkv, cap);
                 int fbk = m[((size_t)b * Hkv + h) * (size_t)nblk + (size_t)(t / BLK)] & 1;
-                double s = kvqo_f16_to_f64(k_scales[r]);
+                double kr[D];
+                if (!fbk)
+                    dequant_key_row(k_codes + r * D, k_scales[r], key_rot, kr);
                 double acc = 0.0;
                 for (int j = 0; j < D; ++j) {
-                    double k = fbk ? kvqo_f16_to_f64(k16[r * D + j]) : s * (double)k_codes[r * D + j];
+                    double k = fbk ? kvqo_f16_to_f64(k16[r * D + j]) : kr[j];
                     acc += qv[j] * k;
                 }
                 logit[t] = (double)sm * acc;
@@ -462,20 +547,20 @@ static void certify_masked(int B, int Hq, int Hkv, int64_t cap, int64_t length, 
                            const uint16_t *k16, const uint16_t *v16, const int8_t *k_codes,
                            const uint16_t *k_scales, const uint8_t *v_codes, const uint16_t *v_scales,
                            const float *k_err, const float *v_err, double *out, double *cert,
-                           double *e_key, double *e_val, uint8_t *recomputed);
+                           double *e_key, double *e_val, uint8_t *recomputed, int key_rot);
 
 void kvqo_certificate(int B, int Hq, int Hkv, int64_t cap, int64_t length, const uint16_t *q,
                       float sm, float tau_k, float tau_v, double tau_out, const uint16_t *k16,
                       const uint16_t *v16, const int8_t *k_codes, const uint16_t *k_scales,
                       const uint8_t *v_codes, const uint16_t *v_scales, const float *k_err,
                       const float *v_err, double *out, double *cert, double *e_key, double *e_val,
-                      uint8_t *recomputed)
+                      uint8_t *recomputed, int key_rot)
 {
     int64_t nblk = (length + BLK - 1) / BLK;
     uint8_t *m = (uint8_t *)malloc((size_t)B * Hkv * (size_t)(nblk ? nblk : 1));
     kvqo_bounds(B, Hq, Hkv, cap, length, q, sm, tau_k, tau_v, k_err, v_err, NULL, NULL, m);
     certify_masked(B, Hq, Hkv, cap, length, q, sm, m, tau_out, NULL, k16, v16, k_codes, k_scales,
-                   v_codes, v_scales, k_err, v_err, out, cert, e_key, e_val, recomputed);
+                   v_codes, v_scales, k_err, v_err, out, cert, e_key, e_val, recomputed, key_rot);
     free(m);
 }
 
@@ -487,7 +572,7 @@ static void certify_masked(int B, int Hq, int Hkv, int64_t cap, int64_t length, 
                            const uint16_t *k16, const uint16_t *v16, const int8_t *k_codes,
                            const uint16_t *k_scales, const uint8_t *v_codes, const uint16_t *v_scales,
                            const float *k_err, const float *v_err, double *out, double *cert,
-                           double *e_key, double *e_val, uint8_t *recomputed)
+                           double *e_key, double *e_val, uint8_t *recomputed, int key_rot)
 {
     int G = Hq / Hkv;
     int64_t nblk = (length + BLK - 1) / BLK;
@@ -515,11 +600,13 @@ static void certify_masked(int B, int Hq, int Hkv, int64_t cap, int64_t length, 
             for (int64_t t = 0; t < length; ++t) {
                 size_t r = row_index(b, h, t, Hkv, cap);
                 int fbk = mb[t / BLK] & 1;
-                double s = kvqo_f16_to_f64(k_scales[r]);
+                double kr[D];
+                if (!fbk)
+                    dequant_key_row(k_codes + r * D, k_scales[r], key_rot, kr);
                 double acc = 0.0, dacc = 0.0;
                 for (int j = 0; j < D; ++j) {
                     double k16v = kvqo_f16_to_f64(k16[r * D + j]);
-                    double k = fbk ? k16v : s * (double)k_codes[r * D + j];
+                    double k = fbk ? k16v : kr[j];
                     acc += qv[j] * k;
                     dacc += qv[j] * k16v;
                 }
@@ -608,7 +695,7 @@ static void certify_masked(int B, int Hq, int Hkv, int64_t cap, int64_t length, 
  * logit. */
 static void block_logmass(int b, int h, int Hkv, int64_t cap, int64_t length, const double *qv, float sm,
                           int fp16, const uint16_t *k16, const int8_t *k_codes, const uint16_t *k_scales,
-                          double *l)
+                          int key_rot, double *l)
 {
     int64_t nblk = (length + BLK - 1) / BLK;
     double lg[BLK];
@@ -617,10 +704,12 @@ static void block_logmass(int b, int h, int Hkv, int64_t cap, int64_t length, co
         double mx = -INFINITY;
         for (int64_t t = t0; t < t1; ++t) {
             size_t r = row_index(b, h, t, Hkv, cap);
-            double s = kvqo_f16_to_f64(k_scales[r]);
+            double kr[D];
+            if (!fp16)
+                dequant_key_row(k_codes + r * D, k_scales[r], key_rot, kr);
             double acc = 0.0;
             for (int j = 0; j < D; ++j) {
-                double k = fp16 ? kvqo_f16_to_f64(k16[r * D + j]) : s * (double)k_codes[r * D + j];
+                double k = fp16 ? kvqo_f16_to_f64(k16[r * D + j]) : kr[j];
                 acc += qv[j] * k;
             }
             lg[t - t0] = (double)sm * acc;
@@ -683,7 +772,7 @@ void kvqo_adaptive(int B, int Hq, int Hkv, int64_t cap, int64_t length, const ui
                    const uint8_t *v_codes, const uint16_t *v_scales, const float *k_err, const float *v_err,
                    double *out, double *cert, double *e_key, double *e_val, uint8_t *recomputed,
                    uint8_t *masks, double *lhat, double *lfp, int32_t *kstar, int64_t *ndisc,
-                   int64_t *npairs, uint8_t *inconsistent)
+                   int64_t *npairs, uint8_t *inconsistent, int key_rot)
 {
     int G = Hq / Hkv;
     int64_t nblk = (length + BLK - 1) / BLK;
@@ -701,8 +790,8 @@ void kvqo_adaptive(int B, int Hq, int Hkv, int64_t cap, int64_t length, const ui
                 qv[j] = kvqo_f16_to_f64(q[oi * D + j]);
             double *lh = lhat + oi * nb1, *lf = lfp + oi * nb1;
             uint8_t *ph = prom + oi * nb1;
-            block_logmass(b, h, Hkv, cap, length, qv, sm, 0, k16, k_codes, k_scales, lh);
-            block_logmass(b, h, Hkv, cap, length, qv, sm, 1, k16, k_codes, k_scales, lf);
+            block_logmass(b, h, Hkv, cap, length, qv, sm, 0, k16, k_codes, k_scales, key_rot, lh);
+            block_logmass(b, h, Hkv, cap, length, qv, sm, 1, k16, k_codes, k_scales, key_rot, lf);
             kstar[oi] = 0;
             ndisc[oi] = npairs[oi] = 0;
             inconsistent[oi] = 0;
@@ -784,5 +873,5 @@ void kvqo_adaptive(int B, int Hq, int Hkv, int64_t cap, int64_t length, const ui
         }
     free(prom);
     certify_masked(B, Hq, Hkv, cap, length, q, sm, masks, tau_out, inconsistent, k16, v16, k_codes, k_scales,
-                   v_codes, v_scales, k_err, v_err, out, cert, e_key, e_val, recomputed);
+                   v_codes, v_scales, k_err, v_err, out, cert, e_key, e_val, recomputed, key_rot);
 }
