@@ -80,6 +80,9 @@ def parse():
     p.add_argument("--tau-cov", type=float, default=0.995, help="adaptive step: coverage of the INT8 mass")
     p.add_argument("--tau-rank", type=float, default=0.1, help="adaptive step: discordant share that flags a head")
     p.add_argument("--tau-vc", type=float, default=float("inf"), help="adaptive step: value-promotion threshold")
+    p.add_argument("--key-rotation", action="store_true",
+                   help="Hadamard-rotated key codec (KVQ_CODEC_ROTATE_K); tolerances from a plain-codec cache of "
+                        "the same data, so the fallback shares compare at a fixed tau")
     p.add_argument("--tier2", default="device", choices=["device", "host"],
                    help="FP16 originals in HBM, or in pinned host memory read in place over the host link")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -172,7 +175,7 @@ def bench_quantize(args, w):
     import workloads
 
     d = workloads.make(w, "cuda")
-    c = kvq.KVCache(w.B, w.Hkv, w.cap, k16=d["k16"], v16=d["v16"])
+    c = kvq.KVCache(w.B, w.Hkv, w.cap, k16=d["k16"], v16=d["v16"], key_rotation=args.key_rotation)
     del d
     stream = torch.cuda.current_stream()
     th = w.B * w.Hkv * w.T
@@ -206,7 +209,8 @@ def bench_quantize(args, w):
         "vs_baseline": None, "dtype": "fp16 in, int8 K / int4 V codes out, fp64 error sums",
         "data": "synthetic (seeded normal fp16 K/V with 3 K outlier channels x20)",
         "config": {"workload": f"{w.name}: {w.T} new tokens x {w.Hkv} KV heads x D128, one bulk append",
-                   "bytes_per_step": nbytes},
+                   "bytes_per_step": nbytes, "key_codec": "rotate_k" if args.key_rotation else "plain",
+                   "k_err_median": float(c.k_err.flatten()[: w.B * w.Hkv * ((w.T + 63) // 64)].median())},
         "roofline": {"kernel": "quantize_append_kernel", "bound": "hbm", "achieved": round(kgbs, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(kgbs / HBM_PEAK_GBS, 4), "traffic": None,
                      "algorithmic_bytes_per_launch": nbytes, "mean_launch_ms": round(k_ms, 5)},
@@ -383,19 +387,23 @@ def main():
     caches = []
     for r in range(R):
         if args.tier2 == "host":
-            c = kvq.KVCache(w.B, w.Hkv, w.cap, device=dev, tier2="host")
+            c = kvq.KVCache(w.B, w.Hkv, w.cap, device=dev, tier2="host", key_rotation=args.key_rotation)
             c.k16.copy_(d["k16"])
             c.v16.copy_(d["v16"])
         else:
             k16 = d["k16"] if r == 0 else d["k16"].clone()
             v16 = d["v16"] if r == 0 else d["v16"].clone()
-            c = kvq.KVCache(w.B, w.Hkv, w.cap, device=dev, k16=k16, v16=v16)
+            c = kvq.KVCache(w.B, w.Hkv, w.cap, device=dev, k16=k16, v16=v16, key_rotation=args.key_rotation)
         kvq.kvq_quantize_append(c, w.T - 1)  # prefill; the step appends token T-1
         caches.append(c)
     q = d["q"].contiguous()
 
     # tolerances: ~fallback_frac of the blocks per bound, from the library's own bounds
     c0 = caches[0]
+    if args.key_rotation:
+        # tolerances of the plain codec on the same data (a fixed tau)
+        c0 = kvq.KVCache(w.B, w.Hkv, w.cap, device=dev, k16=caches[0].k16, v16=caches[0].v16)
+        kvq.kvq_quantize_append(c0, w.T - 1)
     kvq.kvq_quantize_append(c0, 1)
     kb, vb, _ = kvq.kvq_bounds(c0, q, sm, 0.0, 0.0, want=("kb", "vb"))
     kbn, vbn = kb.flatten().float().cpu().numpy(), vb.flatten().float().cpu().numpy()
@@ -412,6 +420,9 @@ def main():
     if args.taus:
         tau_k, tau_v = (float(x) for x in args.taus.split(","))
     c0.length = w.T - 1
+    if args.key_rotation:
+        del c0, kb, vb
+        torch.cuda.empty_cache()
 
     out = torch.empty_like(q)
     mask = torch.empty((w.B, w.Hkv, (w.T + 63) // 64), dtype=torch.uint8, device=dev)
@@ -512,6 +523,7 @@ def main():
             "kernel": args.kernel, "splits": args.splits, "hip_graph": bool(args.graph), "steps_per_graph": R if args.graph else None,
             "fused_append": not args.unfused,
             "tier2": args.tier2,
+            "key_codec": "rotate_k (tolerances of the plain codec)" if args.key_rotation else "plain",
             "bytes_per_step": step_bytes,
         },
         "roofline": {

@@ -93,6 +93,22 @@ typedef enum {
     KVQ_ERR_HIP = -6          /* a HIP call failed; see kvq_last_hip_error() */
 } kvq_status;
 
+/* Key codecs.  KVQ_CODEC_ROTATE_K (outlier-aware codec: the Walsh-Hadamard
+ * transform before scalar quantization of the KQV scheme in "Statistical
+ * Inference and Quality Measures of KV Cache Quantisations Inspired by
+ * TurboQuant", technical summary, quantisation schemes, applied to the keys
+ * alone) quantizes each key row after the rotation u = H k / 16, H the +-1
+ * Sylvester-Hadamard matrix of order 128 (exact in fp64): s = f16(f32(max|u|)
+ * / 127), c = clamp(round_half_even(u / s), -127, 127) with the quotient in
+ * fp64, and reads keys back as k~ = H (s c) / 8; the key error is
+ * ||k - k~|| = f32(sqrt(2 * T128((u - s c)^2))), so the key bound and the
+ * certificate keep their meaning.  The decode rotates q instead of the keys
+ * (q . k~ = (H q / 8) . (s c)); outlier channels spread over the row, which
+ * lowers the key errors and the fallback share.  Values keep their codec.
+ * A cache's codec is fixed when its first token is quantized. */
+#define KVQ_CODEC_PLAIN 0
+#define KVQ_CODEC_ROTATE_K 1
+
 /* A quantized KV cache for one attention layer.  The struct is host memory;
  * every pointer in it is owned by the caller: device memory, except that
  * k16/v16 may be pinned host memory the device reads (kvq_tier2_location). */
@@ -102,7 +118,7 @@ typedef struct kvq_cache {
     int32_t head_dim;     /* must be 128 */
     int32_t block_tokens; /* must be 64 */
     int32_t v_group;      /* must be 32 */
-    int32_t reserved;     /* set to 0 */
+    int32_t codec;        /* KVQ_CODEC_PLAIN or KVQ_CODEC_ROTATE_K */
     int64_t capacity;     /* tokens per sequence, multiple of 64 */
     int64_t length;       /* valid tokens per sequence (host-side) */
     const uint16_t *k16;  /* FP16 originals, written by the caller */

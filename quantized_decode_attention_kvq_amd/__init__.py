@@ -25,6 +25,7 @@ VG = 32
 
 KVQ_OK = 0
 KERNEL_AUTO, KERNEL_VALU, KERNEL_MFMA = 0, 1, 2
+KVQ_CODEC_PLAIN, KVQ_CODEC_ROTATE_K = 0, 1
 DEFAULT_SM_SCALE = float(torch.tensor(1.0 / math.sqrt(D), dtype=torch.float32))
 
 
@@ -40,7 +41,7 @@ class KvqError(RuntimeError):
 class _Cache(ctypes.Structure):
     _fields_ = [
         ("batch", ctypes.c_int32), ("kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
-        ("block_tokens", ctypes.c_int32), ("v_group", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("block_tokens", ctypes.c_int32), ("v_group", ctypes.c_int32), ("codec", ctypes.c_int32),
         ("capacity", ctypes.c_int64), ("length", ctypes.c_int64),
         ("k16", ctypes.c_void_p), ("v16", ctypes.c_void_p),
         ("k_codes", ctypes.c_void_p), ("k_scales", ctypes.c_void_p),
@@ -128,9 +129,12 @@ class KVCache:
         k_err, v_err float32 [B][Hkv][cap/64]
     `length` is host-side and advanced by kvq_quantize_append.
     tier2="host" keeps k16/v16 in pinned host memory that the kernels read
-    in place (zero-copy over the host link), checked by kvq_tier2_location."""
+    in place (zero-copy over the host link), checked by kvq_tier2_location.
+    key_rotation=True selects the Hadamard-rotated key codec
+    (KVQ_CODEC_ROTATE_K)."""
 
-    def __init__(self, batch, kv_heads, capacity, device="cuda", k16=None, v16=None, tier2="device"):
+    def __init__(self, batch, kv_heads, capacity, device="cuda", k16=None, v16=None, tier2="device",
+                 key_rotation=False):
         if capacity % BLK:
             raise ValueError("capacity must be a multiple of 64")
         dev = torch.device(device)
@@ -141,6 +145,7 @@ class KVCache:
         shape = (batch, kv_heads, capacity, D)
         self.batch, self.kv_heads, self.capacity, self.length = batch, kv_heads, capacity, 0
         self.tier2 = tier2
+        self.codec = KVQ_CODEC_ROTATE_K if key_rotation else KVQ_CODEC_PLAIN
         host = tier2 == "host"
         t2dev = torch.device("cpu") if host else dev
         self.k16 = k16 if k16 is not None else torch.zeros(shape, dtype=torch.float16, device=t2dev, pin_memory=host)
@@ -168,7 +173,7 @@ class KVCache:
         return (self.length + BLK - 1) // BLK
 
     def c_struct(self):
-        return _Cache(self.batch, self.kv_heads, D, BLK, VG, 0, self.capacity, self.length,
+        return _Cache(self.batch, self.kv_heads, D, BLK, VG, self.codec, self.capacity, self.length,
                       self.k16.data_ptr(), self.v16.data_ptr(), self.k_codes.data_ptr(),
                       self.k_scales.data_ptr(), self.v_codes.data_ptr(), self.v_scales.data_ptr(),
                       self.k_err.data_ptr(), self.v_err.data_ptr())

@@ -42,6 +42,7 @@ constexpr int SEL_REGS = 16;  // masses per lane held in registers by the select
 // lane (row m, k-group g4) holds channels 32 g4 + 8 kc .. +8 of token m for
 // instruction kc (32 contiguous code bytes per lane), and the q operand uses
 // the same channel order.  Result lane (head m, g4): tokens 4 g4 .. +3.
+template <bool ROT>
 __global__ __launch_bounds__(256) void score_int8_kernel(AdaptArgs a) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int m = lane & 15, g4 = lane >> 4;
@@ -55,6 +56,9 @@ __global__ __launch_bounds__(256) void score_int8_kernel(AdaptArgs a) {
         for (int kc = 0; kc < 4; ++kc)
             qb[kc] = m < g ? *reinterpret_cast<const uint4 *>(qh + 8 * kc) : make_uint4(0u, 0u, 0u, 0u);
     }
+    // rotated key codec: score the codes against the rotated query
+    uint4 qrl[4];
+    if (ROT) rotate_q(qb, lane, qb, qrl);
     const float sml2 = a.sm * 1.4426950408889634f;
     for (int r = 0; r < BPW; ++r) {
         const int64_t i = ((int64_t)blockIdx.x * 4 + wave) * BPW + r;
@@ -67,10 +71,18 @@ __global__ __launch_bounds__(256) void score_int8_kernel(AdaptArgs a) {
             const uint4 c0 = *reinterpret_cast<const uint4 *>(row);
             const uint4 c1 = *reinterpret_cast<const uint4 *>(row + 16);
             float4_t acc = {0.f, 0.f, 0.f, 0.f};
-            acc = mfma(i8x8_to_h8(c0.x, c0.y), qb[0], acc);
-            acc = mfma(i8x8_to_h8(c0.z, c0.w), qb[1], acc);
-            acc = mfma(i8x8_to_h8(c1.x, c1.y), qb[2], acc);
-            acc = mfma(i8x8_to_h8(c1.z, c1.w), qb[3], acc);
+            const uint4 a0 = i8x8_to_h8(c0.x, c0.y), a1 = i8x8_to_h8(c0.z, c0.w);
+            const uint4 a2 = i8x8_to_h8(c1.x, c1.y), a3 = i8x8_to_h8(c1.z, c1.w);
+            acc = mfma(a0, qb[0], acc);
+            acc = mfma(a1, qb[1], acc);
+            acc = mfma(a2, qb[2], acc);
+            acc = mfma(a3, qb[3], acc);
+            if (ROT) {
+                acc = mfma(a0, qrl[0], acc);
+                acc = mfma(a1, qrl[1], acc);
+                acc = mfma(a2, qrl[2], acc);
+                acc = mfma(a3, qrl[3], acc);
+            }
             const uint2 ks = *reinterpret_cast<const uint2 *>(a.c.k_scales + bh * a.cap + t0 + 16 * tt + 4 * g4);
             const uint32_t kw[4] = {ks.x & 0xFFFFu, ks.x >> 16, ks.y & 0xFFFFu, ks.y >> 16};
 #pragma unroll
@@ -206,7 +218,11 @@ __global__ __launch_bounds__(256) void select_kernel(AdaptArgs a) {
 
 hipError_t launch_score(const AdaptArgs &a, int batch, hipStream_t s) {
     const unsigned gx = (unsigned)((a.nb + 4 * BPW - 1) / (4 * BPW));
-    hipLaunchKernelGGL(score_int8_kernel, dim3(gx, (unsigned)a.hkv, (unsigned)batch), dim3(256), 0, s, a);
+    const dim3 grid(gx, (unsigned)a.hkv, (unsigned)batch);
+    if (a.key_rot)
+        hipLaunchKernelGGL(score_int8_kernel<true>, grid, dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL(score_int8_kernel<false>, grid, dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

@@ -26,6 +26,7 @@ kvq_status check_shape(const kvq_cache *c) {
         return KVQ_ERR_INVALID_ARG;
     if (c->length < 0 || c->length > c->capacity) return KVQ_ERR_INVALID_ARG;
     if (c->batch > 65535 || c->kv_heads > 65535) return KVQ_ERR_UNSUPPORTED;
+    if (c->codec != KVQ_CODEC_PLAIN && c->codec != KVQ_CODEC_ROTATE_K) return KVQ_ERR_UNSUPPORTED;
     return KVQ_OK;
 }
 
@@ -226,6 +227,7 @@ kvq_status kvq_quantize_append(kvq_cache *c, int64_t n_new, void *stream) {
     a.len1 = c->length + n_new;
     a.blk_lo = a.len0 / kvq::BLK;
     a.hkv = c->kv_heads;
+    a.key_rot = c->codec == KVQ_CODEC_ROTATE_K ? 1 : 0;
     const int64_t nblk = (a.len1 - 1) / kvq::BLK - a.blk_lo + 1;
     if (nblk > 0x7FFFFFFF) return KVQ_ERR_UNSUPPORTED;
     hipError_t e = kvq::launch_append(a, c->batch, nblk, (hipStream_t)stream);
@@ -330,6 +332,8 @@ kvq_status decode_impl(kvq_cache *c, const uint16_t *q, int32_t q_heads, float s
     int32_t k = kernel;
     if (k == KVQ_KERNEL_AUTO) k = mfma_fits ? KVQ_KERNEL_MFMA : KVQ_KERNEL_VALU;
     if (certify && k != KVQ_KERNEL_MFMA) return KVQ_ERR_UNSUPPORTED;  // the certificate is a matrix-core path
+    // the rotated key codec is read by the matrix-core kernel only
+    if (c->codec == KVQ_CODEC_ROTATE_K && k != KVQ_KERNEL_MFMA) return KVQ_ERR_UNSUPPORTED;
     if (k == KVQ_KERNEL_MFMA && !mfma_fits) return KVQ_ERR_UNSUPPORTED;
     const bool mf = k == KVQ_KERNEL_MFMA;
     const int64_t s = nb > 0 ? choose_splits(c, nb, splits, mf ? 1 : 4, mf ? kvq::MFMA_MAX_BPS : kvq::MAX_BPS) : 1;
@@ -366,6 +370,7 @@ kvq_status decode_impl(kvq_cache *c, const uint16_t *q, int32_t q_heads, float s
     a.tau_k = tau_k;
     a.tau_v = tau_v;
     a.t_new = append ? c->length : -1;
+    a.key_rot = c->codec == KVQ_CODEC_ROTATE_K ? 1 : 0;
     a.cert_mode = certify ? 1 : 0;
     a.part_e = reinterpret_cast<float *>((char *)workspace + w.e);
     a.part_sa = reinterpret_cast<float2 *>((char *)workspace + w.sa);
@@ -400,6 +405,7 @@ kvq_status decode_impl(kvq_cache *c, const uint16_t *q, int32_t q_heads, float s
         aa.hkv = c->kv_heads;
         aa.hq = q_heads;
         aa.g = g;
+        aa.key_rot = a.key_rot;
         aa.sm = sm_scale;
         aa.tau_cov = ad->tau_cov;
         aa.tau_vc = ad->tau_vc;

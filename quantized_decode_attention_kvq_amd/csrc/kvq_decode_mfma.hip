@@ -279,10 +279,14 @@ struct WaveState {
     uint32_t smax, amax;
 };
 
-template <bool CERT, bool RANK, typename Mid>
+// ROT: the key codes are those of Hadamard-rotated keys, scored against the
+// rotated query (qrh + qrl, its fp16 high and low parts); FP16 key rows use
+// the query itself.
+template <bool CERT, bool RANK, bool ROT, typename Mid>
 __device__ __forceinline__ void process_step(const uint8_t *stage, uint32_t mk, int p_lo, int p_hi,
-                                             const uint4 (&qb)[4], float sml2, WaveState &w, int lane,
-                                             float eta, float2 *rank_out, int g, Mid &&mid) {
+                                             const uint4 (&qb)[4], const uint4 (&qrh)[4], const uint4 (&qrl)[4],
+                                             float sml2, WaveState &w, int lane, float eta, float2 *rank_out,
+                                             int g, Mid &&mid) {
     const int m = lane & 15, g4 = lane >> 4;
     const bool partial = p_lo > 0 || p_hi < 32;  // wave-uniform
 
@@ -313,10 +317,24 @@ __device__ __forceinline__ void process_step(const uint8_t *stage, uint32_t mk, 
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
             float4_t c = {0.f, 0.f, 0.f, 0.f};
-            c = mfma(i8x8_to_h8(kt[2 * e].x, kt[2 * e].y), qb[0], c);
-            c = mfma(i8x8_to_h8(kt[2 * e].z, kt[2 * e].w), qb[1], c);
-            c = mfma(i8x8_to_h8(kt[2 * e + 1].x, kt[2 * e + 1].y), qb[2], c);
-            c = mfma(i8x8_to_h8(kt[2 * e + 1].z, kt[2 * e + 1].w), qb[3], c);
+            const uint4 a0 = i8x8_to_h8(kt[2 * e].x, kt[2 * e].y), a1 = i8x8_to_h8(kt[2 * e].z, kt[2 * e].w);
+            const uint4 a2 = i8x8_to_h8(kt[2 * e + 1].x, kt[2 * e + 1].y);
+            const uint4 a3 = i8x8_to_h8(kt[2 * e + 1].z, kt[2 * e + 1].w);
+            if (ROT) {
+                c = mfma(a0, qrh[0], c);
+                c = mfma(a1, qrh[1], c);
+                c = mfma(a2, qrh[2], c);
+                c = mfma(a3, qrh[3], c);
+                c = mfma(a0, qrl[0], c);
+                c = mfma(a1, qrl[1], c);
+                c = mfma(a2, qrl[2], c);
+                c = mfma(a3, qrl[3], c);
+            } else {
+                c = mfma(a0, qb[0], c);
+                c = mfma(a1, qb[1], c);
+                c = mfma(a2, qb[2], c);
+                c = mfma(a3, qb[3], c);
+            }
             sc[e] = c;
         }
         // key scales of positions 8*g4 + 4e + i (one dword per token)
@@ -519,7 +537,7 @@ __device__ __forceinline__ uint16_t f16_up(float x) {
 // CERT: also the per-head output certificate's per-split parts (the
 // mass-weighted value error, the largest certified value scale and
 // fallback |v|, and the largest certified block errors).
-template <bool CERT, bool RANK>
+template <bool CERT, bool RANK, bool ROT>
 __device__ __forceinline__ void decode_group(const DecodeArgs &a, const int split, const int64_t kvh,
                                              const int64_t b) {
     // NW waves x NSTAGE stages x 6656 B of ring.  Before the stream starts, the
@@ -604,6 +622,9 @@ __device__ __forceinline__ void decode_group(const DecodeArgs &a, const int spli
         for (int o = 1; o < 16; o <<= 1) qh = max_keep_nan(qh, __shfl_xor(qh, o));
         qn = qh;
     }
+    // rotated key codec: the query rotated the same way, for the code tiles
+    uint4 qrh[4], qrl[4];
+    if (ROT) rotate_q(qb, lane, qrh, qrl);
 
     __shared__ __attribute__((aligned(16))) uint8_t nk_lds[D];  // key codes of the new token
     __shared__ __attribute__((aligned(16))) uint8_t nv_lds[D];  // its value codes (low nibbles)
@@ -611,7 +632,7 @@ __device__ __forceinline__ void decode_group(const DecodeArgs &a, const int spli
     __shared__ float nerr_lds[2];                                // its key and value errors
     RowQuant rq = {};
     if (qgroup) {
-        rq = quant_row16(rin);
+        rq = quant_row16(rin, ROT, tid & 15);
         const int l16 = tid & 15;
         *reinterpret_cast<uint2 *>(&nk_lds[8 * l16]) = make_uint2(rq.kc[0], rq.kc[1]);
         *reinterpret_cast<uint2 *>(&nv_lds[8 * l16]) = make_uint2(rq.vc[0], rq.vc[1]);
@@ -880,7 +901,7 @@ __device__ __forceinline__ void decode_group(const DecodeArgs &a, const int spli
         const int64_t left = a.length - (blk * BLK + step_len * sub);
         const int nvalid = (int)(left < step_len ? (left > 0 ? left : 0) : step_len);
         if (nvalid > 0)
-            process_step<CERT, RANK>(stage, mk, p_lo, p_lo + nvalid, qb, sml2, ws, lane,
+            process_step<CERT, RANK, ROT>(stage, mk, p_lo, p_lo + nvalid, qb, qrh, qrl, sml2, ws, lane,
                                      CERT ? h2f(teta_lds[blk - blo]) : 0.0f,
                                      RANK ? a.step_ml + ((bh * a.nbc + blk) * 8 + sub * (8 / steps_of(mk))) * g
                                           : nullptr,
@@ -956,9 +977,9 @@ __device__ __forceinline__ void decode_group(const DecodeArgs &a, const int spli
     }
 }
 
-template <bool CERT, bool RANK>
+template <bool CERT, bool RANK, bool ROT>
 __global__ __launch_bounds__(NW * 64, NW / 4) void decode_mfma_kernel(DecodeArgs a) {
-    decode_group<CERT, RANK>(a, blockIdx.x, blockIdx.y, blockIdx.z);
+    decode_group<CERT, RANK, ROT>(a, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
 // Index of the rank-th group i in [0, n) (in index order) with a set byte
@@ -999,13 +1020,14 @@ __device__ int64_t nth_set(const uint8_t *flags, const int g, const int64_t n, c
 // (splits, slots), slot y taking the set groups of rank y, y + slots, ...
 // Few groups are expected, and their count is known only on the device, so
 // a small grid spreads them over the chip instead of a grid over every group.
+template <bool ROT>
 __global__ __launch_bounds__(NW * 64, NW / 4) void decode_mfma_gated_kernel(DecodeArgs a, int64_t nbh) {
     __shared__ int wcnt[NW];
     __shared__ int64_t pick;
     for (int rank = blockIdx.y;; rank += gridDim.y) {
         const int64_t bh = nth_set(a.gate, a.g, nbh, rank, wcnt, &pick);
         if (bh < 0) break;
-        decode_group<false, false>(a, blockIdx.x, bh % a.hkv, bh / a.hkv);
+        decode_group<false, false, ROT>(a, blockIdx.x, bh % a.hkv, bh / a.hkv);
     }
 }
 
@@ -1013,18 +1035,31 @@ bool mfma_supports(int g) { return g >= 1 && g <= 16; }
 
 hipError_t launch_decode_mfma(const DecodeArgs &a, int batch, hipStream_t s) {
     dim3 grid((unsigned)a.splits, (unsigned)a.hkv, (unsigned)batch);
-    if (a.cert_mode && a.step_ml)
-        hipLaunchKernelGGL((decode_mfma_kernel<true, true>), grid, dim3(NW * 64), 0, s, a);
-    else if (a.cert_mode)
-        hipLaunchKernelGGL((decode_mfma_kernel<true, false>), grid, dim3(NW * 64), 0, s, a);
-    else
-        hipLaunchKernelGGL((decode_mfma_kernel<false, false>), grid, dim3(NW * 64), 0, s, a);
+    const dim3 blk(NW * 64);
+    if (a.key_rot) {
+        if (a.cert_mode && a.step_ml)
+            hipLaunchKernelGGL((decode_mfma_kernel<true, true, true>), grid, blk, 0, s, a);
+        else if (a.cert_mode)
+            hipLaunchKernelGGL((decode_mfma_kernel<true, false, true>), grid, blk, 0, s, a);
+        else
+            hipLaunchKernelGGL((decode_mfma_kernel<false, false, true>), grid, blk, 0, s, a);
+    } else {
+        if (a.cert_mode && a.step_ml)
+            hipLaunchKernelGGL((decode_mfma_kernel<true, true, false>), grid, blk, 0, s, a);
+        else if (a.cert_mode)
+            hipLaunchKernelGGL((decode_mfma_kernel<true, false, false>), grid, blk, 0, s, a);
+        else
+            hipLaunchKernelGGL((decode_mfma_kernel<false, false, false>), grid, blk, 0, s, a);
+    }
     return hipGetLastError();
 }
 
 hipError_t launch_decode_mfma_gated(const DecodeArgs &a, int batch, int slots, hipStream_t s) {
     dim3 grid((unsigned)a.splits, (unsigned)slots, 1);
-    hipLaunchKernelGGL(decode_mfma_gated_kernel, grid, dim3(NW * 64), 0, s, a, (int64_t)batch * a.hkv);
+    if (a.key_rot)
+        hipLaunchKernelGGL(decode_mfma_gated_kernel<true>, grid, dim3(NW * 64), 0, s, a, (int64_t)batch * a.hkv);
+    else
+        hipLaunchKernelGGL(decode_mfma_gated_kernel<false>, grid, dim3(NW * 64), 0, s, a, (int64_t)batch * a.hkv);
     return hipGetLastError();
 }
 

@@ -27,6 +27,7 @@ struct AppendArgs {
     int64_t len1;    // one past the last new token
     int64_t blk_lo;  // first block touched (len0 / 64)
     int32_t hkv;
+    int32_t key_rot;  // KVQ_CODEC_ROTATE_K: Hadamard-rotated key codec
 };
 
 struct BoundsArgs {
@@ -52,6 +53,7 @@ struct DecodeArgs {
     int32_t splits, bps;  // number of splits and blocks per split
     float sm, tau_k, tau_v;
     int64_t t_new;  // token appended by this launch (fused append), or -1
+    int32_t key_rot;  // KVQ_CODEC_ROTATE_K: codes of the rotated keys (rotate q for them)
     // per-head output certificate (matrix-core kernel with cert_mode set)
     int32_t cert_mode;
     float *part_e;          // [B*Hkv][S][G] mass-weighted value error, on the split's running-max scale
@@ -88,6 +90,7 @@ struct AdaptArgs {
     int32_t *kstar;          // [B][Hq] blocks each head promotes, or null
     int64_t cap, length, nbc, nb;
     int32_t hkv, hq, g;
+    int32_t key_rot;         // KVQ_CODEC_ROTATE_K
     float sm, tau_cov, tau_vc;
 };
 

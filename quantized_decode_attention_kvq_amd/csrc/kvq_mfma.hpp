@@ -37,4 +37,63 @@ __device__ __forceinline__ uint4 i8x8_to_h8(uint32_t x0, uint32_t x1) {
 }
 
 
+// Hadamard-rotated query for KVQ_CODEC_ROTATE_K caches, in the B-operand
+// layout: lane (n, g) holds q[n][32g + 8s .. +8] in qb[s], s = 0..3.  Returns
+// H q / 8 (H the +-1 Sylvester matrix of order 128) as two fp16 parts per
+// channel, hi = f16(x) and lo = f16(x - hi), so that two matrix-core products
+// reproduce the rotated query to about 2^-22: butterflies at channel
+// strides 1 .. 16 inside the lane and 32, 64 across lanes xor 16, 32, in
+// fp32.  All 64 lanes take part.
+__device__ __forceinline__ void rotate_q(const uint4 (&qb)[4], int lane, uint4 (&hi)[4], uint4 (&lo)[4]) {
+    float v[32];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const uint32_t w[4] = {qb[s].x, qb[s].y, qb[s].z, qb[s].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[8 * s + 2 * i] = h2f(w[i] & 0xFFFFu);
+            v[8 * s + 2 * i + 1] = h2f(w[i] >> 16);
+        }
+    }
+#pragma unroll
+    for (int h = 1; h < 32; h <<= 1)
+#pragma unroll
+        for (int j = 0; j < 32; ++j)
+            if (!(j & h)) {
+                const float x = v[j], y = v[j + h];
+                v[j] = x + y;
+                v[j + h] = x - y;
+            }
+    // partners across lanes xor 16 and xor 32 by the row-swap permutes (VALU,
+    // no LDS round trip): with both operands the value, the first result
+    // holds the partner's value in odd rows (upper half) and the second in
+    // even rows (lower half)
+    const bool up16 = (lane & 16) != 0, up32 = (lane & 32) != 0;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[j]), __float_as_uint(v[j]), false, false);
+        const float o = __uint_as_float(up16 ? r[0] : r[1]);
+        v[j] = up16 ? o - v[j] : v[j] + o;
+    }
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[j]), __float_as_uint(v[j]), false, false);
+        const float o = __uint_as_float(up32 ? r[0] : r[1]);
+        v[j] = up32 ? o - v[j] : v[j] + o;
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        uint32_t wh[4], wl[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float a = v[8 * s + 2 * i] * 0.125f, b = v[8 * s + 2 * i + 1] * 0.125f;
+            const uint32_t ha = f2h_rn(a), hb = f2h_rn(b);
+            wh[i] = ha | (hb << 16);
+            wl[i] = f2h_rn(a - h2f(ha)) | (f2h_rn(b - h2f(hb)) << 16);
+        }
+        hi[s] = make_uint4(wh[0], wh[1], wh[2], wh[3]);
+        lo[s] = make_uint4(wl[0], wl[1], wl[2], wl[3]);
+    }
+}
+
 }  // namespace kvq

@@ -74,7 +74,67 @@ __device__ __forceinline__ RowIn load_row16(const uint16_t *k16row, const uint16
     return r;
 }
 
-__device__ __forceinline__ RowQuant quant_row16(const RowIn &in) {
+// Key row with the Hadamard rotation (KVQ_CODEC_ROTATE_K): u = H k / 16
+// over the 16-lane group, in fp64 where every butterfly is exact (k's values
+// are multiples of 2^-24 below 2^16, so the sums fit 47 bits and their order
+// does not matter): strides 1, 2, 4 in the lane, 8 .. 64 across lanes xor
+// 1 .. 8.  Then the key codec on u with the quotient u / s in fp64 (u is a
+// multiple of 2^-28, so a quotient that is not a half-integer lies at least
+// 2^-43 from one, beyond its fp64 rounding: rint gives the exact round half
+// to even), e = u - s c exact, and the error sqrt(2 * T128(e^2)) with the
+// squares rounded to fp64 (the keys read back are H (s c) / 8).
+__device__ __forceinline__ void quant_key_rot16(const uint32_t kw[4], bool knonfin, int lane16, uint32_t kc[2],
+                                                uint32_t &ksb, float &kerr) {
+    double u[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) u[k] = (double)elem(kw, k);
+#pragma unroll
+    for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (!(j & h)) {
+                const double x = u[j], y = u[j + h];
+                u[j] = x + y;
+                u[j + h] = x - y;
+            }
+#pragma unroll
+    for (int mk = 1; mk < 16; mk <<= 1) {
+        const bool hi = (lane16 & mk) != 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const double o = shfl_xor_d(u[k], mk);
+            u[k] = hi ? o - u[k] : u[k] + o;
+        }
+    }
+    double am = 0.0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        u[k] = u[k] * 0.0625;
+        am = fmax(am, fabs(u[k]));
+    }
+#pragma unroll
+    for (int mk = 1; mk < 16; mk <<= 1) am = fmax(am, shfl_xor_d(am, mk));
+    ksb = knonfin ? 0u : f2h_rn(__fdiv_rn((float)am, 127.0f));
+    const double s = (double)h2f(ksb);
+    kc[0] = kc[1] = 0u;
+    double sq[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        int c = 0;
+        if (s != 0.0) {
+            const double qv = __builtin_rint(u[k] / s);
+            c = (int)(qv > 127.0 ? 127.0 : (qv < -127.0 ? -127.0 : qv));
+        }
+        const double e = u[k] - s * (double)c;  // s * c exact: no rounding to fuse
+        sq[k] = __dmul_rn(e, e);
+        kc[k >> 2] |= ((uint32_t)c & 0xFFu) << (8 * (k & 3));
+    }
+    const double ss = tree128(sq);
+    kerr = knonfin ? __builtin_huge_valf() : (float)__dsqrt_rn(2.0 * ss);
+}
+
+// rot: the key row uses the Hadamard-rotated codec (KVQ_CODEC_ROTATE_K).
+__device__ __forceinline__ RowQuant quant_row16(const RowIn &in, bool rot, int lane16) {
     RowQuant o;
     // ---------------- key row: int8 per token, scale absmax/127
     const uint4 kr = in.k;
@@ -85,23 +145,29 @@ __device__ __forceinline__ RowQuant quant_row16(const RowIn &in) {
     am = umax(am, __shfl_xor(am, 4));
     am = umax(am, __shfl_xor(am, 8));
     const bool knonfin = am >= 0x7C00u;
-    const uint32_t ksb = knonfin ? 0u : f2h_rn(__fdiv_rn(h2f(am), 127.0f));
-    const float ks = h2f(ksb);
-    // a zero scale (tiny, all-zero or non-finite row) gives codes 0
-    const float kr_ = ks != 0.0f ? __builtin_amdgcn_rcpf(ks) : 0.0f;
-    const float khs = ks != 0.0f ? 0.5f * ks : __builtin_huge_valf();
     uint32_t kc[2] = {0u, 0u};
-    double sq[8];
+    uint32_t ksb;
+    float kerr;
+    if (rot) {
+        quant_key_rot16(kw, knonfin, lane16, kc, ksb, kerr);
+    } else {
+        ksb = knonfin ? 0u : f2h_rn(__fdiv_rn(h2f(am), 127.0f));
+        const float ks = h2f(ksb);
+        // a zero scale (tiny, all-zero or non-finite row) gives codes 0
+        const float kr_ = ks != 0.0f ? __builtin_amdgcn_rcpf(ks) : 0.0f;
+        const float khs = ks != 0.0f ? 0.5f * ks : __builtin_huge_valf();
+        double sq[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        const float x = elem(kw, k);
-        float e;
-        const int c = quant_code(x, ks, kr_, khs, 127, e);
-        sq[k] = sq64(e);
-        kc[k >> 2] |= ((uint32_t)c & 0xFFu) << (8 * (k & 3));
+        for (int k = 0; k < 8; ++k) {
+            const float x = elem(kw, k);
+            float e;
+            const int c = quant_code(x, ks, kr_, khs, 127, e);
+            sq[k] = sq64(e);
+            kc[k >> 2] |= ((uint32_t)c & 0xFFu) << (8 * (k & 3));
+        }
+        const double ss = tree128(sq);
+        kerr = knonfin ? __builtin_huge_valf() : (float)__dsqrt_rn(ss);
     }
-    const double ss = tree128(sq);
-    const float kerr = knonfin ? __builtin_huge_valf() : (float)__dsqrt_rn(ss);
 
     // ---------------- value row: int4 per 32-channel group, scale absmax/7
     const uint4 vr = in.v;
@@ -142,8 +208,9 @@ __device__ __forceinline__ RowQuant quant_row16(const RowIn &in) {
     return o;
 }
 
-__device__ __forceinline__ RowQuant quant_row16(const uint16_t *k16row, const uint16_t *v16row, int lane16) {
-    return quant_row16(load_row16(k16row, v16row, lane16));
+__device__ __forceinline__ RowQuant quant_row16(const uint16_t *k16row, const uint16_t *v16row, int lane16,
+                                                bool rot) {
+    return quant_row16(load_row16(k16row, v16row, lane16), rot, lane16);
 }
 
 }  // namespace kvq

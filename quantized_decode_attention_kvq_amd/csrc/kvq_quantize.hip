@@ -42,7 +42,8 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(AppendArgs a) {
         if (t < t_begin || t >= t_end) continue;
         const int64_t roff = (row_base + t) * D + 8 * lane16;
 
-        const RowQuant rq = quant_row16(a.c.k16 + (row_base + t) * D, a.c.v16 + (row_base + t) * D, lane16);
+        const RowQuant rq = quant_row16(a.c.k16 + (row_base + t) * D, a.c.v16 + (row_base + t) * D, lane16,
+                                        a.key_rot != 0);
         const uint32_t kc[2] = {rq.kc[0], rq.kc[1]}, vc[2] = {rq.vc[0], rq.vc[1]};
         const uint32_t ksb = rq.ksb, vsb = rq.vsb;
         const float kerr = rq.kerr, verr = rq.verr;

@@ -13,21 +13,21 @@ SM = float(np.float32(1 / math.sqrt(128)))
 OUT_TOL = 2e-3  # max |o - o_ref| / max |o_ref| per output row
 
 
-def gpu_cache(data, T, device="cuda", append_chunks=None):
+def gpu_cache(data, T, device="cuda", append_chunks=None, key_rotation=False):
     """Device cache holding T tokens of data['k16'/'v16'], appended in
     `append_chunks` (default: one bulk append)."""
     k16 = data["k16"].to(device).contiguous()
     v16 = data["v16"].to(device).contiguous()
     B, Hkv, cap, _ = k16.shape
-    c = kvq.KVCache(B, Hkv, cap, device=device, k16=k16, v16=v16)
+    c = kvq.KVCache(B, Hkv, cap, device=device, k16=k16, v16=v16, key_rotation=key_rotation)
     for n in (append_chunks or [T]):
         kvq.kvq_quantize_append(c, n)
     assert c.length == T
     return c
 
 
-def oracle_cache(data, T):
-    return oracle.Cache(data["k16"].cpu().numpy(), data["v16"].cpu().numpy(), T)
+def oracle_cache(data, T, key_rotation=False):
+    return oracle.Cache(data["k16"].cpu().numpy(), data["v16"].cpu().numpy(), T, key_rotation=key_rotation)
 
 
 def assert_tier1_equal(gc, oc, T):

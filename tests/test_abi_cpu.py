@@ -134,3 +134,10 @@ def test_adaptive_validation():
     # more than 8192 blocks per sequence
     big = cache(B=1, H=1, cap=8194 * 64, length=8193 * 64 + 1)
     assert _adaptive(big, L().kvq_adaptive_workspace_bytes(ctypes.byref(big), 8)) == UNSUPPORTED
+
+
+def test_codec_validation():
+    out = (ctypes.c_size_t * 6)()
+    assert L().kvq_cache_bytes(ctypes.byref(cache(codec=1)), out) == OK
+    assert L().kvq_cache_bytes(ctypes.byref(cache(codec=2)), out) == UNSUPPORTED
+    assert L().kvq_quantize_append(ctypes.byref(cache(codec=-1)), 1, None) == UNSUPPORTED
