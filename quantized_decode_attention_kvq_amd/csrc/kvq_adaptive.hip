@@ -36,6 +36,31 @@ constexpr float NEG_INF = -__builtin_huge_valf();
 constexpr int BPW = 1;        // blocks per wave of the scoring pass (more waves in flight beat fewer, longer ones)
 constexpr int SEL_REGS = 16;  // masses per lane held in registers by the selection
 
+// Rotated query of the Hadamard-rotated key codec, once per call: grid
+// (Hkv, B), one wave; lane (head m, k-group g4) rotates as in the decode and
+// stores hi and lo at qrot[head][0 / 1][32 g4 .. +32].
+__global__ __launch_bounds__(64) void rotate_query_kernel(AdaptArgs a) {
+    const int lane = threadIdx.x;
+    const int m = lane & 15, g4 = lane >> 4;
+    const int64_t kvh = blockIdx.x, b = blockIdx.y;
+    const int g = a.g;
+    const int64_t head = (b * a.hq) + kvh * g + (m < g ? m : 0);
+    uint4 qb[4], hi[4], lo[4];
+    const uint16_t *qh = a.q + head * D + 32 * g4;
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc)
+        qb[kc] = m < g ? *reinterpret_cast<const uint4 *>(qh + 8 * kc) : make_uint4(0u, 0u, 0u, 0u);
+    rotate_q(qb, lane, hi, lo);
+    if (m < g) {
+        uint16_t *dst = a.qrot + head * 2 * D + 32 * g4;
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) {
+            *reinterpret_cast<uint4 *>(dst + 8 * kc) = hi[kc];
+            *reinterpret_cast<uint4 *>(dst + D + 8 * kc) = lo[kc];
+        }
+    }
+}
+
 // Scoring pass.  Grid (ceil(nb / (4 * BPW)), Hkv, B), 4 waves; wave w of
 // workgroup x scores blocks (4x + w) * BPW .. +BPW - 1.  Per 16-token tile,
 // Q.K^T on v_mfma_f32_16x16x32_f16 with the tokens on M and the heads on N:
@@ -49,16 +74,17 @@ __global__ __launch_bounds__(256) void score_int8_kernel(AdaptArgs a) {
     const int64_t kvh = blockIdx.y, b = blockIdx.z;
     const int64_t bh = b * a.hkv + kvh;
     const int g = a.g;
-    uint4 qb[4];
+    // the query (plain codec) or the rotated query's hi and lo parts
+    uint4 qb[4], qrl[4];
     {
-        const uint16_t *qh = a.q + ((b * a.hq) + kvh * g + (m < g ? m : 0)) * D + 32 * g4;
+        const int64_t head = (b * a.hq) + kvh * g + (m < g ? m : 0);
+        const uint16_t *qh = ROT ? a.qrot + head * 2 * D + 32 * g4 : a.q + head * D + 32 * g4;
 #pragma unroll
-        for (int kc = 0; kc < 4; ++kc)
+        for (int kc = 0; kc < 4; ++kc) {
             qb[kc] = m < g ? *reinterpret_cast<const uint4 *>(qh + 8 * kc) : make_uint4(0u, 0u, 0u, 0u);
+            if (ROT) qrl[kc] = m < g ? *reinterpret_cast<const uint4 *>(qh + D + 8 * kc) : make_uint4(0u, 0u, 0u, 0u);
+        }
     }
-    // rotated key codec: score the codes against the rotated query
-    uint4 qrl[4];
-    if (ROT) rotate_q(qb, lane, qb, qrl);
     const float sml2 = a.sm * 1.4426950408889634f;
     for (int r = 0; r < BPW; ++r) {
         const int64_t i = ((int64_t)blockIdx.x * 4 + wave) * BPW + r;
@@ -219,9 +245,10 @@ __global__ __launch_bounds__(256) void select_kernel(AdaptArgs a) {
 hipError_t launch_score(const AdaptArgs &a, int batch, hipStream_t s) {
     const unsigned gx = (unsigned)((a.nb + 4 * BPW - 1) / (4 * BPW));
     const dim3 grid(gx, (unsigned)a.hkv, (unsigned)batch);
-    if (a.key_rot)
+    if (a.key_rot) {
+        hipLaunchKernelGGL(rotate_query_kernel, dim3((unsigned)a.hkv, (unsigned)batch), dim3(64), 0, s, a);
         hipLaunchKernelGGL(score_int8_kernel<true>, grid, dim3(256), 0, s, a);
-    else
+    } else
         hipLaunchKernelGGL(score_int8_kernel<false>, grid, dim3(256), 0, s, a);
     return hipGetLastError();
 }

@@ -85,7 +85,7 @@ WsLayout ws_layout(const kvq_cache *c, int32_t g, int64_t splits) {
 // [phead uint8 x B*Hq*NBc] [promote uint8 x B*Hkv*NBc] [step statistics
 // float2 x B*Hkv*NBc*8*G], each padded to 256 B.
 struct AdaptLayout {
-    size_t lhat, phead, promote, step, total;
+    size_t lhat, phead, promote, step, qrot, total;
 };
 
 AdaptLayout adapt_layout(const kvq_cache *c, int32_t q_heads, size_t base) {
@@ -96,7 +96,8 @@ AdaptLayout adapt_layout(const kvq_cache *c, int32_t q_heads, size_t base) {
     w.phead = round_up(w.lhat + bq * nbc * sizeof(float), 256);
     w.promote = round_up(w.phead + bq * nbc, 256);
     w.step = round_up(w.promote + bh * nbc, 256);
-    w.total = w.step + bq * nbc * 8 * sizeof(float2);
+    w.qrot = round_up(w.step + bq * nbc * 8 * sizeof(float2), 256);
+    w.total = w.qrot + bq * 2 * kvq::D * sizeof(uint16_t);
     return w;
 }
 
@@ -398,6 +399,7 @@ kvq_status decode_impl(kvq_cache *c, const uint16_t *q, int32_t q_heads, float s
         aa.phead = reinterpret_cast<uint8_t *>((char *)workspace + al.phead);
         aa.promote = reinterpret_cast<uint8_t *>((char *)workspace + al.promote);
         aa.kstar = ad->kstar;
+        aa.qrot = reinterpret_cast<uint16_t *>((char *)workspace + al.qrot);
         aa.cap = c->capacity;
         aa.length = length;
         aa.nbc = nbc;

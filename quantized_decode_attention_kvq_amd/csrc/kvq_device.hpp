@@ -30,18 +30,56 @@ __device__ __forceinline__ double shfl_xor_d(double v, int mask) {
     return __shfl_xor(v, mask);
 }
 
-// Sum of 128 fp64 terms held as 8 contiguous terms per lane in 16 consecutive
-// lanes (lane l of the group holds terms 8l .. 8l+7).  Fixed pairing: within
-// the lane strides 1, 2, 4; across lanes xor 8, 4, 2, 1 (term strides 64, 32,
-// 16, 8).  Every lane of the group returns the same value.  IEEE addition is
-// commutative, so lane l and lane l^m form the same sum.
+// The value of lane l ^ M (M = 1, 2, 4 or 8) of the same 16-lane DPP row, on
+// VALU lane moves (no LDS round trip): xor 1 and xor 2 are quad
+// permutations, xor 8 the rotation of the row by 8; xor 4 is a shift left by
+// 4 (lane l reads l + 4) written to the lanes with bit 2 clear (bank mask
+// 0x5: lanes 0-3 and 8-11 of the row), then a shift right by 4 written to
+// the others (0xA).  Every lane of the row must be active.
+template <int M>
+__device__ __forceinline__ int xor16(int v) {
+    static_assert(M == 1 || M == 2 || M == 4 || M == 8, "lane xor inside a row of 16");
+    if constexpr (M == 1) {
+        return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+    } else if constexpr (M == 2) {
+        return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+    } else if constexpr (M == 8) {
+        return __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, false);  // row_ror:8
+    } else {
+        const int t = __builtin_amdgcn_update_dpp(v, v, 0x104, 0xF, 0x5, false);  // row_shl:4
+        return __builtin_amdgcn_update_dpp(t, v, 0x114, 0xF, 0xA, false);        // row_shr:4
+    }
+}
+// m is a compile-time constant once the caller's loop is unrolled.
+__device__ __forceinline__ uint32_t xor16u(uint32_t v, int m) {
+    const int x = (int)v;
+    return (uint32_t)(m == 1 ? xor16<1>(x) : m == 2 ? xor16<2>(x) : m == 4 ? xor16<4>(x) : xor16<8>(x));
+}
+__device__ __forceinline__ float xor16f(float v, int m) { return __uint_as_float(xor16u(__float_as_uint(v), m)); }
+__device__ __forceinline__ double xor16d(double v, int m) {
+    const uint64_t b = (uint64_t)__double_as_longlong(v);
+    const uint64_t lo = xor16u((uint32_t)b, m), hi = xor16u((uint32_t)(b >> 32), m);
+    return __longlong_as_double((long long)((hi << 32) | lo));
+}
+
+// Sum of 128 fp64 terms held as 8 contiguous terms per lane in the 16 lanes
+// of a DPP row (lane l of the row holds terms 8l .. 8l+7).  Fixed pairing:
+// within the lane strides 1, 2, 4; across lanes xor 8, 4, 2, 1 (term strides
+// 64, 32, 16, 8).  Every lane of the row returns the same value.  IEEE
+// addition is commutative, so lane l and lane l^m form the same sum.
 __device__ __forceinline__ double tree128(const double x[8]) {
     double a = x[0] + x[1], b = x[2] + x[3], c = x[4] + x[5], d = x[6] + x[7];
     double s = (a + b) + (c + d);
-    s = s + shfl_xor_d(s, 8);
-    s = s + shfl_xor_d(s, 4);
-    s = s + shfl_xor_d(s, 2);
-    s = s + shfl_xor_d(s, 1);
+    s = s + xor16d(s, 8);
+    // lanes l and l^8 now agree, so the row rotation by 4 reads lane l^4's value
+    {
+        const uint64_t b = (uint64_t)__double_as_longlong(s);
+        const uint64_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)b, 0x124, 0xF, 0xF, false);
+        const uint64_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(b >> 32), 0x124, 0xF, 0xF, false);
+        s = s + __longlong_as_double((long long)((hi << 32) | lo));
+    }
+    s = s + xor16d(s, 2);
+    s = s + xor16d(s, 1);
     return s;
 }
 

@@ -88,6 +88,7 @@ struct AdaptArgs {
     uint8_t *phead;          // [B][Hq][nbc] 1: the head promotes the block's keys
     uint8_t *promote;        // [B][Hkv][nbc] bit 0 key, bit 1 value promotion (union over the group)
     int32_t *kstar;          // [B][Hq] blocks each head promotes, or null
+    uint16_t *qrot;          // [B][Hq][2][D] rotated query, fp16 hi and lo parts (rotated codec)
     int64_t cap, length, nbc, nb;
     int32_t hkv, hq, g;
     int32_t key_rot;         // KVQ_CODEC_ROTATE_K

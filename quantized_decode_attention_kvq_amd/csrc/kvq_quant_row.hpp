@@ -28,26 +28,55 @@ __device__ __forceinline__ float elem(const uint32_t w[4], int k) {
     return h2f((k & 1) ? (w[k >> 1] >> 16) : (w[k >> 1] & 0xFFFFu));
 }
 
-// round_half_even(x / s) clamped to [-lim, lim], for fp16 values x and s > 0,
-// with r ~ 1/s (any estimate within a few ulps) and hs = s/2.  The estimate
-// rint(x*r) is off by at most one, and only next to a half-integer; the
-// residual x - c*s is exact in fp32 (c*s has at most 19 significant bits, and
-// x and c*s lie on the grid of the smaller of their fp16 ulps whenever c is
-// nonzero), so comparing it with s/2 -- ties going to the even code --
-// corrects the estimate exactly.  r == 0 marks a zero scale.  Returns the
-// code; e receives x - c*s for the final (clamped) code, also exact.
-__device__ __forceinline__ int quant_code(float x, float s, float r, float hs, int lim, float &e) {
-    float c = __builtin_rintf(x * r);
-    const float d = __builtin_fmaf(-c, s, x);
-    const bool odd = ((int)c & 1) != 0;
-    if (d > hs || (d == hs && odd))
-        c += 1.0f;
-    else if (d < -hs || (d == -hs && odd))
-        c -= 1.0f;
-    c = __builtin_fminf(__builtin_fmaxf(c, (float)-lim), (float)lim);
-    c = r == 0.0f ? 0.0f : c;  // zero scale (also rows holding Inf/NaN): code 0
-    e = __builtin_fmaf(-c, s, x);
-    return (int)c;
+// Codes by one rounding: fma(x, r, RND_BIAS) = RND_BIAS + rint(x * r) for
+// |x * r| < 2^22 (the sum's ulp is 1 and RND_BIAS is even, so ties go to the
+// even integer), and the low byte of the sum's bit pattern is that integer
+// mod 256.  Clamping the biased value to RND_BIAS +- lim clamps the code.
+constexpr float RND_BIAS = 12582912.0f;  // 1.5 * 2^23
+
+// Biased code of x for scale s > 0 with r ~ 1/s within 2 ulps (v_rcp_f32).
+// A quotient of two fp16 values that is not a half-integer lies at least
+// 2^-14 from one (write x = X 2^a, s = S 2^b with 11-bit X, S: the distance
+// is a nonzero multiple of 2^min(a,b) / (2 s), and near a half-integer x/s >=
+// 1/4 bounds 2^(a-b) from below), while x*r is within 191 * 2^-22 < 2^-14 of
+// x/s (|x/s| <= 190.5 for every scale of the codec, subnormal ones included).
+// So the biased code is round_half_even(x/s), clamped, except at an exact
+// tie, where it may be the odd neighbour (fix_ties).  r = 0 (a zero scale)
+// gives code 0 for finite x.
+__device__ __forceinline__ float code_biased(float x, float r, float lim) {
+    const float cb = __builtin_fmaf(x, r, RND_BIAS);
+    return __builtin_fminf(__builtin_fmaxf(cb, RND_BIAS - lim), RND_BIAS + lim);
+}
+
+// Residual x - c*s of a biased code: exact in fp32 (c*s has at most 19
+// significant bits, and x and c*s lie on the grid of the smaller of their
+// fp16 ulps whenever c is nonzero).
+__device__ __forceinline__ float code_residual(float x, float cb, float s) {
+    return __builtin_fmaf(-(cb - RND_BIAS), s, x);
+}
+
+// Low bytes of four codes, in order, as one dword (byte permutes).
+__device__ __forceinline__ uint32_t pack_bytes(int c0, int c1, int c2, int c3) {
+    const uint32_t lo = __builtin_amdgcn_perm((uint32_t)c1, (uint32_t)c0, 0x0c0c0400u);
+    const uint32_t hi = __builtin_amdgcn_perm((uint32_t)c3, (uint32_t)c2, 0x0c0c0400u);
+    return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+}
+
+// Ties: where |x - c*s| = s/2 exactly and c is odd, the even neighbour c +-
+// 1 (toward x) is the rounded code, clamped again.  |e| is the same for both
+// neighbours, so the residual statistics need no change.  `lane_tie` flags a
+// lane whose largest |e| reached s/2 (ties, and clamped quotients beyond lim +
+// 1/2); the pass runs only when some lane of the wave is flagged.
+__device__ __forceinline__ void fix_ties(const uint32_t w[4], float cb[8], float s, float hs, float lim,
+                                         bool lane_tie) {
+    if (__builtin_amdgcn_ballot_w64(lane_tie) == 0) return;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const float e = code_residual(elem(w, k), cb[k], s);
+        if (__builtin_fabsf(e) == hs && (__float_as_uint(cb[k]) & 1u) != 0)
+            cb[k] = __builtin_fminf(__builtin_fmaxf(cb[k] + __builtin_copysignf(1.0f, e), RND_BIAS - lim),
+                                    RND_BIAS + lim);
+    }
 }
 
 // One token row quantized by a group of 16 lanes (lane16 holds channels
@@ -55,7 +84,7 @@ __device__ __forceinline__ int quant_code(float x, float s, float r, float hs, i
 // lane returns its 8 key codes (bytes), its 8 value codes (low nibble of each
 // byte), the row's key scale and key error, its 32-channel group's value
 // scale, and the row's value error (max over the four groups).  Uses
-// xor-shuffles within the 16-lane group only.
+// lane exchanges within the 16-lane group (one DPP row) only.
 struct RowQuant {
     uint32_t kc[2], vc[2];
     uint32_t ksb, vsb;
@@ -78,11 +107,13 @@ __device__ __forceinline__ RowIn load_row16(const uint16_t *k16row, const uint16
 // over the 16-lane group, in fp64 where every butterfly is exact (k's values
 // are multiples of 2^-24 below 2^16, so the sums fit 47 bits and their order
 // does not matter): strides 1, 2, 4 in the lane, 8 .. 64 across lanes xor
-// 1 .. 8.  Then the key codec on u with the quotient u / s in fp64 (u is a
-// multiple of 2^-28, so a quotient that is not a half-integer lies at least
-// 2^-43 from one, beyond its fp64 rounding: rint gives the exact round half
-// to even), e = u - s c exact, and the error sqrt(2 * T128(e^2)) with the
-// squares rounded to fp64 (the keys read back are H (s c) / 8).
+// 1 .. 8.  Then the key codec on u: the estimate rint(u * RN(1/s)) is within
+// one of round_half_even(u / s) (its error is below 2^-44 for |u / s| < 256),
+// and the exact residual d = u - c s (u is a multiple of 2^-28 below 2^20,
+// s c has at most 19 significant bits) moves it one step toward d when |d| >
+// s/2, or when |d| = s/2 and c is odd.  e = u - s c is exact, and the error
+// is sqrt(2 * T128(e^2)) with the squares rounded to fp64 (the keys read back
+// are H (s c) / 8).
 __device__ __forceinline__ void quant_key_rot16(const uint32_t kw[4], bool knonfin, int lane16, uint32_t kc[2],
                                                 uint32_t &ksb, float &kerr) {
     double u[8];
@@ -97,14 +128,12 @@ __device__ __forceinline__ void quant_key_rot16(const uint32_t kw[4], bool knonf
                 u[j] = x + y;
                 u[j + h] = x - y;
             }
+    // lane with bit mk clear: u + partner; set: partner - u (exact either way)
 #pragma unroll
     for (int mk = 1; mk < 16; mk <<= 1) {
-        const bool hi = (lane16 & mk) != 0;
+        const double sg = (lane16 & mk) ? -1.0 : 1.0;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const double o = shfl_xor_d(u[k], mk);
-            u[k] = hi ? o - u[k] : u[k] + o;
-        }
+        for (int k = 0; k < 8; ++k) u[k] = __builtin_fma(u[k], sg, xor16d(u[k], mk));
     }
     double am = 0.0;
 #pragma unroll
@@ -112,38 +141,59 @@ __device__ __forceinline__ void quant_key_rot16(const uint32_t kw[4], bool knonf
         u[k] = u[k] * 0.0625;
         am = fmax(am, fabs(u[k]));
     }
+    // the row max as f32 (rounding is monotonic, so it commutes with the max)
+    float amf = (float)am;
 #pragma unroll
-    for (int mk = 1; mk < 16; mk <<= 1) am = fmax(am, shfl_xor_d(am, mk));
-    ksb = knonfin ? 0u : f2h_rn(__fdiv_rn((float)am, 127.0f));
+    for (int mk = 1; mk < 16; mk <<= 1) amf = fmaxf(amf, xor16f(amf, mk));
+    ksb = knonfin ? 0u : f2h_rn(__fdiv_rn(amf, 127.0f));
     const double s = (double)h2f(ksb);
-    kc[0] = kc[1] = 0u;
+    const double rs = s != 0.0 ? 1.0 / s : 0.0, hs = 0.5 * s;
     double sq[8];
+    int cc[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-        int c = 0;
-        if (s != 0.0) {
-            const double qv = __builtin_rint(u[k] / s);
-            c = (int)(qv > 127.0 ? 127.0 : (qv < -127.0 ? -127.0 : qv));
-        }
-        const double e = u[k] - s * (double)c;  // s * c exact: no rounding to fuse
+        double c = __builtin_rint(u[k] * rs);
+        const double d = __builtin_fma(-c, s, u[k]);
+        const double ad = __builtin_fabs(d);
+        const bool odd = (((int)c) & 1) != 0;
+        c = (ad > hs || (ad == hs && odd)) ? c + __builtin_copysign(1.0, d) : c;
+        c = __builtin_fmin(__builtin_fmax(c, -127.0), 127.0);
+        c = s != 0.0 ? c : 0.0;
+        const double e = __builtin_fma(-c, s, u[k]);  // exact
         sq[k] = __dmul_rn(e, e);
-        kc[k >> 2] |= ((uint32_t)c & 0xFFu) << (8 * (k & 3));
+        cc[k] = (int)c;
     }
+    kc[0] = pack_bytes(cc[0], cc[1], cc[2], cc[3]);
+    kc[1] = pack_bytes(cc[4], cc[5], cc[6], cc[7]);
     const double ss = tree128(sq);
     kerr = knonfin ? __builtin_huge_valf() : (float)__dsqrt_rn(2.0 * ss);
 }
 
-// rot: the key row uses the Hadamard-rotated codec (KVQ_CODEC_ROTATE_K).
+// Max over the 16 lanes of a DPP row, in every lane: xor 1 and xor 2 make
+// each quad uniform, then the row rotations by 4 and 8 bring in the other
+// three quads.
+__device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
+    v = umax(v, xor16u(v, 1));
+    v = umax(v, xor16u(v, 2));
+    v = umax(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x124, 0xF, 0xF, false));  // row_ror:4
+    v = umax(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false));  // row_ror:8
+    return v;
+}
+// The same for non-negative floats (+inf included), whose bit patterns order
+// like their values.
+__device__ __forceinline__ float row16_max_nonneg(float v) {
+    return __uint_as_float(row16_max_u32(__float_as_uint(v)));
+}
+
+// One token row.  rot: the key row uses the Hadamard-rotated codec
+// (KVQ_CODEC_ROTATE_K).  A row or value group holding Inf or NaN gets scale 0,
+// codes 0 and error +inf.
 __device__ __forceinline__ RowQuant quant_row16(const RowIn &in, bool rot, int lane16) {
     RowQuant o;
     // ---------------- key row: int8 per token, scale absmax/127
     const uint4 kr = in.k;
     const uint32_t kw[4] = {kr.x, kr.y, kr.z, kr.w};
-    uint32_t am = absmax_bits(kw);
-    am = umax(am, __shfl_xor(am, 1));
-    am = umax(am, __shfl_xor(am, 2));
-    am = umax(am, __shfl_xor(am, 4));
-    am = umax(am, __shfl_xor(am, 8));
+    const uint32_t am = row16_max_u32(absmax_bits(kw));
     const bool knonfin = am >= 0x7C00u;
     uint32_t kc[2] = {0u, 0u};
     uint32_t ksb;
@@ -153,18 +203,27 @@ __device__ __forceinline__ RowQuant quant_row16(const RowIn &in, bool rot, int l
     } else {
         ksb = knonfin ? 0u : f2h_rn(__fdiv_rn(h2f(am), 127.0f));
         const float ks = h2f(ksb);
-        // a zero scale (tiny, all-zero or non-finite row) gives codes 0
+        // a zero scale (tiny or all-zero row) gives codes 0
         const float kr_ = ks != 0.0f ? __builtin_amdgcn_rcpf(ks) : 0.0f;
         const float khs = ks != 0.0f ? 0.5f * ks : __builtin_huge_valf();
         double sq[8];
+        float cb[8];
+        float emax = 0.0f;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             const float x = elem(kw, k);
-            float e;
-            const int c = quant_code(x, ks, kr_, khs, 127, e);
+            cb[k] = code_biased(x, kr_, 127.0f);
+            const float e = code_residual(x, cb[k], ks);
+            emax = __builtin_fmaxf(emax, __builtin_fabsf(e));
             sq[k] = sq64(e);
-            kc[k >> 2] |= ((uint32_t)c & 0xFFu) << (8 * (k & 3));
         }
+        fix_ties(kw, cb, ks, khs, 127.0f, emax >= khs);
+        if (__builtin_amdgcn_ballot_w64(knonfin) != 0) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) cb[k] = knonfin ? RND_BIAS : cb[k];
+        }
+        kc[0] = pack_bytes(__float_as_int(cb[0]), __float_as_int(cb[1]), __float_as_int(cb[2]), __float_as_int(cb[3]));
+        kc[1] = pack_bytes(__float_as_int(cb[4]), __float_as_int(cb[5]), __float_as_int(cb[6]), __float_as_int(cb[7]));
         const double ss = tree128(sq);
         kerr = knonfin ? __builtin_huge_valf() : (float)__dsqrt_rn(ss);
     }
@@ -173,34 +232,35 @@ __device__ __forceinline__ RowQuant quant_row16(const RowIn &in, bool rot, int l
     const uint4 vr = in.v;
     const uint32_t vw[4] = {vr.x, vr.y, vr.z, vr.w};
     uint32_t vm = absmax_bits(vw);
-    vm = umax(vm, __shfl_xor(vm, 1));
-    vm = umax(vm, __shfl_xor(vm, 2));
+    vm = umax(vm, xor16u(vm, 1));
+    vm = umax(vm, xor16u(vm, 2));
     const bool vnonfin = vm >= 0x7C00u;
     const uint32_t vsb = vnonfin ? 0u : f2h_rn(__fdiv_rn(h2f(vm), 7.0f));
     const float vs = h2f(vsb);
     const float vr_ = vs != 0.0f ? __builtin_amdgcn_rcpf(vs) : 0.0f;
     const float vhs = vs != 0.0f ? 0.5f * vs : __builtin_huge_valf();
-    uint32_t vc[2] = {0u, 0u};
-    float verr = 0.0f;
+    float cv[8];
+    float verr = 0.0f;  // max |e| over the lane's channels
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
         const float x = elem(vw, k);
-        float e;
-        const int c = quant_code(x, vs, vr_, vhs, 7, e);
-        e = __builtin_fabsf(e);
-        verr = verr > e ? verr : e;
-        vc[k >> 2] |= ((uint32_t)c & 0x0Fu) << (8 * (k & 3));
+        cv[k] = code_biased(x, vr_, 7.0f);
+        verr = __builtin_fmaxf(verr, __builtin_fabsf(code_residual(x, cv[k], vs)));
     }
+    fix_ties(vw, cv, vs, vhs, 7.0f, verr >= vhs);
+    if (__builtin_amdgcn_ballot_w64(vnonfin) != 0) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) cv[k] = vnonfin ? RND_BIAS : cv[k];
+    }
+    const uint32_t vc0 = pack_bytes(__float_as_int(cv[0]), __float_as_int(cv[1]), __float_as_int(cv[2]), __float_as_int(cv[3]));
+    const uint32_t vc1 = pack_bytes(__float_as_int(cv[4]), __float_as_int(cv[5]), __float_as_int(cv[6]), __float_as_int(cv[7]));
     verr = vnonfin ? __builtin_huge_valf() : verr;
-    verr = fmaxf(verr, __shfl_xor(verr, 1));
-    verr = fmaxf(verr, __shfl_xor(verr, 2));
-    verr = fmaxf(verr, __shfl_xor(verr, 4));  // row: max over the 4 groups
-    verr = fmaxf(verr, __shfl_xor(verr, 8));
+    verr = row16_max_nonneg(verr);  // row: max over the 4 groups
 
     o.kc[0] = kc[0];
     o.kc[1] = kc[1];
-    o.vc[0] = vc[0];
-    o.vc[1] = vc[1];
+    o.vc[0] = vc0 & 0x0F0F0F0Fu;
+    o.vc[1] = vc1 & 0x0F0F0F0Fu;
     o.ksb = ksb;
     o.vsb = vsb;
     o.kerr = kerr;

@@ -8,8 +8,10 @@
 // (batch, KV head), so a block's codes and statistics have a single writer and
 // appends of any size compose bit-exactly.  Each token row (128 fp16 = 256 B)
 // is handled by 16 lanes that each load 16 B (8 channels); a wave covers 4
-// rows per pass, the workgroup 16.  Reductions inside a row are xor-shuffles
-// within the 16-lane group: absmax over 16 lanes for the key scale, over 4
+// rows per pass, the workgroup 16, and all four rows of a group are loaded
+// before the first is quantized.  Reductions inside a row are lane exchanges
+// within the 16-lane group (a DPP row, VALU moves with no LDS round trip):
+// absmax over 16 lanes for the key scale, over 4
 // lanes for a 32-channel value group, and the fixed fp64 tree for ||k - k^||.
 // Value nibbles are staged as bytes in LDS and packed channel-major on the way
 // out; key codes go straight from registers to HBM (128 B per row, coalesced).
@@ -18,6 +20,7 @@
 
 namespace kvq {
 
+template <bool ROT>
 __global__ __launch_bounds__(256) void quantize_append_kernel(AppendArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t vtile[BLK][D];  // new value codes (low nibble), [token][channel]
     __shared__ float red[2][4];
@@ -34,16 +37,27 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(AppendArgs a) {
 
     float kmax = 0.0f, vmax = 0.0f;
 
-    for (int r = row0; r < BLK; r += 16) {
+    // the group's four rows are loaded before any is quantized, so that four
+    // loads per lane are in flight; rows outside the appended range are
+    // neither read nor written (a one-token append reads one row, also when
+    // tier 2 is host memory).  The range test is uniform in the 16-lane group,
+    // so the group's shuffles only ever involve active lanes.
+    RowIn rin[BLK / 16];
+#pragma unroll
+    for (int i = 0; i < BLK / 16; ++i) {
+        const int64_t t = t_first + row0 + 16 * i;
+        rin[i].k = rin[i].v = make_uint4(0u, 0u, 0u, 0u);
+        if (t >= t_begin && t < t_end)
+            rin[i] = load_row16(a.c.k16 + (row_base + t) * D, a.c.v16 + (row_base + t) * D, lane16);
+    }
+#pragma unroll
+    for (int i = 0; i < BLK / 16; ++i) {
+        const int r = row0 + 16 * i;
         const int64_t t = t_first + r;
-        // rows outside the appended range are neither read nor written; the
-        // test is uniform in the 16-lane group, so the group's shuffles below
-        // only ever involve active lanes
         if (t < t_begin || t >= t_end) continue;
         const int64_t roff = (row_base + t) * D + 8 * lane16;
 
-        const RowQuant rq = quant_row16(a.c.k16 + (row_base + t) * D, a.c.v16 + (row_base + t) * D, lane16,
-                                        a.key_rot != 0);
+        const RowQuant rq = quant_row16(rin[i], ROT, lane16);
         const uint32_t kc[2] = {rq.kc[0], rq.kc[1]}, vc[2] = {rq.vc[0], rq.vc[1]};
         const uint32_t ksb = rq.ksb, vsb = rq.vsb;
         const float kerr = rq.kerr, verr = rq.verr;
@@ -124,7 +138,10 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(AppendArgs a) {
 
 hipError_t launch_append(const AppendArgs &a, int batch, int64_t nblk, hipStream_t s) {
     dim3 grid((unsigned)nblk, (unsigned)a.hkv, (unsigned)batch);
-    hipLaunchKernelGGL(quantize_append_kernel, grid, dim3(256), 0, s, a);
+    if (a.key_rot)
+        hipLaunchKernelGGL(quantize_append_kernel<true>, grid, dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL(quantize_append_kernel<false>, grid, dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
