@@ -268,6 +268,127 @@ __device__ __forceinline__ RowQuant quant_row16(const RowIn &in, bool rot, int l
     return o;
 }
 
+// ---------------------------------------------------------------------------
+// One token row quantized by the 4 lanes of a quad (plain codec), for bulk
+// appends: four times the channels per lane of quant_row16, so the per-row
+// work (absmax, scales, the fp64 tree's tail, the square root) is shared by
+// 32 channels instead of 8.  Lane j of the quad holds key channels
+// 8j + 32i .. +7 (i = 0..3: the 8-channel chunks j, j+4, j+8, j+12, so that
+// the pinned fp64 tree pairs chunks c and c^8, then c^4, inside the lane, and
+// c^2, c^1 across it, as tree128 does) and value channels 32j .. 32j+31 (the
+// lane's own value group).  Same bytes as quant_row16.
+struct Row4In {
+    uint4 k[4], v[4];
+};
+// Scales and errors of a row; the codes go straight to memory.
+struct Row4Quant {
+    uint32_t ksb, vsb;
+    float kerr, verr;
+};
+
+__device__ __forceinline__ Row4In load_row4(const uint16_t *k16row, const uint16_t *v16row, int j) {
+    Row4In r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        r.k[i] = *reinterpret_cast<const uint4 *>(k16row + 8 * j + 32 * i);
+        r.v[i] = *reinterpret_cast<const uint4 *>(v16row + 32 * j + 8 * i);
+    }
+    return r;
+}
+
+// absmax_bits over the 32 fp16 values of four uint4, on packed 16-bit maxima.
+typedef unsigned short ushort2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t absmax_bits32(const uint4 (&q)[4]) {
+    ushort2_t m = {0, 0};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t w[4] = {q[i].x, q[i].y, q[i].z, q[i].w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            m = __builtin_elementwise_max(m, __builtin_bit_cast(ushort2_t, w[k] & 0x7FFF7FFFu));
+    }
+    return umax(m[0], m[1]);
+}
+
+// kdst: the row's key codes + 8j (chunk i at kdst + 32i); vdst: 32 bytes for
+// the value group's codes (low nibbles, channel order).
+__device__ __forceinline__ Row4Quant quant_row4(const Row4In &in, int8_t *kdst, uint8_t *vdst) {
+    Row4Quant o;
+    // ---------------- key row: int8 per token, scale absmax/127
+    uint32_t am = absmax_bits32(in.k);
+    am = umax(am, xor16u(am, 1));
+    am = umax(am, xor16u(am, 2));
+    const bool knonfin = am >= 0x7C00u;
+    o.ksb = knonfin ? 0u : f2h_rn(__fdiv_rn(h2f(am), 127.0f));
+    const float ks = h2f(o.ksb);
+    const float kr_ = ks != 0.0f ? __builtin_amdgcn_rcpf(ks) : 0.0f;
+    const float khs = ks != 0.0f ? 0.5f * ks : __builtin_huge_valf();
+    double part[4];  // fp64 sum of the squared residuals of chunk i (levels 1-3 of the tree)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t w[4] = {in.k[i].x, in.k[i].y, in.k[i].z, in.k[i].w};
+        float cb[8];
+        double sq[8];
+        float emax = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const float x = elem(w, k);
+            cb[k] = code_biased(x, kr_, 127.0f);
+            const float e = code_residual(x, cb[k], ks);
+            emax = __builtin_fmaxf(emax, __builtin_fabsf(e));
+            sq[k] = sq64(e);
+        }
+        fix_ties(w, cb, ks, khs, 127.0f, emax >= khs);
+        const uint32_t c0 = pack_bytes(__float_as_int(cb[0]), __float_as_int(cb[1]), __float_as_int(cb[2]),
+                                       __float_as_int(cb[3]));
+        const uint32_t c1 = pack_bytes(__float_as_int(cb[4]), __float_as_int(cb[5]), __float_as_int(cb[6]),
+                                       __float_as_int(cb[7]));
+        // a row holding Inf/NaN: codes 0
+        *reinterpret_cast<uint2 *>(kdst + 32 * i) = knonfin ? make_uint2(0u, 0u) : make_uint2(c0, c1);
+        part[i] = ((sq[0] + sq[1]) + (sq[2] + sq[3])) + ((sq[4] + sq[5]) + (sq[6] + sq[7]));
+    }
+    // chunks c + c^8 (i, i + 2), then + c^4 (i + 1), then across the quad
+    double ss = (part[0] + part[2]) + (part[1] + part[3]);
+    ss = ss + xor16d(ss, 2);
+    ss = ss + xor16d(ss, 1);
+    o.kerr = knonfin ? __builtin_huge_valf() : (float)__dsqrt_rn(ss);
+
+    // ---------------- value group: int4, scale absmax/7
+    const uint32_t vm = absmax_bits32(in.v);
+    const bool vnonfin = vm >= 0x7C00u;
+    o.vsb = vnonfin ? 0u : f2h_rn(__fdiv_rn(h2f(vm), 7.0f));
+    const float vs = h2f(o.vsb);
+    const float vr_ = vs != 0.0f ? __builtin_amdgcn_rcpf(vs) : 0.0f;
+    const float vhs = vs != 0.0f ? 0.5f * vs : __builtin_huge_valf();
+    float verr = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t w[4] = {in.v[i].x, in.v[i].y, in.v[i].z, in.v[i].w};
+        float cb[8];
+        float emax = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const float x = elem(w, k);
+            cb[k] = code_biased(x, vr_, 7.0f);
+            emax = __builtin_fmaxf(emax, __builtin_fabsf(code_residual(x, cb[k], vs)));
+        }
+        fix_ties(w, cb, vs, vhs, 7.0f, emax >= vhs);
+        verr = __builtin_fmaxf(verr, emax);
+        const uint32_t c0 = pack_bytes(__float_as_int(cb[0]), __float_as_int(cb[1]), __float_as_int(cb[2]),
+                                       __float_as_int(cb[3]));
+        const uint32_t c1 = pack_bytes(__float_as_int(cb[4]), __float_as_int(cb[5]), __float_as_int(cb[6]),
+                                       __float_as_int(cb[7]));
+        *reinterpret_cast<uint2 *>(vdst + 8 * i) =
+            vnonfin ? make_uint2(0u, 0u) : make_uint2(c0 & 0x0F0F0F0Fu, c1 & 0x0F0F0F0Fu);
+    }
+    // row: max over the quad's four groups (non-negative: compare bit patterns)
+    uint32_t vb = vnonfin ? 0x7F800000u : __float_as_uint(verr);
+    vb = umax(vb, xor16u(vb, 1));
+    vb = umax(vb, xor16u(vb, 2));
+    o.verr = __uint_as_float(vb);
+    return o;
+}
+
 __device__ __forceinline__ RowQuant quant_row16(const uint16_t *k16row, const uint16_t *v16row, int lane16,
                                                 bool rot) {
     return quant_row16(load_row16(k16row, v16row, lane16), rot, lane16);
