@@ -105,6 +105,32 @@ __device__ __forceinline__ float sum_across_rows(float v) {
     return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
 }
 
+// The sum of a double with its value in lane l ^ 32 (X32) or l ^ 16, by the
+// row-swap permutes: the swap of each half with itself returns the lane's own
+// word and its partner's, and addition is commutative.
+template <bool X32>
+__device__ __forceinline__ double add_partner_d(double v) {
+    const uint64_t b = (uint64_t)__double_as_longlong(v);
+    const uint32_t lo = (uint32_t)b, hi = (uint32_t)(b >> 32);
+    const auto rl = X32 ? __builtin_amdgcn_permlane32_swap(lo, lo, false, false)
+                        : __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+    const auto rh = X32 ? __builtin_amdgcn_permlane32_swap(hi, hi, false, false)
+                        : __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+    const double d0 = __longlong_as_double((long long)(((uint64_t)rh[0] << 32) | rl[0]));
+    const double d1 = __longlong_as_double((long long)(((uint64_t)rh[1] << 32) | rl[1]));
+    return d0 + d1;
+}
+
+// Unsigned max over the wave, in every lane (DPP within the rows, then the
+// row-swap permutes).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = row16_max_u32(v);
+    const auto r16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    v = umax(r16[0], r16[1]);
+    const auto r32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return umax(r32[0], r32[1]);
+}
+
 // Row (token) of the half held by MFMA row m of Q.K^T subtile e.
 __device__ __forceinline__ int half_row(int e, int m) { return 8 * (m >> 2) + 4 * e + (m & 3); }
 
@@ -613,14 +639,14 @@ __device__ __forceinline__ void decode_group(const DecodeArgs &a, const int spli
             run[s] = ((t[0] + t[1]) + (t[2] + t[3])) + ((t[4] + t[5]) + (t[6] + t[7]));
         }
 #pragma unroll
-        for (int s = 0; s < 4; ++s) run[s] = run[s] + shfl_xor_d(run[s], 32);
+        for (int s = 0; s < 4; ++s) run[s] = add_partner_d<true>(run[s]);
 #pragma unroll
-        for (int s = 0; s < 4; ++s) run[s] = run[s] + shfl_xor_d(run[s], 16);
-        float qh = (float)__dsqrt_rn((run[0] + run[2]) + (run[1] + run[3]));
-        // group norm: max over the heads (lanes m; heads >= G have norm 0)
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) qh = max_keep_nan(qh, __shfl_xor(qh, o));
-        qn = qh;
+        for (int s = 0; s < 4; ++s) run[s] = add_partner_d<false>(run[s]);
+        const float qh = (float)__dsqrt_rn((run[0] + run[2]) + (run[1] + run[3]));
+        // group norm: max over the heads (lanes m; heads >= G have norm 0),
+        // keeping NaN: non-negative floats, +Inf and NaN order like their
+        // bit patterns
+        qn = __uint_as_float(row16_max_u32(__float_as_uint(qh)));
     }
     // rotated key codec: the query rotated the same way, for the code tiles
     uint4 qrh[4], qrl[4];
@@ -677,11 +703,9 @@ __device__ __forceinline__ void decode_group(const DecodeArgs &a, const int spli
             if (tid + r * NT < nb) put(tid + r * NT, ke[r], ve[r]);
         for (int i = tid + PF * NT; i < nb; i += NT) put(i, a.c.k_err[bh * a.nbc + i], a.c.v_err[bh * a.nbc + i]);
         if (CERT) {
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                kmx = fmaxf(kmx, __shfl_xor(kmx, o));
-                vmx = fmaxf(vmx, __shfl_xor(vmx, o));
-            }
+            // non-negative errors (+Inf included): max of the bit patterns
+            kmx = __uint_as_float(wave_max_u32(__float_as_uint(kmx)));
+            vmx = __uint_as_float(wave_max_u32(__float_as_uint(vmx)));
             if (lane == 0) {
                 kvw[wave] = kmx;
                 kvw[NW + wave] = vmx;
@@ -749,12 +773,7 @@ __device__ __forceinline__ void decode_group(const DecodeArgs &a, const int spli
     const int i0 = tid * c < nb ? tid * c : nb, i1 = i0 + c < nb ? i0 + c : nb;
     int mysum = 0;
     for (int i = i0; i < i1; ++i) mysum += steps_of(maskb[i]);
-    int incl = mysum;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int v = __shfl_up(incl, o);
-        if (lane >= o) incl += v;
-    }
+    const int incl = wave_incl_scan_int(mysum);
     if (lane == 63) wsum_lds[wave] = incl;
     __syncthreads();
     int before = 0, total = 0;
@@ -918,9 +937,7 @@ __device__ __forceinline__ void decode_group(const DecodeArgs &a, const int spli
 
     // ---------------- merge waves, then splits
     // lane (n = m, r = g4) holds O^T[16mt + 4r + i][n] and a share of l
-    float l_run = ws.l_run;
-    l_run += __shfl_xor(l_run, 16);
-    l_run += __shfl_xor(l_run, 32);
+    const float l_run = sum_across_rows(ws.l_run);
     __syncthreads();  // every wave is done with the ring: reuse it for the wave merge
     float *wacc = reinterpret_cast<float *>(&ring[0][0][0]);
     if (m < g) {
@@ -936,15 +953,8 @@ __device__ __forceinline__ void decode_group(const DecodeArgs &a, const int spli
     float *we = reinterpret_cast<float *>(&ring[0][0][0] + NW * 16 * D * 4);  // [NW][16]
     uint32_t *wsa = reinterpret_cast<uint32_t *>(we + NW * 16);                // [NW][2]
     if (CERT) {
-        float e_run = ws.e_run;
-        e_run += __shfl_xor(e_run, 16);
-        e_run += __shfl_xor(e_run, 32);
-        uint32_t sm_ = ws.smax, am_ = ws.amax;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            sm_ = umax(sm_, (uint32_t)__shfl_xor((int)sm_, o));
-            am_ = umax(am_, (uint32_t)__shfl_xor((int)am_, o));
-        }
+        const float e_run = sum_across_rows(ws.e_run);
+        const uint32_t sm_ = wave_max_u32(ws.smax), am_ = wave_max_u32(ws.amax);
         if (m < g && g4 == 0) we[wave * 16 + m] = e_run;
         if (lane == 0) {
             wsa[2 * wave] = sm_;
