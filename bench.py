@@ -47,6 +47,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "decode_counters.json")
+APPEND_COUNTERS = os.path.join(ROOT, "profiles", "append_counters.json")
 
 
 def parse():
@@ -112,15 +113,16 @@ def append_bytes(B, Hkv, n=1):
     return B * Hkv * n * (512 + 128 + 2 + 64 + 8 + 8)
 
 
-def traffic_from_counters():
-    """HBM bytes per split-K launch (FETCH_SIZE + WRITE_SIZE, each scaled by
-    the same counter's reading on a plain 1 GiB copy) from the committed
+def traffic_from_counters(path=PROFILE_COUNTERS):
+    """HBM bytes per launch of the profiled kernel (the split-K decode, or
+    the bulk append for APPEND_COUNTERS): FETCH_SIZE + WRITE_SIZE, each scaled
+    by the same counter's reading on a plain 1 GiB copy, from the committed
     rocprofv3 counter runs, or None when they are absent or were taken on
     other kernel sources."""
-    if not os.path.exists(PROFILE_COUNTERS):
+    if not os.path.exists(path):
         return None
     try:
-        c = json.load(open(PROFILE_COUNTERS))
+        c = json.load(open(path))
         if c.get("kernel_source_hash") != kernel_source_hash():
             return None
         return float(c["hbm_bytes_per_launch"])
@@ -199,6 +201,12 @@ def bench_quantize(args, w):
     torch.cuda.synchronize()
     ms_step = (time.perf_counter() - t0) / args.steps * 1e3
     k_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+    traffic = traffic_from_counters(APPEND_COUNTERS) if not args.key_rotation else None
     gbs = nbytes / (ms_step * 1e-3) / 1e9
     kgbs = nbytes / (k_ms * 1e-3) / 1e9
     print(json.dumps({
@@ -212,7 +220,7 @@ def bench_quantize(args, w):
                    "bytes_per_step": nbytes, "key_codec": "rotate_k" if args.key_rotation else "plain",
                    "k_err_median": float(c.k_err.flatten()[: w.B * w.Hkv * ((w.T + 63) // 64)].median())},
         "roofline": {"kernel": "quantize_append_kernel", "bound": "hbm", "achieved": round(kgbs, 2),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(kgbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(kgbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "algorithmic_bytes_per_launch": nbytes, "mean_launch_ms": round(k_ms, 5)},
     }), flush=True)
 

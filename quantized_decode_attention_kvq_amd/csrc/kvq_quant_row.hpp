@@ -312,6 +312,11 @@ __device__ __forceinline__ uint32_t absmax_bits32(const uint4 (&q)[4]) {
 
 // kdst: the row's key codes + 8j (chunk i at kdst + 32i); vdst: 32 bytes for
 // the value group's codes (low nibbles, channel order).
+// ROT: the key row uses the Hadamard-rotated codec, u = H k / 16 as in
+// quant_key_rot16: butterflies at channel strides 1, 2, 4 inside each chunk,
+// 32 and 64 across the lane's chunks, 8 and 16 across the quad (lanes xor 1,
+// 2), all exact in fp64, then the same codes, scale and error.
+template <bool ROT>
 __device__ __forceinline__ Row4Quant quant_row4(const Row4In &in, int8_t *kdst, uint8_t *vdst) {
     Row4Quant o;
     // ---------------- key row: int8 per token, scale absmax/127
@@ -319,39 +324,121 @@ __device__ __forceinline__ Row4Quant quant_row4(const Row4In &in, int8_t *kdst, 
     am = umax(am, xor16u(am, 1));
     am = umax(am, xor16u(am, 2));
     const bool knonfin = am >= 0x7C00u;
-    o.ksb = knonfin ? 0u : f2h_rn(__fdiv_rn(h2f(am), 127.0f));
-    const float ks = h2f(o.ksb);
-    const float kr_ = ks != 0.0f ? __builtin_amdgcn_rcpf(ks) : 0.0f;
-    const float khs = ks != 0.0f ? 0.5f * ks : __builtin_huge_valf();
-    double part[4];  // fp64 sum of the squared residuals of chunk i (levels 1-3 of the tree)
+    if constexpr (ROT) {
+        const int j = __lane_id() & 3;
+        double u[4][8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t w[4] = {in.k[i].x, in.k[i].y, in.k[i].z, in.k[i].w};
-        float cb[8];
-        double sq[8];
-        float emax = 0.0f;
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t w[4] = {in.k[i].x, in.k[i].y, in.k[i].z, in.k[i].w};
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const float x = elem(w, k);
-            cb[k] = code_biased(x, kr_, 127.0f);
-            const float e = code_residual(x, cb[k], ks);
-            emax = __builtin_fmaxf(emax, __builtin_fabsf(e));
-            sq[k] = sq64(e);
+            for (int k = 0; k < 8; ++k) u[i][k] = (double)elem(w, k);
+#pragma unroll
+            for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+                    if (!(k & h)) {
+                        const double x = u[i][k], y = u[i][k + h];
+                        u[i][k] = x + y;
+                        u[i][k + h] = x - y;
+                    }
         }
-        fix_ties(w, cb, ks, khs, 127.0f, emax >= khs);
-        const uint32_t c0 = pack_bytes(__float_as_int(cb[0]), __float_as_int(cb[1]), __float_as_int(cb[2]),
-                                       __float_as_int(cb[3]));
-        const uint32_t c1 = pack_bytes(__float_as_int(cb[4]), __float_as_int(cb[5]), __float_as_int(cb[6]),
-                                       __float_as_int(cb[7]));
-        // a row holding Inf/NaN: codes 0
-        *reinterpret_cast<uint2 *>(kdst + 32 * i) = knonfin ? make_uint2(0u, 0u) : make_uint2(c0, c1);
-        part[i] = ((sq[0] + sq[1]) + (sq[2] + sq[3])) + ((sq[4] + sq[5]) + (sq[6] + sq[7]));
+#pragma unroll
+        for (int h = 1; h < 4; h <<= 1)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (!(i & h)) {
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) {
+                        const double x = u[i][k], y = u[i + h][k];
+                        u[i][k] = x + y;
+                        u[i + h][k] = x - y;
+                    }
+                }
+        // lane with bit mk clear: u + partner; set: partner - u
+#pragma unroll
+        for (int mk = 1; mk < 4; mk <<= 1) {
+            const double sg = (j & mk) ? -1.0 : 1.0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int k = 0; k < 8; ++k) u[i][k] = __builtin_fma(u[i][k], sg, xor16d(u[i][k], mk));
+        }
+        double amd = 0.0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                u[i][k] = u[i][k] * 0.0625;
+                amd = fmax(amd, fabs(u[i][k]));
+            }
+        // the row max as f32 (rounding is monotonic, so it commutes with the max)
+        uint32_t amb = __float_as_uint((float)amd);
+        amb = umax(amb, xor16u(amb, 1));
+        amb = umax(amb, xor16u(amb, 2));
+        o.ksb = knonfin ? 0u : f2h_rn(__fdiv_rn(__uint_as_float(amb), 127.0f));
+        const double s = (double)h2f(o.ksb);
+        const double rs = s != 0.0 ? 1.0 / s : 0.0, hs = 0.5 * s;
+        double part[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            double sq[8];
+            int cc[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                double c = __builtin_rint(u[i][k] * rs);
+                const double d = __builtin_fma(-c, s, u[i][k]);
+                const double ad = __builtin_fabs(d);
+                const bool odd = (((int)c) & 1) != 0;
+                c = (ad > hs || (ad == hs && odd)) ? c + __builtin_copysign(1.0, d) : c;
+                c = __builtin_fmin(__builtin_fmax(c, -127.0), 127.0);
+                c = s != 0.0 ? c : 0.0;
+                const double e = __builtin_fma(-c, s, u[i][k]);  // exact
+                sq[k] = __dmul_rn(e, e);
+                cc[k] = (int)c;
+            }
+            *reinterpret_cast<uint2 *>(kdst + 32 * i) =
+                make_uint2(pack_bytes(cc[0], cc[1], cc[2], cc[3]), pack_bytes(cc[4], cc[5], cc[6], cc[7]));
+            part[i] = ((sq[0] + sq[1]) + (sq[2] + sq[3])) + ((sq[4] + sq[5]) + (sq[6] + sq[7]));
+        }
+        double ss = (part[0] + part[2]) + (part[1] + part[3]);
+        ss = ss + xor16d(ss, 2);
+        ss = ss + xor16d(ss, 1);
+        o.kerr = knonfin ? __builtin_huge_valf() : (float)__dsqrt_rn(2.0 * ss);
+    } else {
+        o.ksb = knonfin ? 0u : f2h_rn(__fdiv_rn(h2f(am), 127.0f));
+        const float ks = h2f(o.ksb);
+        const float kr_ = ks != 0.0f ? __builtin_amdgcn_rcpf(ks) : 0.0f;
+        const float khs = ks != 0.0f ? 0.5f * ks : __builtin_huge_valf();
+        double part[4];  // fp64 sum of the squared residuals of chunk i (levels 1-3 of the tree)
+    #pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t w[4] = {in.k[i].x, in.k[i].y, in.k[i].z, in.k[i].w};
+            float cb[8];
+            double sq[8];
+            float emax = 0.0f;
+    #pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const float x = elem(w, k);
+                cb[k] = code_biased(x, kr_, 127.0f);
+                const float e = code_residual(x, cb[k], ks);
+                emax = __builtin_fmaxf(emax, __builtin_fabsf(e));
+                sq[k] = sq64(e);
+            }
+            fix_ties(w, cb, ks, khs, 127.0f, emax >= khs);
+            const uint32_t c0 = pack_bytes(__float_as_int(cb[0]), __float_as_int(cb[1]), __float_as_int(cb[2]),
+                                           __float_as_int(cb[3]));
+            const uint32_t c1 = pack_bytes(__float_as_int(cb[4]), __float_as_int(cb[5]), __float_as_int(cb[6]),
+                                           __float_as_int(cb[7]));
+            // a row holding Inf/NaN: codes 0
+            *reinterpret_cast<uint2 *>(kdst + 32 * i) = knonfin ? make_uint2(0u, 0u) : make_uint2(c0, c1);
+            part[i] = ((sq[0] + sq[1]) + (sq[2] + sq[3])) + ((sq[4] + sq[5]) + (sq[6] + sq[7]));
+        }
+        // chunks c + c^8 (i, i + 2), then + c^4 (i + 1), then across the quad
+        double ss = (part[0] + part[2]) + (part[1] + part[3]);
+        ss = ss + xor16d(ss, 2);
+        ss = ss + xor16d(ss, 1);
+        o.kerr = knonfin ? __builtin_huge_valf() : (float)__dsqrt_rn(ss);
     }
-    // chunks c + c^8 (i, i + 2), then + c^4 (i + 1), then across the quad
-    double ss = (part[0] + part[2]) + (part[1] + part[3]);
-    ss = ss + xor16d(ss, 2);
-    ss = ss + xor16d(ss, 1);
-    o.kerr = knonfin ? __builtin_huge_valf() : (float)__dsqrt_rn(ss);
 
     // ---------------- value group: int4, scale absmax/7
     const uint32_t vm = absmax_bits32(in.v);

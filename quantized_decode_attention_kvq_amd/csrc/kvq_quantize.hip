@@ -6,17 +6,17 @@
 //
 // One workgroup (256 threads = 4 waves) owns one 64-token block of one
 // (batch, KV head), so a block's codes and statistics have a single writer and
-// appends of any size compose bit-exactly.  The plain codec gives each token
-// row (128 fp16 = 256 B of keys, as much of values) to the 4 lanes of a quad,
-// 32 channels per lane and tensor, so the workgroup takes the whole block in
-// one pass and the per-row work (absmax, scale, the tail of the fp64 tree,
-// the square root) is spread over 32 channels; the rotated codec gives a row
-// to 16 lanes, whose butterflies span it.  Reductions inside a row are lane
-// exchanges on DPP moves (VALU, no LDS round trip).  This kernel is bound by
-// VALU issue rather than HBM at 16 lanes per row: the per-element work is one
-// biased fma for the code, a clamp, an exact residual and, for keys, the fp64
-// square.  Value nibbles are staged as bytes in LDS and packed channel-major
-// on the way out; key codes go straight from registers to HBM.
+// appends of any size compose bit-exactly.  Each token row (128 fp16 = 256 B
+// of keys, as much of values) goes to the 4 lanes of a quad, 32 channels per
+// lane and tensor, so the workgroup takes the whole block in one pass and the
+// per-row work (absmax, scale, the tail of the fp64 tree, the square root; the
+// Hadamard butterflies of the rotated codec) is spread over 32 channels.
+// Reductions inside a row are lane exchanges on DPP moves (VALU, no LDS round
+// trip).  The per-element work is one biased fma for the code, a clamp, an
+// exact residual and, for keys, the fp64 square; with 16 lanes per row the
+// kernel was bound by VALU issue, with 4 it runs close to the same kernel with
+// the arithmetic removed.  Value nibbles are staged as bytes in LDS and packed
+// channel-major on the way out; key codes go straight from registers to HBM.
 #include "kvq_internal.hpp"
 #include "kvq_quant_row.hpp"
 
@@ -37,61 +37,24 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(AppendArgs a) {
 
     float kmax = 0.0f, vmax = 0.0f;
 
-    if constexpr (!ROT) {
-        // plain codec: one row per quad; wave w takes rows 16w .. 16w+15, so
-        // the workgroup covers the block in one pass.  Rows outside the
-        // appended range are neither read nor written (a one-token append
-        // reads one row, also when tier 2 is host memory); the range test is
-        // uniform in the quad, whose lane exchanges only involve active lanes.
-        const int j = tid & 3;
-        const int r = tid >> 2;  // 0..63
-        const int64_t t = t_first + r;
-        if (t >= t_begin && t < t_end) {
-            const Row4In in = load_row4(a.c.k16 + (row_base + t) * D, a.c.v16 + (row_base + t) * D, j);
-            const Row4Quant rq = quant_row4(in, a.c.k_codes + (row_base + t) * D + 8 * j, &vtile[r][32 * j]);
-            if (j == 0) a.c.k_scales[row_base + t] = (uint16_t)rq.ksb;
-            a.c.v_scales[(row_base + t) * 4 + j] = (uint16_t)rq.vsb;
-            kmax = rq.kerr;
-            vmax = rq.verr;
-        }
-        // max over the wave's 16 rows (non-negative: bit patterns order like values)
-        kmax = __uint_as_float(row16_max_u32(__float_as_uint(kmax)));
-        vmax = __uint_as_float(row16_max_u32(__float_as_uint(vmax)));
-    } else {
-        // rotated codec: one row per 16-lane group (the Hadamard butterflies
-        // span the row); group g takes rows g, g + 16, g + 32, g + 48, all four
-        // loaded before any is quantized so that four loads per lane are in
-        // flight.  The range test is uniform in the group.
-        const int lane16 = tid & 15;
-        const int row0 = tid >> 4;  // 0..15
-        RowIn rin[BLK / 16];
-#pragma unroll
-        for (int i = 0; i < BLK / 16; ++i) {
-            const int64_t t = t_first + row0 + 16 * i;
-            rin[i].k = rin[i].v = make_uint4(0u, 0u, 0u, 0u);
-            if (t >= t_begin && t < t_end)
-                rin[i] = load_row16(a.c.k16 + (row_base + t) * D, a.c.v16 + (row_base + t) * D, lane16);
-        }
-#pragma unroll
-        for (int i = 0; i < BLK / 16; ++i) {
-            const int r = row0 + 16 * i;
-            const int64_t t = t_first + r;
-            if (t < t_begin || t >= t_end) continue;
-            const int64_t roff = (row_base + t) * D + 8 * lane16;
-
-            const RowQuant rq = quant_row16(rin[i], ROT, lane16);
-            const uint32_t kc[2] = {rq.kc[0], rq.kc[1]}, vc[2] = {rq.vc[0], rq.vc[1]};
-            const uint32_t ksb = rq.ksb, vsb = rq.vsb;
-            const float kerr = rq.kerr, verr = rq.verr;
-
-            *reinterpret_cast<uint2 *>(a.c.k_codes + roff) = make_uint2(kc[0], kc[1]);
-            if (lane16 == 0) a.c.k_scales[row_base + t] = (uint16_t)ksb;
-            if ((lane16 & 3) == 0) a.c.v_scales[(row_base + t) * 4 + (lane16 >> 2)] = (uint16_t)vsb;
-            *reinterpret_cast<uint2 *>(&vtile[r][8 * lane16]) = make_uint2(vc[0], vc[1]);
-            kmax = fmaxf(kmax, kerr);
-            vmax = fmaxf(vmax, verr);
-        }
+    // one row per quad; wave w takes rows 16w .. 16w+15.  Rows outside the
+    // appended range are neither read nor written (a one-token append reads
+    // one row, also when tier 2 is host memory); the range test is uniform in
+    // the quad, whose lane exchanges only involve active lanes.
+    const int j = tid & 3;
+    const int r = tid >> 2;  // 0..63
+    const int64_t t = t_first + r;
+    if (t >= t_begin && t < t_end) {
+        const Row4In in = load_row4(a.c.k16 + (row_base + t) * D, a.c.v16 + (row_base + t) * D, j);
+        const Row4Quant rq = quant_row4<ROT>(in, a.c.k_codes + (row_base + t) * D + 8 * j, &vtile[r][32 * j]);
+        if (j == 0) a.c.k_scales[row_base + t] = (uint16_t)rq.ksb;
+        a.c.v_scales[(row_base + t) * 4 + j] = (uint16_t)rq.vsb;
+        kmax = rq.kerr;
+        vmax = rq.verr;
     }
+    // max over the wave's 16 rows (non-negative: bit patterns order like values)
+    kmax = __uint_as_float(row16_max_u32(__float_as_uint(kmax)));
+    vmax = __uint_as_float(row16_max_u32(__float_as_uint(vmax)));
 
     // block statistics: max over this workgroup's rows, then over old rows
     kmax = fmaxf(kmax, __shfl_xor(kmax, 16));
