@@ -179,14 +179,11 @@ __global__ __launch_bounds__(256) void merge_cert_kernel(DecodeArgs a) {
     const float2 *pml = a.part_ml + bh * S * g + h;  // split s at pml[s * g]
     const float2 e0 = lane < S ? pml[lane * g] : make_float2(NEG_INF, 0.0f);
     const float2 e1 = lane + 64 < S ? pml[(lane + 64) * g] : make_float2(NEG_INF, 0.0f);
-    float M = fmaxf(e0.x, e1.x);
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
+    const float M = wave_total_max(fmaxf(e0.x, e1.x));  // DPP moves
     float L = 0.0f;
     if (e0.x != NEG_INF) L += e0.y * __builtin_amdgcn_exp2f(e0.x - M);
     if (e1.x != NEG_INF) L += e1.y * __builtin_amdgcn_exp2f(e1.x - M);
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) L += __shfl_xor(L, o);
+    L = wave_total_sum(L);
     const float *pacc = a.part_acc + (bh * S * g + h) * D + 2 * lane;  // split s at pacc[s * g * D]
     float2 acc = make_float2(0.0f, 0.0f);
 #pragma unroll 8

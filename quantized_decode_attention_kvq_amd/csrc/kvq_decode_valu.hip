@@ -276,25 +276,26 @@ __global__ __launch_bounds__(256) void merge_splits_kernel(DecodeArgs a) {
     if (a.gate && !a.gate[head]) return;  // recompute pass: only the recomputed heads
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const float2 *pml = a.part_ml + bh * S * g + h;  // split s at pml[s * g]
+    const float *pacc = a.part_acc + (bh * S * g + h) * D + 2 * lane;  // split s at pacc[s * g * D]
     constexpr float NEG_INF = -__builtin_huge_valf();
-    // M and L over the splits (at most 128: lanes l and l + 64)
+    // the first split's partial of this wave is loaded with (m, l), before
+    // the maxima are known
+    const float2 v0 = wave < S ? *reinterpret_cast<const float2 *>(pacc + (int64_t)wave * g * D)
+                               : make_float2(0.0f, 0.0f);
+    // M and L over the splits (at most 128: lanes l and l + 64), on DPP moves
     const float2 e0 = lane < S ? pml[lane * g] : make_float2(NEG_INF, 0.0f);
     const float2 e1 = lane + 64 < S ? pml[(lane + 64) * g] : make_float2(NEG_INF, 0.0f);
-    float M = fmaxf(e0.x, e1.x);
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
+    const float M = wave_total_max(fmaxf(e0.x, e1.x));
     float L = 0.0f;
     if (e0.x != NEG_INF) L += e0.y * __builtin_amdgcn_exp2f(e0.x - M);
     if (e1.x != NEG_INF) L += e1.y * __builtin_amdgcn_exp2f(e1.x - M);
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) L += __shfl_xor(L, o);
-    const float *pacc = a.part_acc + (bh * S * g + h) * D + 2 * lane;  // split s at pacc[s * g * D]
+    L = wave_total_sum(L);
     float2 acc = make_float2(0.0f, 0.0f);
 #pragma unroll 8
     for (int s = wave; s < S; s += 4) {
         const float m_s = pml[s * g].x;
         const float w = (L > 0.0f && m_s != NEG_INF) ? __builtin_amdgcn_exp2f(m_s - M) / L : 0.0f;
-        const float2 v = *reinterpret_cast<const float2 *>(pacc + (int64_t)s * g * D);
+        const float2 v = s == wave ? v0 : *reinterpret_cast<const float2 *>(pacc + (int64_t)s * g * D);
         acc.x += w * v.x;
         acc.y += w * v.y;
     }

@@ -35,6 +35,23 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(AppendArgs a) {
     const int64_t t_end = a.len1 < t_first + BLK ? a.len1 : t_first + BLK;
     const int64_t row_base = head * a.cap;
 
+    // a block that already holds tokens: its statistics and the thread's 16
+    // bytes of value nibbles are loaded with the new rows
+    const bool has_old = t_first < a.len0;
+    const int64_t si = head * (a.cap / BLK) + blk;
+    const int vj = tid & (D - 1);   // the thread's channel in the value packing (a wave reads 64
+    const int vi0 = (tid / D) * 16;  // consecutive channels of one token row: no bank conflicts)
+    uint8_t *vdst = a.c.v_codes + si * (D * BLK / 2) + vj * (BLK / 2) + vi0;
+    float kold = 0.0f, vold = 0.0f;
+    uint4 vold16 = make_uint4(0u, 0u, 0u, 0u);
+    if (has_old) {
+        vold16 = *reinterpret_cast<const uint4 *>(vdst);
+        if (tid == 0) {
+            kold = a.c.k_err[si];
+            vold = a.c.v_err[si];
+        }
+    }
+
     float kmax = 0.0f, vmax = 0.0f;
 
     // one row per quad; wave w takes rows 16w .. 16w+15.  Rows outside the
@@ -67,14 +84,12 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(AppendArgs a) {
     }
     __syncthreads();
 
-    const bool has_old = t_first < a.len0;
     if (tid == 0) {
         float km = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
         float vm2 = fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3]));
-        const int64_t si = head * (a.cap / BLK) + blk;
         if (has_old) {
-            km = fmaxf(km, a.c.k_err[si]);
-            vm2 = fmaxf(vm2, a.c.v_err[si]);
+            km = fmaxf(km, kold);
+            vm2 = fmaxf(vm2, vold);
         }
         a.c.k_err[si] = km;
         a.c.v_err[si] = vm2;
@@ -82,11 +97,8 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(AppendArgs a) {
 
     // value codes: channel-major nibble pairs, 16 bytes per thread
     {
-        // a wave reads 64 consecutive channels of one token row per LDS read
-        // (no bank conflicts)
-        const int j = tid & (D - 1);     // channel
-        const int i0 = (tid / D) * 16;   // first byte (token pair) of this thread
-        uint8_t *dst = a.c.v_codes + (head * (a.cap / BLK) + blk) * (D * BLK / 2) + j * (BLK / 2) + i0;
+        const int j = vj, i0 = vi0;  // channel, first byte (token pair) of this thread
+        uint8_t *dst = vdst;
         // tokens [lo, hi) of the block are new, [0, lo) kept, [hi, 64) zero
         const int lo = (int)(t_begin - t_first), hi = (int)(t_end - t_first);
         uint32_t nw[4] = {0u, 0u, 0u, 0u};
@@ -99,9 +111,7 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(AppendArgs a) {
                 nw[i >> 2] |= byte << (8 * (i & 3));
             }
         } else {
-            uint4 old = make_uint4(0, 0, 0, 0);
-            if (has_old) old = *reinterpret_cast<const uint4 *>(dst);
-            const uint32_t ow[4] = {old.x, old.y, old.z, old.w};
+            const uint32_t ow[4] = {vold16.x, vold16.y, vold16.z, vold16.w};
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 uint32_t byte = 0;
