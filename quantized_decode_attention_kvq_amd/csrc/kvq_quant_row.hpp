@@ -1,6 +1,7 @@
 // kvq_quant_row.hpp -- quantization of one token row of one KV head
-// (quantize-on-append), shared by the append kernel and the fused
-// append-and-decode path so that both give the same bytes.
+// (quantize-on-append): quant_row4 for the append kernel (a row per quad) and
+// quant_row16 for the fused append-and-decode path (a row per 16 lanes).  The
+// two share the code arithmetic below and give the same bytes.
 //
 // "Runtime-Certified Bounded-Error Quantized Attention", Methodology 1: INT8
 // keys (one fp16 scale per token and KV head, absmax/127) and INT4 values (one
@@ -79,8 +80,9 @@ __device__ __forceinline__ void fix_ties(const uint32_t w[4], float cb[8], float
     }
 }
 
-// One token row quantized by a group of 16 lanes (lane16 holds channels
-// 8*lane16 .. +7; load_row16 lets the caller issue the loads early).  Every
+// One token row quantized by a group of 16 lanes, for the fused append of one
+// token (lane16 holds channels 8*lane16 .. +7; load_row16 lets the caller
+// issue the loads early).  Every
 // lane returns its 8 key codes (bytes), its 8 value codes (low nibble of each
 // byte), the row's key scale and key error, its 32-channel group's value
 // scale, and the row's value error (max over the four groups).  Uses
