@@ -142,26 +142,32 @@ def cpu_baseline(w, d, tau_k, tau_v, sm, target_s):
     q = d["q"].cpu().numpy()
     groups = [(b, h) for b in range(w.B) for h in range(w.Hkv)]
 
-    def sample(n):
+    def sample(n, reps=1):
         idx = groups[:n]
         ks = np.stack([k16[b, h] for b, h in idx])[:, None]
         vs = np.stack([v16[b, h] for b, h in idx])[:, None]
         qs = np.stack([q[b, h * w.G:(h + 1) * w.G] for b, h in idx])
         oc = oracle.Cache(ks, vs, w.T)  # the quantized cache (setup, untimed)
         t0 = time.perf_counter()
-        _, mask = oc.attention(qs, sm, tau_k, tau_v)
+        for _ in range(reps):
+            _, mask = oc.attention(qs, sm, tau_k, tau_v)
         dt = time.perf_counter() - t0
         return dt, mask
 
     dt1, _ = sample(1)
     n = int(max(1, min(len(groups), target_s / max(dt1, 1e-3))))
     dt, mask = sample(n)
-    nbytes = decode_bytes(mask, n, w.G)
+    reps = 1
+    if n == len(groups) and dt < 0.5 * target_s:
+        # the whole workload takes less than the target: repeat it
+        reps = int(max(1, round(target_s / max(dt, 1e-3))))
+        dt, mask = sample(n, reps)
+    nbytes = decode_bytes(mask, n, w.G) * reps
     return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": oracle.max_threads(),
             "kind": "oracle",
             "sample": f"fp64 decode of {n} of {len(groups)} (batch, KV head) groups at T={w.T} "
-                      f"({n * w.G} query heads), {dt:.2f} s; same byte accounting as the GPU line",
-            "tokens_per_s_equiv": round(n / len(groups) * w.B / dt, 3)}
+                      f"({n * w.G} query heads), {reps} pass(es), {dt:.2f} s; same byte accounting as the GPU line",
+            "tokens_per_s_equiv": round(reps * n / len(groups) * w.B / dt, 3)}
 
 
 def bench_quantize(args, w):
