@@ -84,13 +84,15 @@ def test_decode_full_size_sampled(name):
         assert np.all(np.isfinite(err)) and err.max() <= OUT_TOL
 
 
-def test_bulk_quantize_full_size_sampled():
-    """1,048,576 new tokens x 8 KV heads in one append; sampled block-aligned
-    windows of every head against the oracle, bitwise."""
+@pytest.mark.parametrize("rot", [False, True])
+def test_bulk_quantize_full_size_sampled(rot):
+    """1,048,576 new tokens x 8 KV heads in one append (plain and
+    Hadamard-rotated key codec); sampled block-aligned windows of every head
+    against the oracle, bitwise."""
     w = workloads.WORKLOADS["bulk_quantize"]
-    print(f"[full size] {w}", flush=True)
+    print(f"[full size] {w} key_rotation={rot}", flush=True)
     d = workloads.make(w, "cuda")
-    c = kvq.KVCache(w.B, w.Hkv, w.cap, k16=d["k16"], v16=d["v16"])
+    c = kvq.KVCache(w.B, w.Hkv, w.cap, k16=d["k16"], v16=d["v16"], key_rotation=rot)
     kvq.kvq_quantize_append(c, w.T)
     torch.cuda.synchronize()
     win = 2048
@@ -99,7 +101,7 @@ def test_bulk_quantize_full_size_sampled():
         for t0 in starts[h % 2:]:
             k16 = d["k16"][:, h:h + 1, t0:t0 + win].cpu().numpy()
             v16 = d["v16"][:, h:h + 1, t0:t0 + win].cpu().numpy()
-            oc = oracle.Cache(k16, v16, win)
+            oc = oracle.Cache(k16, v16, win, key_rotation=rot)
             b0, nb = t0 // 64, win // 64
             pairs = [
                 ("k_codes", c.k_codes[0, h, t0:t0 + win], oc.k_codes[0, 0]),
