@@ -158,11 +158,15 @@ __global__ __launch_bounds__(256) void select_kernel(AdaptArgs a) {
         // the lane's masses in registers when they fit (every load issued
         // before the first is used; 0 past nb, never counted as every probe
         // is above 0), else in LDS
-        float mr[SEL_REGS];
+        float mr[SEL_REGS], ve[SEL_REGS];
         float mx = NEG_INF, tot = 0.0f;
         if (in_regs) {
+            // the value errors (for value promotion) are loaded with the masses
 #pragma unroll
-            for (int k = 0; k < SEL_REGS; ++k) mr[k] = lane + 64 * k < nb ? lh[lane + 64 * k] : NEG_INF;
+            for (int k = 0; k < SEL_REGS; ++k) {
+                mr[k] = lane + 64 * k < nb ? lh[lane + 64 * k] : NEG_INF;
+                ve[k] = lane + 64 * k < nb ? a.c.v_err[bh * a.nbc + lane + 64 * k] : 0.0f;
+            }
 #pragma unroll
             for (int k = 0; k < SEL_REGS; ++k) mx = fmaxf(mx, mr[k]);
             mx = wave_total_max(mx);
@@ -186,7 +190,7 @@ __global__ __launch_bounds__(256) void select_kernel(AdaptArgs a) {
         const float target = a.tau_cov * tot;
         const bool none = !(a.tau_cov > 0.0f);
         const bool all = !none && !(target <= tot);  // out of reach (or NaN): every block
-        uint32_t lo = 0u, hi = 0x7F800000u;            // F(lo) >= target > F(hi)
+        uint32_t lo = 0u, hi = 0x3F800001u;            // F(lo) >= target > F(hi); masses are at most 1
         if (!none && !all && in_regs) {
             while (hi - lo > 1u) {
                 const uint32_t mid = lo + (hi - lo) / 2u;
@@ -223,9 +227,6 @@ __global__ __launch_bounds__(256) void select_kernel(AdaptArgs a) {
             if (bits) atomicOr(&uni[i >> 2], bits << (8 * (i & 3)));
         };
         if (in_regs) {
-            float ve[SEL_REGS];
-#pragma unroll
-            for (int k = 0; k < SEL_REGS; ++k) ve[k] = lane + 64 * k < nb ? a.c.v_err[bh * a.nbc + lane + 64 * k] : 0.0f;
 #pragma unroll
             for (int k = 0; k < SEL_REGS; ++k)
                 if (lane + 64 * k < nb) mark(lane + 64 * k, mr[k], ve[k]);
