@@ -53,13 +53,61 @@ __device__ __forceinline__ float fp16_block_logmass(const DecodeArgs &a, int64_t
     return M + __log2f(s);
 }
 
+// Promoted blocks per head up to which the ranking check counts every pair.
+constexpr int PAIRWISE_MAX = 1024;
+
+// First index in [lo, hi) of an ascending run whose key is >= k (lower) or
+// > k (upper); keys (x, y) compare lexicographically, or by y alone when x
+// is null.
+template <bool UPPER>
+__device__ __forceinline__ int run_bound(const float *x, const float *y, int lo, int hi, float kx, float ky) {
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        const float xm = x ? x[mid] : 0.0f, ym = y[mid];
+        const float kxx = x ? kx : 0.0f;
+        const bool before = UPPER ? (xm < kxx || (xm == kxx && ym <= ky)) : (xm < kxx || (xm == kxx && ym < ky));
+        if (before)
+            lo = mid + 1;
+        else
+            hi = mid;
+    }
+    return lo;
+}
+
+// One bottom-up pass of a stable merge sort over n keys in LDS (run width w
+// to 2w): an element of a left run moves past the right run's smaller keys,
+// one of a right run past the left run's smaller or equal keys (binary
+// searches, so every element is placed independently).  With x null the key
+// is y alone, and the return value counts, over this thread's right-run
+// elements, the left-run keys strictly above them: summed over the passes,
+// the inversions of the sequence.
+__device__ __forceinline__ int merge_pass(const float *x, const float *y, float *nx, float *ny, int n, int w) {
+    int inv = 0;
+    for (int i = threadIdx.x; i < n; i += blockDim.x) {
+        const int r0 = i / (2 * w) * (2 * w);
+        const int le = r0 + w < n ? r0 + w : n, re = r0 + 2 * w < n ? r0 + 2 * w : n;
+        const float kx = x ? x[i] : 0.0f, ky = y[i];
+        int dst;
+        if (i < le) {
+            dst = i + (run_bound<false>(x, y, le, re, kx, ky) - le);
+        } else {
+            const int ub = run_bound<true>(x, y, r0, le, kx, ky);
+            dst = r0 + (i - le) + (ub - r0);
+            inv += le - ub;
+        }
+        if (x) nx[dst] = kx;
+        ny[dst] = ky;
+    }
+    return inv;
+}
+
 // Ranking-consistency check of one head (Methodology 3): its promoted blocks
-// are compacted into LDS with their INT8 and FP16 log-masses, every pair is
-// compared, and the head is inconsistent when the pairs ordered oppositely
-// exceed tau_rank of all pairs.  All 256 threads take part; every thread
-// returns the result.
+// are compacted into LDS with their INT8 and FP16 log-masses, the pairs
+// ordered oppositely are counted (every pair up to PAIRWISE_MAX blocks, by
+// merge sorts above), and the head is inconsistent when they exceed tau_rank
+// of all pairs.  All 256 threads take part; every thread returns the result.
 __device__ bool ranking_inconsistent(const DecodeArgs &a, int64_t bh, int64_t head, int hl, float *pa, float *pf,
-                                     int *wcnt, int *bcast) {
+                                     float *qa, float *qf, int *wcnt, int *bcast) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     if (a.nb == 0) {  // uniform: no barrier is skipped by part of the workgroup
         if (tid == 0 && a.ndisc) a.ndisc[head] = 0;
@@ -118,21 +166,51 @@ __device__ bool ranking_inconsistent(const DecodeArgs &a, int64_t bh, int64_t he
             }
     }
     __syncthreads();
+    // Discordant pairs: (a_i - a_j)(f_i - f_j) < 0.
     int cnt = 0;
-    for (int i = tid; i < n; i += 256) {
-        const float ai = pa[i], fi = pf[i];
-        int j = i + 1;
-        for (; j + 8 <= n; j += 8) {
-            float aj[8], fj[8];
+    if (n <= PAIRWISE_MAX) {
+        // every pair, 8 at a time (independent LDS reads)
+        for (int i = tid; i < n; i += 256) {
+            const float ai = pa[i], fi = pf[i];
+            int j = i + 1;
+            for (; j + 8 <= n; j += 8) {
+                float aj[8], fj[8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                aj[u] = pa[j + u];
-                fj[u] = pf[j + u];
+                for (int u = 0; u < 8; ++u) {
+                    aj[u] = pa[j + u];
+                    fj[u] = pf[j + u];
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) cnt += ((ai - aj[u]) * (fi - fj[u]) < 0.0f) ? 1 : 0;
             }
-#pragma unroll
-            for (int u = 0; u < 8; ++u) cnt += ((ai - aj[u]) * (fi - fj[u]) < 0.0f) ? 1 : 0;
+            for (; j < n; ++j) cnt += ((ai - pa[j]) * (fi - pf[j]) < 0.0f) ? 1 : 0;
         }
-        for (; j < n; ++j) cnt += ((ai - pa[j]) * (fi - pf[j]) < 0.0f) ? 1 : 0;
+    } else {
+        // Sorted by (a, f), a pair tied in a has f ascending and a pair tied
+        // in f is never strictly inverted, so the count is the number of
+        // strict inversions of the f sequence in that order: a merge sort by
+        // (a, f), then a merge sort by f counting, per pass, the left-run keys
+        // above each right-run key.  O(n log n) in log2(n) barrier-separated
+        // passes each (the binary searches are dependent LDS reads, so below
+        // PAIRWISE_MAX promoted blocks the pairs are cheaper).
+        float *ca = pa, *cf = pf, *na = qa, *nf = qf;
+        for (int w = 1; w < n; w *= 2) {
+            merge_pass(ca, cf, na, nf, n, w);
+            __syncthreads();
+            float *t = ca;
+            ca = na;
+            na = t;
+            t = cf;
+            cf = nf;
+            nf = t;
+        }
+        for (int w = 1; w < n; w *= 2) {  // ca and na are free: na takes the f keys of the next pass
+            cnt += merge_pass(nullptr, cf, nullptr, na, n, w);
+            __syncthreads();
+            float *t = cf;
+            cf = na;
+            na = t;
+        }
     }
     cnt = wave_total_sum_int(cnt);
     __syncthreads();  // every thread has read wcnt
@@ -160,6 +238,7 @@ __global__ __launch_bounds__(256) void merge_cert_kernel(DecodeArgs a) {
     __shared__ float2 red[4][64];
     __shared__ float qn_lds;
     __shared__ float pa[RANK ? ADAPT_MAX_NB : 1], pf[RANK ? ADAPT_MAX_NB : 1];
+    __shared__ float qa[RANK ? ADAPT_MAX_NB : 1], qf[RANK ? ADAPT_MAX_NB : 1];  // merge-sort buffers
     __shared__ int wcnt[4], bcast;
     const int h = blockIdx.x;
     const int64_t kvh = blockIdx.y, b = blockIdx.z;
@@ -196,7 +275,7 @@ __global__ __launch_bounds__(256) void merge_cert_kernel(DecodeArgs a) {
     }
     red[wave][lane] = acc;
     __syncthreads();
-    const bool inconsistent = RANK && ranking_inconsistent(a, bh, head, h, pa, pf, wcnt, &bcast);
+    const bool inconsistent = RANK && ranking_inconsistent(a, bh, head, h, pa, pf, qa, qf, wcnt, &bcast);
     if (wave == 0) {
         float2 o = red[0][lane];
 #pragma unroll

@@ -178,3 +178,11 @@ def test_empty_cache():
     assert not g["out"].float().cpu().numpy().any()
     assert not g["kstar"].cpu().numpy().any() and not g["recomputed"].cpu().numpy().any()
     assert not g["ndisc"].cpu().numpy().any()
+
+
+def test_ranking_check_over_many_promoted_blocks():
+    # heads promoting more than 1024 blocks: the discordant pairs are counted
+    # by the merge sorts instead of pair by pair
+    w = small("llama3_8b_32k", B=1, T=80000)
+    ref, g = _run(w.name, workloads.make(w), w, w.T, w.fallback_frac, 0.9999, tau_rank=0.3)
+    assert g["kstar"].cpu().numpy().max() > 1024
