@@ -34,7 +34,6 @@ namespace {
 
 constexpr float NEG_INF = -__builtin_huge_valf();
 constexpr int BPW = 1;        // blocks per wave of the scoring pass (more waves in flight beat fewer, longer ones)
-constexpr int SEL_REGS = 16;  // masses per lane held in registers by the selection
 
 // Rotated query of the Hadamard-rotated key codec, once per call: grid
 // (Hkv, B), one wave; lane (head m, k-group g4) rotates as in the decode and
@@ -141,6 +140,9 @@ __global__ __launch_bounds__(256) void score_int8_kernel(AdaptArgs a) {
 // largest theta with sum_{m_i >= theta} m_i >= tau_cov * S, found by a binary
 // search over the bit patterns of non-negative floats (which order like the
 // values); that theta is the K*-th largest mass.
+// SEL_REGS: masses per lane held in registers (64 * SEL_REGS blocks per head;
+// the launcher takes the smallest that holds the sequence, 16 or 32).
+template <int SEL_REGS>
 __global__ __launch_bounds__(256) void select_kernel(AdaptArgs a) {
     __shared__ float mass[4][ADAPT_MAX_NB];
     __shared__ uint32_t uni[ADAPT_MAX_NB / 4];
@@ -255,7 +257,10 @@ hipError_t launch_score(const AdaptArgs &a, int batch, hipStream_t s) {
 }
 
 hipError_t launch_select(const AdaptArgs &a, int batch, hipStream_t s) {
-    hipLaunchKernelGGL(select_kernel, dim3((unsigned)a.hkv, (unsigned)batch), dim3(256), 0, s, a);
+    if (a.nb <= 64 * 16)
+        hipLaunchKernelGGL(select_kernel<16>, dim3((unsigned)a.hkv, (unsigned)batch), dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL(select_kernel<32>, dim3((unsigned)a.hkv, (unsigned)batch), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
