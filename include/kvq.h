@@ -276,13 +276,26 @@ kvq_status kvq_decode_attn_adaptive(kvq_cache *c, const uint16_t *q, int32_t q_h
                                     void *workspace, size_t ws_bytes, void *stream);
 
 /* Decode kernel selection and timing, for measurement.  kvq_decode_attn and
- * kvq_append_decode use KVQ_KERNEL_AUTO; the _ex forms let a benchmark force a variant and a
- * split count (0 = automatic), and, when split_done is a hipEvent_t (passed
- * as void*, NULL = none), records it on the stream between the split-K kernel
- * and the merge kernel, so that the split-K kernel can be timed alone.  Same
- * semantics and errors as kvq_decode_attn; a variant that does not support
- * the group size or the context length returns KVQ_ERR_UNSUPPORTED. */
-typedef enum { KVQ_KERNEL_AUTO = 0, KVQ_KERNEL_VALU = 1, KVQ_KERNEL_MFMA = 2 } kvq_kernel;
+ * kvq_append_decode use KVQ_KERNEL_AUTO: the matrix-core kernel for every
+ * group size up to 16 and up to 1,048,576 tokens per sequence, else the VALU
+ * kernel.  The matrix-core kernel has two variants with the same results:
+ * up to 2048 blocks (131,072 tokens) per sequence, without the certificate
+ * and adaptive passes, a streaming variant that starts copying tiles before
+ * the masks are known (KVQ_KERNEL_MFMA picks it where it applies), and a
+ * general one that forms every mask first (KVQ_KERNEL_MFMA_TABLE forces it).
+ * The _ex forms let a benchmark force a kernel and a split count (0 =
+ * automatic), and, when split_done is a hipEvent_t (passed as void*, NULL =
+ * none), record it on the stream between the split-K kernel and the merge
+ * kernel, so that the split-K kernel can be timed alone.  Same semantics and
+ * errors as kvq_decode_attn; a kernel that does not support the group size
+ * or the context length returns KVQ_ERR_UNSUPPORTED.  The environment
+ * variable KVQ_SPLITS, when set, replaces the automatic split count. */
+typedef enum {
+    KVQ_KERNEL_AUTO = 0,
+    KVQ_KERNEL_VALU = 1,
+    KVQ_KERNEL_MFMA = 2,
+    KVQ_KERNEL_MFMA_TABLE = 3
+} kvq_kernel;
 kvq_status kvq_decode_attn_ex(const kvq_cache *c, const uint16_t *q, int32_t q_heads,
                               float sm_scale, float tau_k, float tau_v, uint16_t *out,
                               uint8_t *mask_out, void *workspace, size_t ws_bytes, void *stream,

@@ -24,7 +24,7 @@ BLK = 64
 VG = 32
 
 KVQ_OK = 0
-KERNEL_AUTO, KERNEL_VALU, KERNEL_MFMA = 0, 1, 2
+KERNEL_AUTO, KERNEL_VALU, KERNEL_MFMA, KERNEL_MFMA_TABLE = 0, 1, 2, 3
 KVQ_CODEC_PLAIN, KVQ_CODEC_ROTATE_K = 0, 1
 DEFAULT_SM_SCALE = float(torch.tensor(1.0 / math.sqrt(D), dtype=torch.float32))
 

@@ -307,7 +307,9 @@ kvq_status decode_impl(kvq_cache *c, const uint16_t *q, int32_t q_heads, float s
     if ((st = check_buffers(c, true)) != KVQ_OK) return st;
     if (!out) return KVQ_ERR_INVALID_ARG;
     if (!aligned(out, 16)) return KVQ_ERR_ALIGNMENT;
-    if (kernel < KVQ_KERNEL_AUTO || kernel > KVQ_KERNEL_MFMA || splits < 0) return KVQ_ERR_INVALID_ARG;
+    if (kernel < KVQ_KERNEL_AUTO || kernel > KVQ_KERNEL_MFMA_TABLE || splits < 0) return KVQ_ERR_INVALID_ARG;
+    const bool no_stream = kernel == KVQ_KERNEL_MFMA_TABLE;
+    if (no_stream) kernel = KVQ_KERNEL_MFMA;
     const bool certify = cert != nullptr;
     if (certify && (tau_out != tau_out || !aligned(cert, 4))) return tau_out != tau_out ? KVQ_ERR_INVALID_ARG : KVQ_ERR_ALIGNMENT;
     if (append && c->length >= c->capacity) return KVQ_ERR_CAPACITY;
@@ -375,6 +377,7 @@ kvq_status decode_impl(kvq_cache *c, const uint16_t *q, int32_t q_heads, float s
     a.tau_v = tau_v;
     a.t_new = append ? c->length : -1;
     a.key_rot = c->codec == KVQ_CODEC_ROTATE_K ? 1 : 0;
+    a.no_stream = no_stream ? 1 : 0;
     a.cert_mode = certify ? 1 : 0;
     a.part_e = reinterpret_cast<float *>((char *)workspace + w.e);
     a.part_sa = reinterpret_cast<float2 *>((char *)workspace + w.sa);

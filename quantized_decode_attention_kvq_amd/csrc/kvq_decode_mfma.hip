@@ -29,27 +29,25 @@
 //   channel-major nibble layout -- in the slot order (0,4),(1,5),(2,6),(3,7)
 //   that the C registers of subtiles 0 and 1 provide.
 //
-// Grid (splits, Hkv, B), 256 threads = 4 waves, two workgroups per CU (so two
-// waves per SIMD: one wave's VALU and matrix work hides the other's
-// latencies), several workgroups per CU over the launch so that the hardware
-// dispatcher evens out the finishing times.  After the fallback masks of its
-// block range are known, a workgroup lists its blocks (certified ones first)
-// and its waves share them out: wave w takes every fourth certified block and
-// two of the eight fallback steps of every fallback block, so the waves of a
-// workgroup carry equal work however the fallback blocks fall.  Each wave
-// streams its steps
+// Grid (splits, Hkv, B), NW = 8 waves, one workgroup per CU (two waves per
+// SIMD: one wave's VALU and matrix work hides the other's latencies).  After
+// the fallback masks of its (b, kvh) are known, a workgroup takes an equal
+// share of the group's work in steps, in block order, lists the blocks the
+// share touches, and its waves claim the share's steps one at a time from
+// an LDS counter at issue time, so that the waves of a workgroup finish
+// together however the fallback blocks fall.  Each wave streams its steps
 // through its own 3-stage LDS ring: the quantized data of a half (4 KB key
 // codes, 2 KB value codes, key and value scales) is copied HBM -> LDS by
 // global_load_lds (no registers held while in flight), so two halves are in
 // flight while the wave computes a third.  The copy places every chunk where
 // the MFMA lane that consumes it reads it back with a lane-linear ds_read.
-// A block with a fallback bit is streamed through the same ring as eight
-// 8-token steps (an 8-token slice of FP16 rows is 2 KB per tensor, so a step
-// with both tensors in FP16 still fits a stage); its tokens sit in the rows
-// of the MFMA tiles that a 32-token half gives to its first 8 tokens, and the
-// other rows are masked.  Every step, of either kind, issues exactly 8 copy
-// instructions, so the waits stay compile-time constants, and no global load
-// is ever waited on while later steps are in flight.
+// A block with a fallback bit is streamed through the same ring as 16-token
+// steps (keys or values alone falling back) or 8-token steps (both), whose
+// FP16 rows fit a stage; the step's tokens sit in the rows of the MFMA tiles
+// that a 32-token half gives to them, and the other rows are masked.  Every
+// step, of either kind, issues exactly 8 copy instructions, so the waits
+// stay compile-time constants, and no global load is ever waited on while
+// later steps are in flight.
 // Waves and splits are merged by log-sum-exp in a second kernel.
 #include "kvq_decode_common.hpp"
 #include "kvq_mfma.hpp"
@@ -149,15 +147,21 @@ constexpr int ST_K = 0, ST_V = 4096, ST_KS = 6144, ST_VS = 6400, ST_BYTES = 6656
 // 16j .. 16j+15 of the block (half u = j/2, positions 16(j%2) .. +15), with
 //   keys   [0, 4096): chunk c (1 KB), lane (s, dg, r) = lane 16s + 4dg + r:
 //          token 4c + r of the step, channels [32dg + 8s, +8);
-// and the value codes and scales of half u as for a certified half.  Other
-// fallback masks: tokens 8j .. 8j+7 (half u = j/4, positions 8(j%4) .. +7),
-// a part served from the codes copied exactly as for half u (only the step's
-// positions are used), a part served from FP16 rows taking
-//   keys   [0, 2048): chunk e as above, token 4e + r of the step;
-//   values [4096, 6144): the step's 8 rows, row-major [8][128].
+// and the value codes and scales of half u as for a certified half.  Values
+// alone falling back: the same 16 tokens, with
+//   keys   [0, 2048): the code bytes of the MFMA rows m of the step
+//          (8(j%2) <= m < 8(j%2) + 8) packed: chunk k (1 KB), slot
+//          32h' + 8dg + (m & 7) holds what a certified half keeps in chunk
+//          2k + h', lane m + 16dg;
+//   key scales as for a certified half (all 32 of half u);
+//   values [2048, 6144): the step's 16 rows, row-major [16][128].
+// Both falling back: tokens 8j .. 8j+7 (half u = j/4, positions 8(j%4) ..
+// +7), with
+//   keys   [0, 2048): chunk e as for keys alone, token 4e + r of the step;
+//   values [2048, 4096): the step's 8 rows, row-major [8][128].
 // The copies are padded up to 8 with dwords of the block's statistics into a
 // region the step leaves unused.
-constexpr int FB_K16 = 0, FB_V16 = 4096;
+constexpr int FB_K16 = 0, FB_V16 = 2048;
 constexpr int NSTAGE = 3;  // LDS stages per wave
 // With three stages the copies of step k+2 are issued in the middle of step k;
 // with two, those of step k+1 at the start of step k.
@@ -234,14 +238,17 @@ __device__ __forceinline__ void issue_half(const DecodeArgs &a, int64_t bh, int6
 }
 
 // Steps of a block by its fallback mask: two certified halves, four 16-token
-// steps of FP16 keys with value codes, or eight 8-token steps otherwise.
-__device__ __forceinline__ int steps_of(uint32_t mk) { return mk == 0u ? 2 : (mk == 1u ? 4 : 8); }
+// steps when only the keys or only the values fall back, eight 8-token steps
+// when both do.
+__device__ __forceinline__ int steps_of(uint32_t mk) { return mk == 0u ? 2 : (mk == 3u ? 8 : 4); }
 
 // Issues the 8 copies of fallback step j of block `blk` with fallback mask
 // mk (nonzero): tokens 16j .. 16j+15 when only the keys fall back (FP16 key
 // rows in the four 1 KB chunks: chunk c, lane (r, dg, st) holds token 4c + r,
-// channels 32dg + 8st .. +8; the value codes and scales of half j >> 1),
-// tokens 8j .. 8j+7 otherwise.  Every source address lies inside the block.
+// channels 32dg + 8st .. +8; the value codes and scales of half j >> 1) or
+// only the values (the packed key codes and the key scales of half j >> 1,
+// FP16 value rows), tokens 8j .. 8j+7 otherwise.  Every source address lies
+// inside the block.
 __device__ __forceinline__ void issue_fb(const DecodeArgs &a, int64_t bh, int64_t blk, int j,
                                          uint32_t mk, uint32_t stage, int lane_) {
     const int lane = opaque_lane(lane_);
@@ -257,32 +264,37 @@ __device__ __forceinline__ void issue_fb(const DecodeArgs &a, int64_t bh, int64_
         dma4(stage + ST_KS, pad, 0u);  // padding into the unused key-scale region
         return;
     }
-    const int64_t rs = row0 + 8 * j;  // first token of the step
-    const int u = j >> 2;
-    if (mk & 1u) {
-        const int r = lane & 3, dg = (lane >> 2) & 3, st = lane >> 4;
+    if (mk == 2u) {
+        const int u = j >> 1, hh = j & 1;
+        const int8_t *kc = a.c.k_codes + (row0 + 32 * u) * D;
+        const int ci = lane & 31, dg = ci >> 3, mm = 8 * hh + (ci & 7);
 #pragma unroll
-        for (int e = 0; e < 2; ++e)
-            dma16(stage + FB_K16 + 1024 * e, a.c.k16 + rs * D, (uint32_t)(2 * ((4 * e + r) * D + 32 * dg + 8 * st)));
-    } else {
-        issue_keys(a, row0, u, stage, lane);
-    }
-    if (mk & 2u) {
+        for (int k = 0; k < 2; ++k) {
+            const int jj = 2 * k + (lane >> 5), e = jj >> 1, h = jj & 1;
+            dma16(stage + ST_K + 1024 * k, kc, (uint32_t)(half_row(e, mm) * D + 32 * dg + 16 * h));
+        }
+        dma2(stage + ST_KS, a.c.k_scales + row0 + 32 * u, (uint32_t)(2 * (lane & 31)));
+        const int64_t rv = row0 + 16 * j;
 #pragma unroll
-        for (int d = 0; d < 2; ++d)
-            dma16(stage + FB_V16 + 1024 * d, a.c.v16 + rs * D,
+        for (int d = 0; d < 4; ++d)
+            dma16(stage + FB_V16 + 1024 * d, a.c.v16 + rv * D,
                   (uint32_t)(2 * ((4 * d + (lane >> 4)) * D + 8 * (lane & 15))));
-    } else {
-        issue_values(a, bh, blk, row0, u, stage, lane);
+        dma4(stage + ST_VS, pad, 0u);  // padding into the unused value-scale region
+        return;
     }
-    // padding: K16 + V16 (4 copies) -> 4 into the unused key-code region; key
-    // codes + V16 (7) -> 1 into the unused value-scale region
-    if (mk & 1u) {
+    // both parts fall back: 8 tokens of FP16 keys and values
+    const int64_t rs = row0 + 8 * j;  // first token of the step
+    const int r = lane & 3, dg = (lane >> 2) & 3, st = lane >> 4;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dma4(stage + 2048 + 256 * i, pad, 0u);
-    } else {
-        dma4(stage + ST_VS, pad, 0u);
-    }
+    for (int e = 0; e < 2; ++e)
+        dma16(stage + FB_K16 + 1024 * e, a.c.k16 + rs * D, (uint32_t)(2 * ((4 * e + r) * D + 32 * dg + 8 * st)));
+#pragma unroll
+    for (int d = 0; d < 2; ++d)
+        dma16(stage + FB_V16 + 1024 * d, a.c.v16 + rs * D,
+              (uint32_t)(2 * ((4 * d + (lane >> 4)) * D + 8 * (lane & 15))));
+    // padding: 4 copies into the unused region past the values
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma4(stage + 4096 + 256 * i, pad, 0u);
 }
 
 // Scores, online softmax and P.V of one step for one wave, from its stage in
@@ -337,9 +349,15 @@ __device__ __forceinline__ void process_step(const uint8_t *stage, uint32_t mk, 
             sc[e] = c * sml2;
         }
     } else {
+        // a value-fallback step keeps the code bytes of its 8 MFMA rows packed
+        // (the other rows read a copy of them and are masked below)
         uint4 kt[4];
+        const bool packed = mk == 2u;
+        const int koff = packed ? 16 * ((m & 7) + 8 * g4) : 16 * lane;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) kt[j] = *reinterpret_cast<const uint4 *>(stage + ST_K + j * 1024 + 16 * lane);
+        for (int j = 0; j < 4; ++j)
+            kt[j] = *reinterpret_cast<const uint4 *>(stage + ST_K + (packed ? 1024 * (j >> 1) + 512 * (j & 1) : 1024 * j) +
+                                                     koff);
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
             float4_t c = {0.f, 0.f, 0.f, 0.f};
@@ -430,22 +448,25 @@ __device__ __forceinline__ void process_step(const uint8_t *stage, uint32_t mk, 
 #pragma unroll
     for (int q = 0; q < 4; ++q) pp[q] = __builtin_bit_cast(half2_t, pack_h2(pv[0][q], pv[1][q]));
     if (mk & 2u) {
-        // FP16 value rows: lane (m, kg = p_lo/8) gathers channel 16mt + m of
-        // the step's tokens; other lanes and tokens past p_hi give 0 (a stale
-        // row could hold NaN, and 0 * NaN would reach the accumulator).  All
-        // 64 reads first, then the selects, so that the reads share one wait.
+        // FP16 value rows: lane (m, kg) with its 8 positions 8kg .. 8kg+7
+        // inside the step gathers channel 16mt + m of them (rows from
+        // 8kg - p_lo); other lanes and tokens past p_hi give 0 (a stale row
+        // could hold NaN, and 0 * NaN would reach the accumulator).  All 64
+        // reads first, then the selects, so that the reads share one wait.
         const uint4 bop = make_uint4(__builtin_bit_cast(uint32_t, pp[0]), __builtin_bit_cast(uint32_t, pp[1]),
                                      __builtin_bit_cast(uint32_t, pp[2]), __builtin_bit_cast(uint32_t, pp[3]));
+        const bool act = tk0 >= p_lo && tk0 < p_hi;
+        const int rb = act ? tk0 - p_lo : 0;
         uint32_t v[8][8];
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) {
-            const uint16_t *col = reinterpret_cast<const uint16_t *>(stage + FB_V16) + 16 * mt + m;
+            const uint16_t *col = reinterpret_cast<const uint16_t *>(stage + FB_V16) + rb * D + 16 * mt + m;
 #pragma unroll
             for (int t = 0; t < 8; ++t) v[mt][t] = col[t * D];
         }
         uint32_t keep = 0;  // bit t: token t of the step is valid in this lane
 #pragma unroll
-        for (int t = 0; t < 8; ++t) keep |= (tk0 == p_lo && p_lo + t < p_hi) ? (1u << t) : 0u;
+        for (int t = 0; t < 8; ++t) keep |= (act && tk0 + t < p_hi) ? (1u << t) : 0u;
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) {
             uint32_t r[4];
@@ -528,8 +549,10 @@ __device__ __forceinline__ void patch_new_token(uint8_t *stage, uint32_t mk, int
         const int e = (q >> 2) & 1, mrow = 4 * (q >> 3) + (q & 3);
         if (lane < 8) {
             const int dg = lane >> 1, h = lane & 1;
-            *reinterpret_cast<uint4 *>(stage + ST_K + (2 * e + h) * 1024 + 16 * (mrow + 16 * dg)) =
-                *reinterpret_cast<const uint4 *>(nk + 32 * dg + 16 * h);
+            // a value-fallback step holds its rows' code bytes packed
+            const int off = mk == 2u ? 1024 * e + 512 * h + 16 * ((mrow & 7) + 8 * dg)
+                                     : (2 * e + h) * 1024 + 16 * (mrow + 16 * dg);
+            *reinterpret_cast<uint4 *>(stage + ST_K + off) = *reinterpret_cast<const uint4 *>(nk + 32 * dg + 16 * h);
         }
         if (lane == 8) *reinterpret_cast<uint32_t *>(stage + ST_KS + 4 * q) = nks;
         if (lane == 9) *reinterpret_cast<uint32_t *>(stage + ST_KS + 4 * (q + 32)) = nks;
@@ -987,6 +1010,460 @@ __device__ __forceinline__ void decode_group(const DecodeArgs &a, const int spli
     }
 }
 
+// ---------------------------------------------------------------------------
+// Streaming split-K decode with its set-up overlapped: the plain and rotated
+// key codecs, up to STREAM_MAX_NB blocks per sequence, no certificate.
+//
+// The bounds of Methodology 2 need the query norm and the block statistics
+// before a tile can be chosen, and the first memory accesses of a launch take
+// several microseconds.  The tiles of most blocks are certified, so each
+// workgroup streams the quantized halves of the first NSPEC blocks of its
+// home range before it knows their masks: wave w issues half w of them right
+// behind its set-up loads (query operand, the statistics of its blocks of
+// the mask pass, and in one lane group the appended token's rows) and half
+// w + NW once those loads are in.  It then forms the group norm and the masks
+// of its blocks, with each 64-block chunk's pool steps, and after the one
+// workgroup barrier every wave knows every mask.  A first block whose tile is
+// certified keeps its speculative halves (MK_SPEC); a speculative half whose
+// block falls back is dropped when it lands.  Every other block joins the
+// group's pool in block order, with two halves, four 16-token steps (keys or
+// values alone falling back) or eight 8-token steps (both).  The pool is cut
+// so that every workgroup of the group carries the same work, its
+// speculative halves included, and the waves claim the steps of their range
+// from an LDS counter.  A wave finds a step's block through a window over 64
+// consecutive blocks of the group (mask byte and first pool step, one per
+// lane) that only moves forward, with the pool steps before each 64-block
+// chunk held one per lane.  The appended token (fused append) lies in the
+// last block, which stays out of the pool: after the barrier, the first
+// split quantizes it and writes its tier-1 bytes, and the last split
+// quantizes it, forms the block's mask and takes its steps after its range,
+// so that no wave waits for that work at the barrier.
+constexpr int STREAM_MAX_NB = 2048;  // blocks per sequence: four rounds of statistics per wave
+constexpr int NSPEC = 8;             // first blocks of a split streamed before their masks are known
+constexpr uint32_t MK_SPEC = 4u;     // mask byte of such a block whose tile is certified
+constexpr uint32_t MK_LATE = 5u;     // the appended token's block (its mask is formed after the barrier)
+constexpr int NO_STEP = 0x7fffffff;
+static_assert(2 * NSPEC == NW * (NSTAGE - 1), "one speculative half per wave in each stage but the last");
+
+// Steps a block adds to the pool, from its mask byte.
+__device__ __forceinline__ int pool_steps(uint32_t code) {
+    return code == 0u ? 2 : (code == 3u ? 8 : (code >= MK_SPEC ? 0 : 4));
+}
+
+template <bool ROT>
+__device__ __forceinline__ void decode_group_stream(const DecodeArgs &a, const int split, const int64_t kvh,
+                                                    const int64_t b) {
+    __shared__ __attribute__((aligned(16))) uint8_t ring[NW][NSTAGE][ST_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t maskb[STREAM_MAX_NB];
+    __shared__ int csteps_lds[STREAM_MAX_NB / 64];  // pool steps per 64-block chunk
+    __shared__ float wm[NW][16], wl[NW][16];
+    __shared__ int next_lds;
+    __shared__ int late_lds;  // mask of the appended token's block | LATE_READY, once formed
+    __shared__ __attribute__((aligned(16))) uint8_t nk_lds[D];  // key codes of the new token
+    __shared__ __attribute__((aligned(16))) uint8_t nv_lds[D];  // its value codes (low nibbles)
+    __shared__ uint16_t nks_lds, nvs_lds[4];                     // its key and value scales
+    __shared__ float nerr_lds[2];                                // its key and value errors
+
+    constexpr int NT = NW * 64;
+    constexpr int MAXR = STREAM_MAX_NB / NT;  // blocks per thread in the mask pass
+    constexpr int LATE_READY = 0x100;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int m = lane & 15, g4 = lane >> 4;
+    const int64_t bh = b * a.hkv + kvh;
+    const int g = a.g;
+    const int nb = (int)a.nb;
+    const int bps = a.bps;
+    const int nsplit = a.splits;
+    const int a0 = split * bps;  // first block of the home range
+    const uint32_t ring0 = (uint32_t)(uintptr_t)&ring[wave][0][0];
+
+    // fused append: token t_new lies in the last block.  The workgroups that
+    // need it quantize it after the mask barrier, in the 16-lane group of the
+    // thread holding that block in the mask pass (block i: thread i % NT):
+    // the first split writes its tier-1 bytes, the last split attends over it
+    // and takes the block after its share of the pool.
+    const int64_t t_new = a.t_new;
+    const bool late = t_new >= 0;
+    const int blk_new = late ? (int)(t_new / BLK) : -1;
+    const int p_new = late ? (int)(t_new % BLK) : 0;
+    const bool take_late = late && split == nsplit - 1;
+    const bool qgroup = late && (split == 0 || take_late) && (tid >> 4) == ((blk_new % NT) >> 4);
+
+    if (tid == 0) {
+        next_lds = 0;  // both read after the mask barrier
+        late_lds = 0;
+    }
+
+    // ---------------- set-up loads: query operand, block statistics (thread
+    // t: blocks t + NT r), the appended token's rows
+    const int rounds = (nb + NT - 1) / NT;
+    uint4 qraw[4];
+    {
+        const uint16_t *qr = a.q + (b * a.hq + kvh * g + (m < g ? m : 0)) * D + 32 * g4;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) qraw[s] = *reinterpret_cast<const uint4 *>(qr + 8 * s);
+    }
+    float ke[MAXR], ve[MAXR];
+#pragma unroll
+    for (int r = 0; r < MAXR; ++r) {
+        const int i = r * NT + tid;
+        ke[r] = (r < rounds && i < nb) ? a.c.k_err[bh * a.nbc + i] : 0.0f;
+        ve[r] = (r < rounds && i < nb) ? a.c.v_err[bh * a.nbc + i] : 0.0f;
+    }
+    RowIn rin;
+    if (qgroup) {
+        const int64_t row = bh * a.cap + t_new;
+        rin = load_row16(a.c.k16 + row * D, a.c.v16 + row * D, tid & 15);
+    }
+
+    // ---------------- speculative halves: half j = wave + NW * st of the home
+    // range's first NSPEC blocks into stage st (the appended token's block is
+    // never speculative).  Stage 0's copies go right behind the set-up loads:
+    // the first accesses of a launch take microseconds, and these land with
+    // them.  Stage 1's follow once the set-up loads are used (more copies
+    // ahead of them would delay them).  `live` bit st: stage st holds copies
+    // not yet consumed.
+    int tq[NSTAGE];
+    uint32_t live = 0u;
+    const int na = min(NSPEC, min(bps, nb - a0));
+    auto spec_issue = [&](int st) {
+        const int j = wave + NW * st;
+        const int blk = a0 + (j >> 1);
+        tq[st] = NO_STEP;
+        if ((j >> 1) < na && blk != blk_new && (int64_t)blk * BLK + 32 * (j & 1) < a.length) {
+            issue_half(a, bh, blk, j & 1, ring0 + st * ST_BYTES, lane);
+            tq[st] = -1 - j;
+            live |= 1u << st;
+        }
+    };
+    spec_issue(0);
+    tq[NSTAGE - 1] = NO_STEP;
+
+    // ---------------- query operand and group norm (as decode_group); the
+    // first use of the set-up loads waits for everything issued so far
+    uint4 qb[4];
+    float qn;
+    {
+        double run[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            qb[s] = m < g ? qraw[s] : make_uint4(0u, 0u, 0u, 0u);
+            const uint32_t w4[4] = {qb[s].x, qb[s].y, qb[s].z, qb[s].w};
+            double t[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                t[2 * i] = sq64(h2f(w4[i] & 0xFFFFu));
+                t[2 * i + 1] = sq64(h2f(w4[i] >> 16));
+            }
+            run[s] = ((t[0] + t[1]) + (t[2] + t[3])) + ((t[4] + t[5]) + (t[6] + t[7]));
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) run[s] = add_partner_d<true>(run[s]);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) run[s] = add_partner_d<false>(run[s]);
+        const float qh = (float)__dsqrt_rn((run[0] + run[2]) + (run[1] + run[3]));
+        qn = __uint_as_float(row16_max_u32(__float_as_uint(qh)));
+    }
+    spec_issue(1);
+    uint4 qrh[4], qrl[4];
+    if (ROT) rotate_q(qb, lane, qrh, qrl);
+
+    // ---------------- masks of every block of (b, kvh) but the appended
+    // token's (MK_LATE); mask_out receives the home range.  Bytes past the
+    // last block (to the end of its 64-block chunk) are MK_SPEC: no steps.
+    const int nch = (nb + 63) / 64;
+#pragma unroll
+    for (int r = 0; r < MAXR; ++r) {
+        if (r >= rounds) break;
+        const int i = r * NT + tid;  // the wave's 64 lanes hold chunk r * NW + wave
+        uint32_t code = MK_SPEC;
+        if (i == blk_new) {
+            code = MK_LATE;
+        } else if (i < nb) {
+            const uint32_t mk = block_mask(a.sm, qn, ke[r], ve[r], a.tau_k, a.tau_v);
+            if (a.mask_out && i >= a0 && i < a0 + bps) a.mask_out[bh * a.nb + i] = (uint8_t)mk;
+            code = (mk == 0u && (uint32_t)i % (uint32_t)bps < (uint32_t)NSPEC) ? MK_SPEC : mk;
+        }
+        const int c = r * NW + wave;
+        if (c < nch) {
+            maskb[i] = (uint8_t)code;
+            const int cs = wave_total_sum_int(pool_steps(code));
+            if (lane == 0) csteps_lds[c] = cs;
+        }
+    }
+    __syncthreads();
+
+    // ---------------- the appended token (quantizing group only): its codes,
+    // its block's statistics and mask, then (first split) its tier-1 bytes,
+    // written by the whole wave from what its lanes put in LDS
+    if (qgroup) {
+        const int l16 = tid & 15;
+        const RowQuant rq = quant_row16(rin, ROT, l16);
+        *reinterpret_cast<uint2 *>(&nk_lds[8 * l16]) = make_uint2(rq.kc[0], rq.kc[1]);
+        *reinterpret_cast<uint2 *>(&nv_lds[8 * l16]) = make_uint2(rq.vc[0], rq.vc[1]);
+        if ((l16 & 3) == 0) nvs_lds[l16 >> 2] = (uint16_t)rq.vsb;
+        if (l16 == 0) {
+            nks_lds = (uint16_t)rq.ksb;
+            nerr_lds[0] = rq.kerr;
+            nerr_lds[1] = rq.verr;
+        }
+        if (tid == blk_new % NT) {
+            // statistics after the append: max with the block's earlier tokens
+            const int rb = blk_new / NT;
+            float ko = ke[0], vo = ve[0];
+#pragma unroll
+            for (int r = 1; r < MAXR; ++r)
+                if (rb == r) {
+                    ko = ke[r];
+                    vo = ve[r];
+                }
+            const float kerr = p_new > 0 ? fmaxf(rq.kerr, ko) : rq.kerr;
+            const float verr = p_new > 0 ? fmaxf(rq.verr, vo) : rq.verr;
+            const uint32_t mk = block_mask(a.sm, qn, kerr, verr, a.tau_k, a.tau_v);
+            if (a.mask_out && blk_new >= a0 && blk_new < a0 + bps) a.mask_out[bh * a.nb + blk_new] = (uint8_t)mk;
+            // the codes and scales above are in LDS before the flag (this
+            // lane's LDS writes complete in order)
+            __hip_atomic_store(&late_lds, (int)mk | LATE_READY, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+    }
+    if (late && split == 0 && wave == ((blk_new % NT) >> 6)) {
+        // the quantizing wave (the same lanes wrote the LDS values read here)
+        const int64_t row = bh * a.cap + t_new;
+        if (lane < 8)
+            *reinterpret_cast<uint4 *>(a.c.k_codes + row * D + 16 * lane) =
+                *reinterpret_cast<const uint4 *>(&nk_lds[16 * lane]);
+        if (lane == 8) a.c.k_scales[row] = nks_lds;
+        if (lane >= 12 && lane < 16) a.c.v_scales[row * 4 + (lane - 12)] = nvs_lds[lane - 12];
+        uint8_t *vblk = a.c.v_codes + (bh * a.nbc + blk_new) * (D * BLK / 2);
+        if (p_new == 0) {
+            // a new block: byte (c, 0) holds the token's nibble, every other
+            // nibble of the block is 0
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int i = lane + 64 * k;
+                *reinterpret_cast<uint4 *>(vblk + 16 * i) =
+                    make_uint4((i & 1) ? 0u : (uint32_t)(nv_lds[i >> 1] & 0x0Fu), 0u, 0u, 0u);
+            }
+        } else {
+            // the token's nibble replaced in its byte by two atomics (clear,
+            // then set; same address, so in order)
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const int c = lane + 64 * k;
+                const int byte = c * (BLK / 2) + (p_new >> 1);
+                const int sh = 8 * (byte & 3) + 4 * (p_new & 1);
+                unsigned int *word = reinterpret_cast<unsigned int *>(vblk + (byte & ~3));
+                atomicAnd(word, ~(0x0Fu << sh));
+                atomicOr(word, (uint32_t)(nv_lds[c] & 0x0Fu) << sh);
+            }
+        }
+        if (lane == 0) {
+            const int64_t si = bh * a.nbc + blk_new;
+            if (p_new > 0) {
+                atomicMax(reinterpret_cast<unsigned int *>(a.c.k_err + si), __float_as_uint(nerr_lds[0]));
+                atomicMax(reinterpret_cast<unsigned int *>(a.c.v_err + si), __float_as_uint(nerr_lds[1]));
+            } else {
+                a.c.k_err[si] = nerr_lds[0];
+                a.c.v_err[si] = nerr_lds[1];
+            }
+        }
+    }
+
+    // ---------------- the pool: the steps before each 64-block chunk (lane
+    // c) and this workgroup's equal share; the last split then takes the
+    // appended token's block
+    const int csteps = lane < nch ? csteps_lds[lane] : 0;
+    const int cincl = wave_incl_scan_int(csteps);
+    const int ptotal = __builtin_amdgcn_readlane(cincl, 63);
+    const int cpre = lane < nch ? cincl - csteps : NO_STEP;
+    // Each split's pool range: the work before split s (its speculative
+    // halves and pool steps) is s/S of the whole, the halves being those of
+    // the certified first blocks of every split (lane s and s + 64 count
+    // split s's); a running max keeps the ranges ordered when a split's
+    // halves exceed its fair share.  s * work < 2^31: at most 128 splits of
+    // 2048 blocks of 8 steps.
+    int p0, nshare;
+    {
+        auto spec_count = [&](int sp) -> int {
+            int c = 0;
+            if (sp < nsplit) {
+                const int b0 = sp * bps, n = min(NSPEC, min(bps, nb - b0));
+                for (int k = 0; k < n; ++k) c += maskb[b0 + k] == MK_SPEC ? 1 : 0;
+            }
+            return c;
+        };
+        const int sc0 = spec_count(lane), sc1 = spec_count(lane + 64);
+        const int in0 = wave_incl_scan_int(sc0);
+        const int in1 = wave_incl_scan_int(sc1) + __builtin_amdgcn_readlane(in0, 63);
+        const int work = ptotal + 2 * __builtin_amdgcn_readlane(in1, 63);
+        auto raw = [&](int sp, int before) -> int {
+            return sp < nsplit ? (int)((uint32_t)(sp * work) / (uint32_t)nsplit) - 2 * before : NO_STEP;
+        };
+        const int r0 = wave_incl_scan_max_int(raw(lane, in0 - sc0));
+        const int r1 = max(wave_incl_scan_max_int(raw(lane + 64, in1 - sc1)), __builtin_amdgcn_readlane(r0, 63));
+        auto start = [&](int sp) -> int {
+            const int v = sp >= nsplit ? ptotal
+                                       : (sp < 64 ? __builtin_amdgcn_readlane(r0, sp) : __builtin_amdgcn_readlane(r1, sp - 64));
+            return min(max(v, 0), ptotal);
+        };
+        p0 = start(split);
+        nshare = start(split + 1) - p0;
+    }
+
+    // window over chunk c: lane j holds block 64c + j, its first pool step
+    // (off) and mask byte (0xFF: no steps); cursors only move forward
+    struct Window {
+        int c, off;
+        uint32_t code;
+    };
+    auto load_window = [&](Window &wn, int c) {
+        wn.c = c;
+        const uint32_t code = maskb[64 * c + lane];
+        const int st = pool_steps(code);
+        const int incl = wave_incl_scan_int(st);
+        wn.off = __builtin_amdgcn_readlane(cpre, c) + incl - st;
+        wn.code = st > 0 ? code : 0xFFu;
+    };
+    // share step t (>= 0) -> block, sub-step (half or fallback step), mask
+    // bits; false past the last step
+    auto resolve = [&](Window &wn, int t, int &blk, int &sub, uint32_t &mk) -> bool {
+        if (t < nshare) {
+            const int pt = p0 + t;
+            if (wn.c < 0 || pt >= __builtin_amdgcn_readlane(cpre, wn.c + 1)) {
+                const uint64_t cb = __builtin_amdgcn_ballot_w64(cpre <= pt);
+                load_window(wn, 63 - __builtin_clzll(cb));
+            }
+            const uint64_t bal = __builtin_amdgcn_ballot_w64(wn.code != 0xFFu && wn.off <= pt);
+            const int idx = 63 - __builtin_clzll(bal);
+            blk = 64 * wn.c + idx;
+            sub = pt - __builtin_amdgcn_readlane(wn.off, idx);
+            mk = (uint32_t)__builtin_amdgcn_readlane((int)wn.code, idx) & 3u;
+            return true;
+        }
+        if (!take_late) return false;
+        // the appended token's block: wait until its mask is formed (by the
+        // time a share is used up it nearly always is)
+        int v;
+        while (((v = __hip_atomic_load(&late_lds, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP)) & LATE_READY) == 0)
+            __builtin_amdgcn_s_sleep(2);
+        mk = (uint32_t)v & 3u;
+        blk = blk_new;
+        sub = t - nshare;
+        return sub < steps_of(mk);
+    };
+    Window iwin = {-1, 0, 0xFFu}, pwin = {-1, 0, 0xFFu};  // issue and process cursors
+    auto claim_issue = [&](int st) {
+        int t = 0;
+        if (lane == 0) t = atomicAdd(&next_lds, 1);
+        t = __builtin_amdgcn_readfirstlane(t);
+        tq[st] = t;
+        int blk, sub;
+        uint32_t mk;
+        if (resolve(iwin, t, blk, sub, mk)) {
+            const uint32_t sa = ring0 + st * ST_BYTES;
+            if (mk)
+                issue_fb(a, bh, blk, sub, mk, sa, lane);
+            else
+                issue_half(a, bh, blk, sub, sa, lane);
+            live |= 1u << st;
+        }
+    };
+    // stages without a speculative half take the first claims, in stage
+    // order (the last stage is claimed during the first step)
+#pragma unroll
+    for (int st = 0; st < NSTAGE - 1; ++st)
+        if (!((live >> st) & 1u)) claim_issue(st);
+
+    const float sml2 = a.sm * 1.4426950408889634f;  // scores in log2 units
+    WaveState ws;
+    ws.m_run = NEG_INF;
+    ws.l_run = 0.0f;
+    ws.e_run = 0.0f;
+    ws.smax = 0u;
+    ws.amax = 0u;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) ws.acc[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+    // Step in stage s.  Copies complete in issue order, and the only stage
+    // issued after s is s + 1, so waiting until at most its copies are
+    // outstanding makes stage s resident.  Once this step's key part is in
+    // the matrix cores, the stage consumed by the previous step (s + 2) takes
+    // the next claim (unless it still holds a speculative half).  Returns
+    // false once the wave has no step left.
+    auto step = [&](int s) -> bool {
+        if (!((live >> s) & 1u)) return false;
+        const int s1 = s + 1 == NSTAGE ? 0 : s + 1;
+        const int s2 = s1 + 1 == NSTAGE ? 0 : s1 + 1;
+        if ((live >> s1) & 1u)
+            wait_vmcnt<DMA_PER_STEP>();
+        else
+            wait_vmcnt<0>();
+        auto mid = [&]() {
+            if (!((live >> s2) & 1u)) claim_issue(s2);
+        };
+        const int t = tq[s];
+        int blk, sub;
+        uint32_t mk;
+        bool keep = true;
+        if (t < 0) {
+            const int j = -1 - t;
+            blk = a0 + (j >> 1);
+            sub = j & 1;
+            mk = 0u;
+            keep = maskb[blk] == MK_SPEC;  // else its block is in the pool
+        } else {
+            resolve(pwin, t, blk, sub, mk);
+        }
+        uint8_t *stage = &ring[wave][s][0];
+        const int step_len = BLK / steps_of(mk);
+        if (keep && blk == blk_new && p_new / step_len == sub)
+            patch_new_token(stage, mk, p_new & 31, nk_lds, nv_lds, nks_lds, nvs_lds, lane);
+        const int p_lo = (step_len * sub) & 31;
+        const int64_t left = a.length - ((int64_t)blk * BLK + step_len * sub);
+        const int nvalid = keep ? (int)(left < step_len ? (left > 0 ? left : 0) : step_len) : 0;
+        if (nvalid > 0)
+            process_step<false, false, ROT>(stage, mk, p_lo, p_lo + nvalid, qb, qrh, qrl, sml2, ws, lane, 0.0f,
+                                            nullptr, g, mid);
+        else
+            mid();
+        live &= ~(1u << s);
+        return true;
+    };
+    for (bool more = true; more;) {
+#pragma unroll
+        for (int s = 0; s < NSTAGE; ++s)
+            if (more) more = step(s);
+    }
+
+    // ---------------- merge waves, then write this split's partial
+    const float l_run = sum_across_rows(ws.l_run);
+    __syncthreads();  // every wave is done with the ring
+    float *wacc = reinterpret_cast<float *>(&ring[0][0][0]);
+    if (m < g) {
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) wacc[(wave * 16 + m) * D + 16 * mt + 4 * g4 + i] = ws.acc[mt][i];
+        if (g4 == 0) {
+            wm[wave][m] = ws.m_run;
+            wl[wave][m] = l_run;
+        }
+    }
+    __syncthreads();
+    write_partial(a, bh, split, NW, 16, wm, wl, wacc);
+}
+
+template <bool ROT>
+__global__ __launch_bounds__(NW * 64, NW / 4) void decode_stream_kernel(DecodeArgs a) {
+    decode_group_stream<ROT>(a, blockIdx.x, blockIdx.y, blockIdx.z);
+}
+
+bool stream_supports(const DecodeArgs &a) {
+    return !a.cert_mode && !a.gate && !a.promote && !a.step_ml && a.nb >= 1 && a.nb <= STREAM_MAX_NB &&
+           a.bps >= 1;
+}
+
 template <bool CERT, bool RANK, bool ROT>
 __global__ __launch_bounds__(NW * 64, NW / 4) void decode_mfma_kernel(DecodeArgs a) {
     decode_group<CERT, RANK, ROT>(a, blockIdx.x, blockIdx.y, blockIdx.z);
@@ -1046,6 +1523,13 @@ bool mfma_supports(int g) { return g >= 1 && g <= 16; }
 hipError_t launch_decode_mfma(const DecodeArgs &a, int batch, hipStream_t s) {
     dim3 grid((unsigned)a.splits, (unsigned)a.hkv, (unsigned)batch);
     const dim3 blk(NW * 64);
+    if (stream_supports(a) && !a.no_stream) {
+        if (a.key_rot)
+            hipLaunchKernelGGL(decode_stream_kernel<true>, grid, blk, 0, s, a);
+        else
+            hipLaunchKernelGGL(decode_stream_kernel<false>, grid, blk, 0, s, a);
+        return hipGetLastError();
+    }
     if (a.key_rot) {
         if (a.cert_mode && a.step_ml)
             hipLaunchKernelGGL((decode_mfma_kernel<true, true, true>), grid, blk, 0, s, a);

@@ -141,6 +141,17 @@ __device__ __forceinline__ int wave_incl_scan_int(int v) {
     v += dpp_from<0x143, 0xC>(0, v);
     return v;
 }
+// Inclusive running maximum over the lanes (the same moves), per lane.
+__device__ __forceinline__ int wave_incl_scan_max_int(int v) {
+    constexpr int LO = (int)0x80000000u;
+    v = max(v, dpp_from<0x111, 0xF>(LO, v));
+    v = max(v, dpp_from<0x112, 0xF>(LO, v));
+    v = max(v, dpp_from<0x114, 0xF>(LO, v));
+    v = max(v, dpp_from<0x118, 0xF>(LO, v));
+    v = max(v, dpp_from<0x142, 0xA>(LO, v));
+    v = max(v, dpp_from<0x143, 0xC>(LO, v));
+    return v;
+}
 __device__ __forceinline__ int wave_total_sum_int(int v) {
     return __builtin_amdgcn_readlane(wave_incl_scan_int(v), 63);
 }

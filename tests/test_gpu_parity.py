@@ -97,13 +97,13 @@ def test_decode_parity(case, frac):
     print(f"  err={e:.3e} fallback k={np.mean(m & 1):.3f} v={np.mean(m >> 1):.3f}")
 
 
-@pytest.mark.parametrize("kernel", [kvq.KERNEL_VALU, kvq.KERNEL_MFMA])
+@pytest.mark.parametrize("kernel", [kvq.KERNEL_VALU, kvq.KERNEL_MFMA, kvq.KERNEL_MFMA_TABLE])
 @pytest.mark.parametrize("G", [1, 2, 3, 4, 5, 8, 16])
 def test_decode_group_sizes(kernel, G):
     w = small("llama3_8b_32k", B=2, Hkv=2, Hq=2 * G, T=450)
     print(f"[decode G={G} kernel={kernel}]", flush=True)
     d = workloads.make(w)
-    if kernel == kvq.KERNEL_MFMA:
+    if kernel != kvq.KERNEL_VALU:
         gc = gpu_cache(d, w.T)
         try:
             kvq.kvq_decode_attn(gc, d["q"].cuda(), SM, 0.0, 0.0, kernel=kernel)
@@ -113,11 +113,13 @@ def test_decode_group_sizes(kernel, G):
     _decode_check(w, d, 0.2, kernel=kernel)
 
 
+@pytest.mark.parametrize("kernel", [kvq.KERNEL_AUTO, kvq.KERNEL_MFMA_TABLE])
 @pytest.mark.parametrize("splits", [1, 2, 3, 7, 64])
-def test_decode_split_counts(splits):
+def test_decode_split_counts(splits, kernel):
     w = small("stress_fallback", B=1, T=3000)
+    print(f"[decode splits={splits} kernel={kernel}]", flush=True)
     d = workloads.make(w)
-    _decode_check(w, d, 0.1, splits=splits)
+    _decode_check(w, d, 0.1, kernel=kernel, splits=splits)
 
 
 def test_decode_is_repeatable():
