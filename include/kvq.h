@@ -202,6 +202,22 @@ kvq_status kvq_append_decode(kvq_cache *c, const uint16_t *q, int32_t q_heads, f
                              float tau_k, float tau_v, uint16_t *out, uint8_t *mask_out,
                              void *workspace, size_t ws_bytes, void *stream);
 
+/* Allocation-free decode step, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): kvq_append_decode, with the per-split partial results
+ * in a static device array of KVQ_SCRATCH_BYTES inside the library instead
+ * of a caller workspace.  Each device the library runs on holds its own
+ * copy of the array until the process ends; it needs no particular contents
+ * and keeps the last call's.  Every call on a device shares that device's
+ * copy, so calls that overlap on one device (other streams, other host
+ * threads) race and must be serialized by the caller.  The call allocates
+ * nothing.  Errors: as kvq_append_decode; KVQ_ERR_WORKSPACE when the
+ * partials of the split count used, about 524 bytes per (batch, query head,
+ * split), exceed KVQ_SCRATCH_BYTES. */
+#define KVQ_SCRATCH_BYTES (8u << 20)
+kvq_status kvq_append_decode_noalloc(kvq_cache *c, const uint16_t *q, int32_t q_heads, float sm_scale,
+                                     float tau_k, float tau_v, uint16_t *out, uint8_t *mask_out, void *stream);
+
 /* Certified decode with a per-head output certificate and per-head FP16
  * recompute ("Runtime-Certified Bounded-Error Quantized Attention",
  * Methodology 2, two-term error decomposition; Methodology 3, rung 3 of the

@@ -54,7 +54,7 @@ _lib = None
 EXPORTS = ("kvq_cache_bytes", "kvq_quantize_append", "kvq_bounds", "kvq_decode_workspace_bytes",
            "kvq_decode_attn", "kvq_decode_attn_ex", "kvq_append_decode", "kvq_append_decode_ex",
            "kvq_decode_attn_cert", "kvq_adaptive_workspace_bytes", "kvq_decode_attn_adaptive",
-           "kvq_tier2_location", "kvq_status_str", "kvq_last_hip_error")
+           "kvq_tier2_location", "kvq_append_decode_noalloc", "kvq_status_str", "kvq_last_hip_error")
 
 
 def lib_path():
@@ -93,6 +93,8 @@ def lib():
         L.kvq_decode_attn_adaptive.argtypes = [CP, P, i32, f32, f32, f32, f32, f32, f32, f32, i32,
                                                P, P, P, P, P, P, P, sz, P]
         L.kvq_decode_attn_adaptive.restype = ctypes.c_int
+        L.kvq_append_decode_noalloc.argtypes = [CP, P, i32, f32, f32, f32, P, P, P]
+        L.kvq_append_decode_noalloc.restype = ctypes.c_int
         L.kvq_tier2_location.argtypes = [CP, ctypes.POINTER(i32)]
         L.kvq_tier2_location.restype = ctypes.c_int
         L.kvq_status_str.argtypes = [ctypes.c_int]
@@ -263,6 +265,22 @@ def kvq_decode_workspace_bytes(cache: KVCache, q_heads: int) -> int:
 
 def kvq_adaptive_workspace_bytes(cache: KVCache, q_heads: int) -> int:
     return int(lib().kvq_adaptive_workspace_bytes(ctypes.byref(cache.c_struct()), int(q_heads)))
+
+
+def kvq_append_decode_noalloc(cache: KVCache, q, sm_scale=DEFAULT_SM_SCALE, tau_k=0.0, tau_v=0.0, out=None,
+                              mask_out=None, stream=None):
+    """kvq_append_decode with its split partials in the library's static
+    device scratch (no workspace; the library call allocates nothing).  Pass
+    `out` to keep the binding from allocating it."""
+    _check_q(cache, q)
+    if out is None:
+        out = torch.empty_like(q)
+    c = cache.c_struct()
+    st = lib().kvq_append_decode_noalloc(ctypes.byref(c), _ptr(q), q.shape[1], sm_scale, tau_k, tau_v, _ptr(out),
+                                         _ptr(mask_out), _stream(stream))
+    _check("kvq_append_decode_noalloc", st)
+    cache.length = int(c.length)
+    return out
 
 
 def make_workspace(cache: KVCache, q_heads: int, device=None, adaptive=False):

@@ -4,6 +4,8 @@
 #include <math.h>
 #include <stdlib.h>
 
+#include <mutex>
+
 #include "kvq.h"
 #include "kvq_internal.hpp"
 
@@ -300,7 +302,7 @@ kvq_status decode_impl(kvq_cache *c, const uint16_t *q, int32_t q_heads, float s
                        float tau_v, uint16_t *out, uint8_t *mask_out, void *workspace, size_t ws_bytes,
                        void *stream, int32_t kernel, int32_t splits, void *split_done, bool append,
                        float *cert = nullptr, float tau_out = 0.0f, uint8_t *recomputed = nullptr,
-                       const AdaptOpts *ad = nullptr) {
+                       const AdaptOpts *ad = nullptr, bool scratch_ws = false) {
     kvq_status st = check_shape(c);
     if (st != KVQ_OK) return st;
     if ((st = check_query(c, q, q_heads, sm_scale, tau_k, tau_v)) != KVQ_OK) return st;
@@ -314,7 +316,9 @@ kvq_status decode_impl(kvq_cache *c, const uint16_t *q, int32_t q_heads, float s
     if (certify && (tau_out != tau_out || !aligned(cert, 4))) return tau_out != tau_out ? KVQ_ERR_INVALID_ARG : KVQ_ERR_ALIGNMENT;
     if (append && c->length >= c->capacity) return KVQ_ERR_CAPACITY;
     const int32_t g = q_heads / c->kv_heads;
-    if (!workspace || ws_bytes < kvq_decode_workspace_bytes(c, q_heads)) return KVQ_ERR_WORKSPACE;
+    // the static scratch (scratch_ws) is checked below against the layout of
+    // the split count actually used
+    if (!workspace || (!scratch_ws && ws_bytes < kvq_decode_workspace_bytes(c, q_heads))) return KVQ_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return KVQ_ERR_ALIGNMENT;
     if (ad) {
         if (!certify || bad_tol(ad->tau_cov) || bad_tol(ad->tau_vc) || bad_tol(ad->tau_rank))
@@ -345,6 +349,12 @@ kvq_status decode_impl(kvq_cache *c, const uint16_t *q, int32_t q_heads, float s
     const int64_t s = nb > 0 ? choose_splits(c, nb, splits, mf ? 1 : 4, mf ? kvq::MFMA_MAX_BPS : kvq::MAX_BPS) : 1;
     const int64_t bps = nb > 0 ? (nb + s - 1) / s : 1;
     const int64_t s_eff = nb > 0 ? (nb + bps - 1) / bps : 1;
+    // offsets for the largest split count, so that passes with different
+    // split counts share the certificate regions; the static scratch is laid
+    // out for the split count used (no certificate or recompute pass there),
+    // and checked before anything is enqueued
+    const WsLayout w = ws_layout(c, g, scratch_ws ? s_eff : max_splits(c));
+    if (scratch_ws && (certify || ad || w.total > ws_bytes)) return KVQ_ERR_WORKSPACE;
 
     if (append && (!mf || ad)) {
         // no fused path in the VALU kernel, and the adaptive scoring pass
@@ -353,9 +363,6 @@ kvq_status decode_impl(kvq_cache *c, const uint16_t *q, int32_t q_heads, float s
         append = false;
     }
 
-    // offsets for the largest split count, so that passes with different
-    // split counts share the certificate regions
-    const WsLayout w = ws_layout(c, g, max_splits(c));
     kvq::DecodeArgs a;
     a.c = ptrs(c);
     a.q = q;
@@ -463,9 +470,48 @@ kvq_status decode_impl(kvq_cache *c, const uint16_t *q, int32_t q_heads, float s
     return KVQ_OK;
 }
 
+// Static device scratch of kvq_append_decode_noalloc: a file-scope array, one
+// copy per device, whose address is looked up once per device (with that
+// device current) and kept; host code uses only that address.
+static __device__ __align__(256) unsigned char scratch[KVQ_SCRATCH_BYTES];
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[64] = {nullptr};
+
+kvq_status scratch_address(void **p) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e);
+    if (dev < 0 || dev >= 64) return KVQ_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e);
+        g_scratch_ptr[dev] = ptr;
+    }
+    *p = g_scratch_ptr[dev];
+    return KVQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+kvq_status kvq_append_decode_noalloc(kvq_cache *c, const uint16_t *q, int32_t q_heads, float sm_scale,
+                                     float tau_k, float tau_v, uint16_t *out, uint8_t *mask_out, void *stream) {
+    // argument errors first, before any device query
+    kvq_status st = check_shape(c);
+    if (st != KVQ_OK) return st;
+    if ((st = check_query(c, q, q_heads, sm_scale, tau_k, tau_v)) != KVQ_OK) return st;
+    if ((st = check_buffers(c, true)) != KVQ_OK) return st;
+    if (!out) return KVQ_ERR_INVALID_ARG;
+    if (!aligned(out, 16)) return KVQ_ERR_ALIGNMENT;
+    if (c->length >= c->capacity) return KVQ_ERR_CAPACITY;
+    void *ws = nullptr;
+    if ((st = scratch_address(&ws)) != KVQ_OK) return st;
+    return decode_impl(c, q, q_heads, sm_scale, tau_k, tau_v, out, mask_out, ws, KVQ_SCRATCH_BYTES, stream,
+                       KVQ_KERNEL_AUTO, 0, nullptr, true, nullptr, 0.0f, nullptr, nullptr, true);
+}
 
 kvq_status kvq_decode_attn_ex(const kvq_cache *c, const uint16_t *q, int32_t q_heads,
                               float sm_scale, float tau_k, float tau_v, uint16_t *out,
