@@ -523,10 +523,13 @@ void kvqo_attention(int B, int Hq, int Hkv, int64_t cap, int64_t length, const u
  *   o    : the dense output over the FP16 keys and values.
  * Reading of the two terms (the page names them, prints no formula):
  *   key term   E_key = tanh(Delta/2) * R.  Every key-certified block moves a
- *              logit by at most sm*qn_h*k_err (Cauchy-Schwarz; qn_h is this
- *              head's own norm), fallback blocks not at all, so all logit
- *              moves lie in [-Delta, Delta] with
- *              Delta = sm*qn_h*max{k_err_b : b key-certified}; then the total
+ *              logit by at most its key bound for this head,
+ *              kvqo_key_bound(sm, qn_h, k_err) (Cauchy-Schwarz with qn_h this
+ *              head's own norm; the fp32 product's 2^-16 inflation covers the
+ *              rounding of the stored norm and error), fallback blocks not at
+ *              all, so all logit moves lie in [-Delta, Delta] with
+ *              Delta = kvqo_key_bound(sm, qn_h, max{k_err_b : b key-certified});
+ *              then the total
  *              variation between the dense and the decode softmax is at most
  *              tanh(Delta/2), and sum_t (p_t - p^_t) v_tj is at most that times
  *              the range of channel j over the tokens, bounded by
@@ -669,7 +672,9 @@ static void certify_masked(int B, int Hq, int Hkv, int64_t cap, int64_t length, 
                 }
             }
             double qn = (double)kvqo_qnorm(q + oi * D);
-            double delta = (double)sm * qn * kmax;
+            /* every logit move of a key-certified token is at most the key
+             * bound of its block's error, hence of the largest such error */
+            double delta = (double)kvqo_key_bound(sm, (float)qn, (float)kmax);
             double r2 = 7.0 * smax + etamax;
             double rng = 2.0 * (r2 > amax ? r2 : amax);
             double ek = tanh(delta / 2.0) * rng;
