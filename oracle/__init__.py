@@ -128,6 +128,17 @@ def quant_k_row(x):
     return codes, scale[0], err[0]
 
 
+def quant_k_row_rot(x):
+    """The rotated key codec on one row: (codes int8[128] of u = H x / 16,
+    scale float16, err float32 = ||x - x~||)."""
+    x = _c(x, np.float16)
+    codes = np.zeros(D, np.int8)
+    scale = np.zeros(1, np.float16)
+    err = np.zeros(1, np.float32)
+    lib().kvqo_quant_k_row_rot(_p(x), _p(codes), _p(scale), _p(err))
+    return codes, scale[0], err[0]
+
+
 def quant_v_row(x):
     """Returns (codes int8[128] in [-7,7], scales float16[4], err float32)."""
     x = _c(x, np.float16)
