@@ -2,9 +2,10 @@
 
 One step = one decode step of one attention layer for the whole batch:
 kvq_append_decode, i.e. quantize-on-append of the new token of every sequence
-fused into the split-K decode kernel (bounds, fallback masks, streamed tiles
-and the online softmax), then a kernel merging the splits (--unfused: the
-append as its own kernel first).  Inputs are resident in HBM when
+fused into the split-K decode kernel (bounds, fallback masks, streamed tiles,
+the online softmax and the merge of the splits, by the last workgroup of each
+(batch, KV head) group to finish; --unfused: the append as its own kernel
+first).  Inputs are resident in HBM when
 the timed region starts.  Several layers' caches ("replicas") are cycled so
 that consecutive steps never find their KV stream in the 256 MB Infinity
 Cache, as in a real multi-layer decode; by default the steps of those
@@ -13,12 +14,17 @@ layers are captured in one HIP graph, replayed steps / layers times.
 Prints one JSON line:
   value      effective KV bandwidth of the step: algorithmic bytes / step time
              (GB/s, 1e9 B/s); tokens_per_s and pct_of_hbm_peak beside it.
-  roofline   for the dominant kernel (the split-K decode kernel): its
-             algorithmic bytes per launch (all of the decode's bytes but the
-             output) / its mean launch time from HIP events on its stream (the
-             library records one between the split-K and merge kernels),
-             against the 8 TB/s HBM3E peak; traffic from committed rocprofv3
-             FETCH_SIZE / WRITE_SIZE runs when they match the sources.
+  roofline   for the dominant kernel: its algorithmic bytes per launch / its
+             mean launch time, against the 8 TB/s HBM3E peak.  On the
+             matrix-core path the fused step is one kernel (append, decode,
+             and the split merge done by the last workgroup of each group):
+             its bytes are the step's, and its launch time comes from HIP
+             events on the stream around the timed loop.  Elsewhere (VALU
+             kernel, --unfused) it is the split-K kernel: the decode's bytes
+             but the output, timed by events around each of the same steps
+             run again eagerly (the library records one after the split-K
+             kernel).  traffic: from committed rocprofv3 FETCH_SIZE /
+             WRITE_SIZE runs when they match the sources.
   adaptive_step  the same step through kvq_decode_attn_adaptive (INT8
              scoring pass, top-K* promotion covering tau_cov, ranking check,
              recompute of inconsistent heads), with the promoted shares.
@@ -56,7 +62,7 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="llama3_8b_32k")
-    p.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma"])
+    p.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma", "mfma_table"])
     p.add_argument("--q-heads", type=int, default=0,
                    help="query heads (0: the workload's), for group-size comparisons")
     p.add_argument("--splits", type=int, default=0)
@@ -233,7 +239,9 @@ def bench_quantize(args, w):
 
 def timed_steps(args, R, step, stream):
     """Milliseconds per step over exactly args.steps steps (step(i, stream)
-    launches step i on layer cache i % R), after args.warmup untimed ones.
+    launches step i on layer cache i % R), after args.warmup untimed ones:
+    (host wall clock between synchronisations, HIP events recorded on the
+    stream the steps run on, right before the first and after the last).
     With args.graph, the R layers' steps are captured in one HIP graph
     (plus one of the first steps % R layers) and replayed; otherwise every
     step is launched eagerly."""
@@ -269,10 +277,14 @@ def timed_steps(args, R, step, stream):
             for i in range(args.steps):
                 step(i, stream)
     torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    e0.record(torch.cuda.current_stream())
     run_all()
+    e1.record(torch.cuda.current_stream())
     torch.cuda.synchronize()
-    return (time.perf_counter() - t0) / args.steps * 1e3
+    wall = (time.perf_counter() - t0) / args.steps * 1e3
+    return wall, e0.elapsed_time(e1) / args.steps
 
 
 def bench_certified(args, w, caches, ws, q, sm, tau_k, tau_v, ms_plain):
@@ -304,8 +316,8 @@ def bench_certified(args, w, caches, ws, q, sm, tau_k, tau_v, ms_plain):
     k = max(1, int(round(args.recompute_frac * cv.size)))
     tau_out = float(np.float32((cv[cv.size - k - 1] + cv[cv.size - k]) / 2)) if cv.size > k else -1.0
 
-    ms_cert = timed_steps(args, R, lambda i, strm: cstep(i, float("inf"), strm), stream)
-    ms_rec = timed_steps(args, R, lambda i, strm: cstep(i, tau_out, strm), stream)
+    ms_cert = timed_steps(args, R, lambda i, strm: cstep(i, float("inf"), strm), stream)[0]
+    ms_rec = timed_steps(args, R, lambda i, strm: cstep(i, tau_out, strm), stream)[0]
     cstep(0, tau_out, stream)
     torch.cuda.synchronize()
     r = rec.cpu().numpy()
@@ -354,7 +366,7 @@ def bench_adaptive(args, w, caches, q, sm, tau_k, tau_v, ms_plain):
     m = mask.cpu().numpy()
     ks = kstar.cpu().numpy()
     r = rec.cpu().numpy()
-    ms = timed_steps(args, R, lambda i, strm: astep(i, strm), stream)
+    ms = timed_steps(args, R, lambda i, strm: astep(i, strm), stream)[0]
     nb = m.shape[-1]
     return {
         "api": "kvq_decode_attn_adaptive (append=True)",
@@ -391,7 +403,8 @@ def main():
         return bench_quantize(args, w)
     dev = "cuda"
     sm = kvq.DEFAULT_SM_SCALE
-    kernel = {"auto": kvq.KERNEL_AUTO, "valu": kvq.KERNEL_VALU, "mfma": kvq.KERNEL_MFMA}[args.kernel]
+    kernel = {"auto": kvq.KERNEL_AUTO, "valu": kvq.KERNEL_VALU, "mfma": kvq.KERNEL_MFMA,
+              "mfma_table": kvq.KERNEL_MFMA_TABLE}[args.kernel]
 
     d = workloads.make(w, dev)
     # layer caches: same data, distinct HBM allocations
@@ -449,13 +462,9 @@ def main():
         c.length = w.T - 1
         if args.unfused:
             kvq.kvq_quantize_append(c, 1, strm)
-        if ev is not None:
-            ev[0].record(strm)
         call = kvq.kvq_decode_attn if args.unfused else kvq.kvq_append_decode
         call(c, q, sm, tau_k, tau_v, out=out, mask_out=mask if i == 0 else None, workspace=ws[i % R],
-             stream=strm, kernel=kernel, splits=args.splits, split_done=None if ev is None else ev[1])
-        if ev is not None:
-            ev[2].record(strm)
+             stream=strm, kernel=kernel, splits=args.splits)
 
     step(0)
     torch.cuda.synchronize()
@@ -471,25 +480,43 @@ def main():
     # eagerly or replayed from captured HIP graphs (append + decode + merge of
     # each of the R layers in one graph, as a decoder's per-token graph holds
     # every layer)
-    ms_step = timed_steps(args, R, lambda i, strm: step(i, strm=strm), stream)
+    ms_step, ms_step_ev = timed_steps(args, R, lambda i, strm: step(i, strm=strm), stream)
 
-    # kernel timing, right after: the same steps launched eagerly with HIP
-    # events on the stream before the decode call, between its split-K and
-    # merge kernels (recorded by the library) and after it; each event is
-    # recorded once first so that it exists before the library records it
-    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
-    for e3 in evs:
-        for e in e3:
-            e.record(stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    for i in range(args.steps):
-        step(i, evs[i])
-    torch.cuda.synchronize()
-    ms_step_events = (time.perf_counter() - t1) / args.steps * 1e3
-    split_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    merge_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
-    call_ms = float(np.mean([e[0].elapsed_time(e[2]) for e in evs]))
+    # the dominant kernel's launch time.  The fused step on the matrix-core
+    # kernel is that one kernel (its last workgroup per group merges the
+    # splits), so the events around the timed loop time it: per launch,
+    # their span / steps (which counts the gaps between graph-launched
+    # kernels too).  Otherwise the step holds more kernels: the same steps
+    # again, eagerly, with events before each call, after its split-K kernel
+    # (recorded by the library) and after the call.
+    one_kernel = not args.unfused and args.kernel != "valu" and w.G <= 16
+    if one_kernel:
+        split_ms = call_ms = ms_step_ev
+        merge_ms = 0.0
+        launch_source = (f"HIP events on the stream around the timed loop's {args.steps} steps "
+                         f"({'graph-replayed' if args.graph else 'eager'}), one kernel per step")
+    else:
+        evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
+        for e3 in evs:
+            for e in e3:
+                e.record(stream)
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            c = caches[i % R]
+            c.length = w.T - 1
+            if args.unfused:
+                kvq.kvq_quantize_append(c, 1, stream)
+            evs[i][0].record(stream)
+            call = kvq.kvq_decode_attn if args.unfused else kvq.kvq_append_decode
+            call(c, q, sm, tau_k, tau_v, out=out, workspace=ws[i % R], stream=stream, kernel=kernel,
+                 splits=args.splits, split_done=evs[i][1])
+            evs[i][2].record(stream)
+        torch.cuda.synchronize()
+        split_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+        merge_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+        call_ms = float(np.mean([e[0].elapsed_time(e[2]) for e in evs]))
+        launch_source = f"HIP events on the stream around each of {args.steps} eager decode calls"
+
 
     # the certificate needs the matrix-core kernel (group sizes up to 16)
     no_cert = args.no_certify or args.kernel == "valu" or w.G > 16
@@ -504,13 +531,15 @@ def main():
         torch.cuda.synchronize()
 
     gbs = step_bytes / (ms_step * 1e-3) / 1e9
-    # the split-K kernel reads the tiles, statistics and q; the merge kernel
-    # writes the output
-    split_bytes = dec_bytes - w.B * w.Hq * 256
+    # the fused kernel appends, reads the tiles, statistics and q and writes
+    # the output; a split-K kernel followed by a merge kernel leaves the
+    # output to the merge
+    split_bytes = step_bytes if one_kernel else dec_bytes - w.B * w.Hq * 256
     split_gbs = split_bytes / (split_ms * 1e-3) / 1e9
     traffic = traffic_from_counters()
-    kname = {"mfma": "decode_mfma_kernel", "valu": "decode_valu_kernel"}.get(
-        args.kernel, "decode_mfma_kernel" if w.G <= 16 else "decode_valu_kernel")
+    nblk = (w.T + 63) // 64
+    kname = "decode_valu_kernel" if args.kernel == "valu" or w.G > 16 else (
+        "decode_stream_kernel" if nblk <= 2048 and args.kernel != "mfma_table" else "decode_mfma_kernel")
     line = {
         "metric": "quantized-KV decode attention: effective KV GB/s (% of HBM peak), tokens/s",
         "value": round(gbs, 2),
@@ -541,7 +570,8 @@ def main():
             "bytes_per_step": step_bytes,
         },
         "roofline": {
-            "kernel": kname + " (split-K: bounds, masks, tiles, online softmax)",
+            "kernel": kname + (" (append, bounds, masks, tiles, online softmax, split merge)" if one_kernel
+                               else " (split-K: bounds, masks, tiles, online softmax)"),
             "bound": "hbm",
             "achieved": round(split_gbs, 2),
             "peak": HBM_PEAK_GBS,
@@ -550,10 +580,10 @@ def main():
             "traffic": traffic,
             "algorithmic_bytes_per_launch": split_bytes,
             "mean_launch_ms": round(split_ms, 5),
+            "launch_time_source": launch_source,
             "merge_kernel_ms": round(merge_ms, 5),
             "decode_call_ms": round(call_ms, 5),
             "decode_call_gbs": round(dec_bytes / (call_ms * 1e-3) / 1e9, 2),
-            "eager_ms_per_step_with_events": round(ms_step_events, 5),
         },
     }
     if certified is not None:

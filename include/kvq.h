@@ -178,11 +178,17 @@ size_t kvq_decode_workspace_bytes(const kvq_cache *c, int32_t q_heads);
  * (same arithmetic as kvq_bounds); fallback blocks read k16/v16, the others
  * read the int8/int4 codes.  mask_out [B][Hkv][NB] receives the masks used
  * (may be NULL).  workspace: device memory of at least
- * kvq_decode_workspace_bytes() bytes, 256-byte aligned, with no required
- * contents; it holds the per-split partial results between the split-K
- * kernel and the merge kernel that this call enqueues, so concurrent calls
- * need distinct workspaces.  Errors: INVALID_ARG, UNSUPPORTED, ALIGNMENT,
- * WORKSPACE, HIP. */
+ * kvq_decode_workspace_bytes() bytes, 256-byte aligned.  Its first
+ * 4 * batch * kv_heads bytes are arrival counters, one per (batch, KV head):
+ * zero them before the first use (and again before using the workspace for
+ * a cache with a larger batch * kv_heads); every call leaves them at zero,
+ * so the workspace is allocated and cleared once and reused.  The rest holds
+ * the per-split partial results, with no required contents: the last of the
+ * matrix-core kernel's workgroups of each (batch, KV head) to finish merges
+ * that group's splits in the same launch (one kernel per call); the VALU
+ * kernel is followed by a merge kernel.  Concurrent calls need distinct
+ * workspaces.  Errors: INVALID_ARG, UNSUPPORTED, ALIGNMENT, WORKSPACE,
+ * HIP. */
 kvq_status kvq_decode_attn(const kvq_cache *c, const uint16_t *q, int32_t q_heads, float sm_scale,
                            float tau_k, float tau_v, uint16_t *out, uint8_t *mask_out,
                            void *workspace, size_t ws_bytes, void *stream);
@@ -207,14 +213,18 @@ kvq_status kvq_append_decode(kvq_cache *c, const uint16_t *q, int32_t q_heads, f
  * forbid hipMalloc): kvq_append_decode, with the per-split partial results
  * in a static device array of KVQ_SCRATCH_BYTES inside the library instead
  * of a caller workspace.  Each device the library runs on holds its own
- * copy of the array until the process ends; it needs no particular contents
- * and keeps the last call's.  Every call on a device shares that device's
+ * copy of the array until the process ends; it starts zeroed, keeps the
+ * last call's partials and is left fit for the next call (its arrival
+ * counters back at zero).  Every call on a device shares that device's
  * copy, so calls that overlap on one device (other streams, other host
  * threads) race and must be serialized by the caller.  The call allocates
- * nothing.  Errors: as kvq_append_decode; KVQ_ERR_WORKSPACE when the
- * partials of the split count used, about 524 bytes per (batch, query head,
- * split), exceed KVQ_SCRATCH_BYTES. */
+ * nothing.  Errors: as kvq_append_decode; KVQ_ERR_WORKSPACE when
+ * batch * kv_heads exceeds KVQ_SCRATCH_MAX_GROUPS (the arrival counters at
+ * the head of the array) or the partials of the split count used, about 524
+ * bytes per (batch, query head, split), do not fit in the rest of
+ * KVQ_SCRATCH_BYTES. */
 #define KVQ_SCRATCH_BYTES (8u << 20)
+#define KVQ_SCRATCH_MAX_GROUPS 16384u
 kvq_status kvq_append_decode_noalloc(kvq_cache *c, const uint16_t *q, int32_t q_heads, float sm_scale,
                                      float tau_k, float tau_v, uint16_t *out, uint8_t *mask_out, void *stream);
 
@@ -301,8 +311,9 @@ kvq_status kvq_decode_attn_adaptive(kvq_cache *c, const uint16_t *q, int32_t q_h
  * general one that forms every mask first (KVQ_KERNEL_MFMA_TABLE forces it).
  * The _ex forms let a benchmark force a kernel and a split count (0 =
  * automatic), and, when split_done is a hipEvent_t (passed as void*, NULL =
- * none), record it on the stream between the split-K kernel and the merge
- * kernel, so that the split-K kernel can be timed alone.  Same semantics and
+ * none), record it on the stream right after the split-K kernel (before the
+ * merge kernel, where there is one), so that the split-K kernel can be
+ * timed alone.  Same semantics and
  * errors as kvq_decode_attn; a kernel that does not support the group size
  * or the context length returns KVQ_ERR_UNSUPPORTED.  The environment
  * variable KVQ_SPLITS, when set, replaces the automatic split count. */

@@ -114,6 +114,15 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _event(ev):
+    """A torch.cuda.Event, a raw hipEvent_t (int or c_void_p), or None."""
+    if ev is None:
+        return None
+    if hasattr(ev, "cuda_event"):
+        return ctypes.c_void_p(ev.cuda_event)
+    return ev if isinstance(ev, ctypes.c_void_p) else ctypes.c_void_p(int(ev))
+
+
 def _stream(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -296,8 +305,9 @@ def kvq_decode_attn(cache: KVCache, q, sm_scale=DEFAULT_SM_SCALE, tau_k=0.0, tau
                     mask_out=None, workspace=None, stream=None, kernel=KERNEL_AUTO, splits=0, split_done=None):
     """Certified decode attention: q [B][Hq][128] fp16 -> out [B][Hq][128] fp16.
     mask_out (optional uint8 [B][Hkv][nblocks]) receives the fallback masks.
-    split_done (optional torch.cuda.Event, already recorded once so that it
-    exists) is recorded between the split-K kernel and the merge kernel."""
+    split_done (optional: a torch.cuda.Event already recorded once so that it
+    exists, or a raw hipEvent_t) is recorded between the split-K kernel and
+    the merge kernel."""
     _check_q(cache, q)
     if out is None:
         out = torch.empty_like(q)
@@ -307,7 +317,7 @@ def kvq_decode_attn(cache: KVCache, q, sm_scale=DEFAULT_SM_SCALE, tau_k=0.0, tau
     st = lib().kvq_decode_attn_ex(ctypes.byref(c), _ptr(q), q.shape[1], sm_scale, tau_k, tau_v, _ptr(out),
                                   _ptr(mask_out), _ptr(workspace), workspace.numel(), _stream(stream),
                                   int(kernel), int(splits),
-                                  None if split_done is None else ctypes.c_void_p(split_done.cuda_event))
+                                  _event(split_done))
     _check("kvq_decode_attn", st)
     return out
 
@@ -327,7 +337,7 @@ def kvq_append_decode(cache: KVCache, q, sm_scale=DEFAULT_SM_SCALE, tau_k=0.0, t
     st = lib().kvq_append_decode_ex(ctypes.byref(c), _ptr(q), q.shape[1], sm_scale, tau_k, tau_v, _ptr(out),
                                     _ptr(mask_out), _ptr(workspace), workspace.numel(), _stream(stream),
                                     int(kernel), int(splits),
-                                    None if split_done is None else ctypes.c_void_p(split_done.cuda_event))
+                                    _event(split_done))
     _check("kvq_append_decode", st)
     cache.length = int(c.length)
     return out

@@ -60,21 +60,25 @@ kvq::CachePtrs ptrs(const kvq_cache *c) {
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Workspace layout: [part_ml float2 x B*Hkv*S*G, padded to 256 B]
-//                   [part_acc float x B*Hkv*S*G*128]
+// Workspace layout: [arrival counters uint32 x slots: zero before the first
+//                    call, left zero by every call]
+//                   [part_ml float2 x B*Hkv*S*G] [part_acc float x B*Hkv*S*G*128]
 //                   certificate: [part_e float x B*Hkv*S*G] [part_sa float2 x
 //                   B*Hkv*S] [part_kv float2 x B*Hkv] [flags uint8 x B*Hq],
-//                   each padded to 256 B
+//                   each padded to 256 B.  The counters come first, so that
+//                   no other region of a later call with another split count
+//                   (the static scratch) or a smaller B*Hkv lands on them.
 struct WsLayout {
-    size_t ml, acc, e, sa, kv, flags, total;
+    size_t arrive, ml, acc, e, sa, kv, flags, total;
 };
 
-WsLayout ws_layout(const kvq_cache *c, int32_t g, int64_t splits) {
+WsLayout ws_layout(const kvq_cache *c, int32_t g, int64_t splits, size_t slots) {
     const size_t bh = (size_t)c->batch * (size_t)c->kv_heads;
     const size_t parts = bh * (size_t)splits * (size_t)g;
     WsLayout w;
-    w.ml = 0;
-    w.acc = round_up(parts * sizeof(float2), 256);
+    w.arrive = 0;
+    w.ml = round_up(slots * sizeof(uint32_t), 256);
+    w.acc = round_up(w.ml + parts * sizeof(float2), 256);
     w.e = round_up(w.acc + parts * kvq::D * sizeof(float), 256);
     w.sa = round_up(w.e + parts * sizeof(float), 256);
     w.kv = round_up(w.sa + bh * (size_t)splits * sizeof(float2), 256);
@@ -273,7 +277,7 @@ size_t kvq_decode_workspace_bytes(const kvq_cache *c, int32_t q_heads) {
     if (check_shape(c) != KVQ_OK || q_heads < 1 || q_heads % c->kv_heads != 0 ||
         q_heads / c->kv_heads > 16)
         return 0;
-    return ws_layout(c, q_heads / c->kv_heads, max_splits(c)).total;
+    return ws_layout(c, q_heads / c->kv_heads, max_splits(c), (size_t)c->batch * (size_t)c->kv_heads).total;
 }
 
 size_t kvq_adaptive_workspace_bytes(const kvq_cache *c, int32_t q_heads) {
@@ -353,8 +357,11 @@ kvq_status decode_impl(kvq_cache *c, const uint16_t *q, int32_t q_heads, float s
     // split counts share the certificate regions; the static scratch is laid
     // out for the split count used (no certificate or recompute pass there),
     // and checked before anything is enqueued
-    const WsLayout w = ws_layout(c, g, scratch_ws ? s_eff : max_splits(c));
-    if (scratch_ws && (certify || ad || w.total > ws_bytes)) return KVQ_ERR_WORKSPACE;
+    const int64_t nbh = (int64_t)c->batch * c->kv_heads;
+    const WsLayout w = scratch_ws ? ws_layout(c, g, s_eff, KVQ_SCRATCH_MAX_GROUPS)
+                                  : ws_layout(c, g, max_splits(c), (size_t)nbh);
+    if (scratch_ws && (certify || ad || nbh > (int64_t)KVQ_SCRATCH_MAX_GROUPS || w.total > ws_bytes))
+        return KVQ_ERR_WORKSPACE;
 
     if (append && (!mf || ad)) {
         // no fused path in the VALU kernel, and the adaptive scoring pass
@@ -399,6 +406,8 @@ kvq_status decode_impl(kvq_cache *c, const uint16_t *q, int32_t q_heads, float s
     a.lhat = nullptr;
     a.ndisc = nullptr;
     a.tau_rank = 1.0f;
+    // the plain matrix-core decode merges its splits in the same launch
+    a.arrive = (mf && !certify && !ad) ? reinterpret_cast<uint32_t *>((char *)workspace + w.arrive) : nullptr;
 
     hipError_t e = hipSuccess;
     kvq::AdaptArgs aa;
@@ -437,8 +446,9 @@ kvq_status decode_impl(kvq_cache *c, const uint16_t *q, int32_t q_heads, float s
         e = mf ? kvq::launch_decode_mfma(a, c->batch, (hipStream_t)stream)
                : kvq::launch_decode_valu(a, c->batch, (hipStream_t)stream);
     if (e == hipSuccess && split_done) e = hipEventRecord((hipEvent_t)split_done, (hipStream_t)stream);
-    if (e == hipSuccess) e = certify ? kvq::launch_merge_cert(a, c->batch, (hipStream_t)stream)
-                                     : kvq::launch_merge(a, c->batch, (hipStream_t)stream);
+    if (e == hipSuccess && !a.arrive)
+        e = certify ? kvq::launch_merge_cert(a, c->batch, (hipStream_t)stream)
+                    : kvq::launch_merge(a, c->batch, (hipStream_t)stream);
     const bool rung3 = certify && (tau_out != __builtin_huge_valf() || (ad && ad->tau_rank < 1.0f));
     if (e == hipSuccess && rung3) {
         // rung 3: the groups holding a flagged head run again with every
@@ -456,9 +466,9 @@ kvq_status decode_impl(kvq_cache *c, const uint16_t *q, int32_t q_heads, float s
         r.mask_out = nullptr;
         r.cert_mode = 0;
         r.gate = a.flags;
+        r.arrive = nullptr;
         r.promote = nullptr;
         r.step_ml = nullptr;
-        const int64_t nbh = (int64_t)c->batch * c->kv_heads;
         int64_t slots = (device_cus() + r.splits - 1) / r.splits;  // about one workgroup per CU
         if (slots > nbh) slots = nbh;
         if (slots < 1) slots = 1;

@@ -46,6 +46,16 @@ __device__ __forceinline__ void compute_masks(const DecodeArgs &a, int64_t bh, i
     __syncthreads();
 }
 
+// Device-coherent (agent-scope) stores and loads: values written by one
+// workgroup and read by another of the same launch, which may run on another
+// XCD with its own L2.
+__device__ __forceinline__ void st_agent(float *p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_agent(const float *p) {
+    return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Online-softmax state of one head on one wave, and its merge with another.
 struct Running {
     float m, l;
@@ -86,9 +96,74 @@ __device__ __forceinline__ void write_partial(const DecodeArgs &a, int64_t bh, i
             }
         }
         const int64_t p = (bh * a.splits + split) * g + h;
-        a.part_acc[p * D + j] = A;
-        if (j == 0) a.part_ml[p] = make_float2(M, L);
+        if (a.arrive) {
+            // read back in this launch by another workgroup, maybe on another
+            // XCD: device-coherent stores
+            st_agent(a.part_acc + p * D + j, A);
+            if (j == 0) {
+                st_agent(reinterpret_cast<float *>(a.part_ml + p), M);
+                st_agent(reinterpret_cast<float *>(a.part_ml + p) + 1, L);
+            }
+        } else {
+            a.part_acc[p * D + j] = A;
+            if (j == 0) a.part_ml[p] = make_float2(M, L);
+        }
     }
+}
+
+// The split merge in the decode launch itself: once this workgroup's partial
+// stores have completed (device-coherent), it counts itself in; the last of
+// the group's a.splits workgroups to arrive loads every partial of the group
+// (device-coherent loads) and writes the fp16 output rows of its G heads,
+// with the arithmetic of the separate merge kernel:
+//   M = max_s m_s, L = sum_s l_s 2^(m_s - M), out = sum_s acc_s 2^(m_s - M) / L
+// (0 when no split saw a token).  It then leaves the counter at zero.  lds:
+// at least 8 * G * splits + 128 bytes of LDS free for the merge.  Called by
+// every thread of the workgroup.
+__device__ __forceinline__ void fold_merge(const DecodeArgs &a, int64_t bh, int64_t b, int64_t kvh, uint8_t *lds) {
+    __shared__ int last_lds;
+    constexpr float NEG_INF = -__builtin_huge_valf();
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's partial stores are complete
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t prev = __hip_atomic_fetch_add(a.arrive + bh, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last_lds = prev == (uint32_t)(a.splits - 1);
+    }
+    __syncthreads();
+    if (!last_lds) return;
+    const int g = a.g, S = a.splits, nt = blockDim.x;
+    float2 *wml = reinterpret_cast<float2 *>(lds);               // [G][S] (m, l) of every split
+    float2 *hml = reinterpret_cast<float2 *>(lds) + g * S;       // [G] (M, L)
+    const float2 *pml = a.part_ml + bh * S * g;                  // split s, head h at [s * g + h]
+    for (int i = threadIdx.x; i < g * S; i += nt) {
+        const int h = i / S, s_ = i % S;
+        const float *e = reinterpret_cast<const float *>(pml + s_ * g + h);
+        wml[i] = make_float2(ld_agent(e), ld_agent(e + 1));
+    }
+    __syncthreads();
+    for (int h = threadIdx.x; h < g; h += nt) {
+        float M = NEG_INF;
+        for (int s_ = 0; s_ < S; ++s_) M = fmaxf(M, wml[h * S + s_].x);
+        float L = 0.0f;
+        if (M != NEG_INF)
+            for (int s_ = 0; s_ < S; ++s_)
+                if (wml[h * S + s_].x != NEG_INF) L += wml[h * S + s_].y * __builtin_amdgcn_exp2f(wml[h * S + s_].x - M);
+        hml[h] = make_float2(M, L);
+    }
+    __syncthreads();
+    const float *pacc = a.part_acc + bh * S * g * D;             // split s, head h, channel j at [(s g + h) D + j]
+    for (int i = threadIdx.x; i < g * D; i += nt) {
+        const int h = i / D, j = i % D;
+        const float M = hml[h].x, L = hml[h].y;
+        float o = 0.0f;
+        for (int s_ = 0; s_ < S; ++s_) {
+            const float m_s = wml[h * S + s_].x;
+            const float w = (L > 0.0f && m_s != NEG_INF) ? __builtin_amdgcn_exp2f(m_s - M) / L : 0.0f;
+            o += w * ld_agent(pacc + ((int64_t)s_ * g + h) * D + j);
+        }
+        a.out[(b * a.hq + kvh * g + h) * D + j] = (uint16_t)f2h_rn(o);
+    }
+    if (threadIdx.x == 0) __hip_atomic_store(a.arrive + bh, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace kvq

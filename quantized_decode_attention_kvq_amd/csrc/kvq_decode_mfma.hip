@@ -163,6 +163,8 @@ constexpr int ST_K = 0, ST_V = 4096, ST_KS = 6144, ST_VS = 6400, ST_BYTES = 6656
 // region the step leaves unused.
 constexpr int FB_K16 = 0, FB_V16 = 2048;
 constexpr int NSTAGE = 3;  // LDS stages per wave
+// the split merge in the launch reuses the ring for its (m, l) tables
+static_assert(8 * 16 * (MAX_SPLITS + 1) <= NW * NSTAGE * ST_BYTES, "fold_merge needs 8 (S + 1) G bytes of LDS");
 // With three stages the copies of step k+2 are issued in the middle of step k;
 // with two, those of step k+1 at the start of step k.
 constexpr bool EARLY_ISSUE = NSTAGE == 2;
@@ -986,6 +988,10 @@ __device__ __forceinline__ void decode_group(const DecodeArgs &a, const int spli
     }
     __syncthreads();
     write_partial(a, bh, split, NW, 16, wm, wl, wacc);
+    if (!CERT && a.arrive) {
+        __syncthreads();  // the wave merge's LDS is read; the ring is free for the split merge
+        fold_merge(a, bh, b, kvh, &ring[0][0][0]);
+    }
     if (CERT) {
         // per head: the split's mass-weighted value error on the scale of its
         // running maximum (as write_partial scales the running sum)
@@ -1452,6 +1458,10 @@ __device__ __forceinline__ void decode_group_stream(const DecodeArgs &a, const i
     }
     __syncthreads();
     write_partial(a, bh, split, NW, 16, wm, wl, wacc);
+    if (a.arrive) {
+        __syncthreads();  // the wave merge's LDS is read; the ring is free for the split merge
+        fold_merge(a, bh, b, kvh, &ring[0][0][0]);
+    }
 }
 
 template <bool ROT>

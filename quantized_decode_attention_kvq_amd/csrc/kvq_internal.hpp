@@ -55,6 +55,10 @@ struct DecodeArgs {
     int64_t t_new;  // token appended by this launch (fused append), or -1
     int32_t key_rot;  // KVQ_CODEC_ROTATE_K: codes of the rotated keys (rotate q for them)
     int32_t no_stream;  // 1: the general matrix-core kernel even where the streaming one applies
+    // per-(b, kvh) arrival counters [B*Hkv], zero on entry and left zero:
+    // the last workgroup of a group to write its partial merges the group's
+    // splits into out in the same launch (null: a merge kernel follows)
+    uint32_t *arrive;
     // per-head output certificate (matrix-core kernel with cert_mode set)
     int32_t cert_mode;
     float *part_e;          // [B*Hkv][S][G] mass-weighted value error, on the split's running-max scale

@@ -54,15 +54,21 @@ def test_decode_full_size_sampled(name):
     w = workloads.WORKLOADS[name]
     print(f"[full size] {w}", flush=True)
     d = workloads.make(w, "cuda")
-    c = kvq.KVCache(w.B, w.Hkv, w.cap, k16=d["k16"], v16=d["v16"])
     q = d["q"].contiguous()
     # tolerances from the bounds of the full cache (as the benchmark does)
+    c = kvq.KVCache(w.B, w.Hkv, w.cap, k16=d["k16"], v16=d["v16"])
     kvq.kvq_quantize_append(c, w.T)
     kb, vb, _ = kvq.kvq_bounds(c, q, SM, 0.0, 0.0, want=("kb", "vb"))
     tk, tv = _taus(kb, vb, w.fallback_frac)
-    # the benchmark's step: prefill T-1 tokens, then one fused append + decode
-    c.length = w.T - 1
-    mask = torch.full(kb.shape, 0xEE, dtype=torch.uint8, device="cuda")
+    shape = kb.shape
+    del c, kb, vb
+    torch.cuda.empty_cache()
+    # the benchmark's step on a fresh cache: prefill T-1 tokens, then one
+    # fused append of token T-1 + decode (its tier-1 bytes written by the
+    # decode kernel alone)
+    c = kvq.KVCache(w.B, w.Hkv, w.cap, k16=d["k16"], v16=d["v16"])
+    kvq.kvq_quantize_append(c, w.T - 1)
+    mask = torch.full(shape, 0xEE, dtype=torch.uint8, device="cuda")
     out = kvq.kvq_append_decode(c, q, SM, tk, tv, mask_out=mask)
     assert c.length == w.T
     _, _, bmask = kvq.kvq_bounds(c, q, SM, tk, tv, want=("mask",))
