@@ -149,6 +149,17 @@ kvq_status kvq_cache_bytes(const kvq_cache *c, size_t bytes_out[6]);
  * sees at another address; HIP when the attribute query itself fails. */
 kvq_status kvq_tier2_location(const kvq_cache *c, int32_t *where_out);
 
+/* Empties the cache for reuse by another sequence (Methodology 1's per-block
+ * error annotations start over): enqueues on the stream a fill of k_err and
+ * v_err with zeros over the whole capacity (a kernel, not a memset, so the
+ * call can be captured into a graph) and sets c->length = 0.  The other
+ * tier-1 buffers keep their bytes, which no entry point reads at positions
+ * >= length: the first append into a block overwrites its statistics and
+ * writes every nibble byte of the block, so appends after a reset give the
+ * same tier-1 bytes as appends into a fresh cache.  Allocates nothing, does
+ * not block.  Errors: INVALID_ARG (shape, null statistics), ALIGNMENT, HIP. */
+kvq_status kvq_cache_reset(kvq_cache *c, void *stream);
+
 /* Quantize-on-append (Methodology 1: tier-1 codes, scales and per-block error
  * annotations derived from the FP16 originals).  Quantizes tokens
  * [length, length + n_new) of every (batch, KV head) from k16/v16 into the

@@ -51,7 +51,7 @@ class _Cache(ctypes.Structure):
 
 
 _lib = None
-EXPORTS = ("kvq_cache_bytes", "kvq_quantize_append", "kvq_bounds", "kvq_decode_workspace_bytes",
+EXPORTS = ("kvq_cache_bytes", "kvq_cache_reset", "kvq_quantize_append", "kvq_bounds", "kvq_decode_workspace_bytes",
            "kvq_decode_attn", "kvq_decode_attn_ex", "kvq_append_decode", "kvq_append_decode_ex",
            "kvq_decode_attn_cert", "kvq_adaptive_workspace_bytes", "kvq_decode_attn_adaptive",
            "kvq_tier2_location", "kvq_append_decode_noalloc", "kvq_status_str", "kvq_last_hip_error")
@@ -62,11 +62,16 @@ def lib_path():
 
 
 def lib():
-    """Load libkvq.so (building it in-tree first if it is absent)."""
+    """Load libkvq.so (building it in-tree first if it is absent).  A library
+    built from other sources than the present csrc/ and include/kvq.h is
+    refused: rebuild it with quantized_decode_attention_kvq_amd.build.build()."""
     global _lib
     if _lib is None:
         if not os.path.exists(_build.LIB):
             _build.build()
+        if not _build.is_current():
+            raise RuntimeError(f"{_build.LIB} was not built from the present sources (csrc/, include/kvq.h); "
+                               "rebuild it (python -m quantized_decode_attention_kvq_amd.build)")
         L = ctypes.CDLL(_build.LIB)
         P, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
         CP = ctypes.POINTER(_Cache)
@@ -74,6 +79,8 @@ def lib():
         L.kvq_cache_bytes.restype = ctypes.c_int
         L.kvq_quantize_append.argtypes = [CP, i64, P]
         L.kvq_quantize_append.restype = ctypes.c_int
+        L.kvq_cache_reset.argtypes = [CP, P]
+        L.kvq_cache_reset.restype = ctypes.c_int
         L.kvq_bounds.argtypes = [CP, P, i32, f32, f32, f32, P, P, P, P]
         L.kvq_bounds.restype = ctypes.c_int
         L.kvq_decode_workspace_bytes.argtypes = [CP, i32]
@@ -243,6 +250,14 @@ def kvq_quantize_append(cache: KVCache, n_new: int, stream=None):
     advance cache.length (asynchronous on `stream`)."""
     c = cache.c_struct()
     _check("kvq_quantize_append", lib().kvq_quantize_append(ctypes.byref(c), int(n_new), _stream(stream)))
+    cache.length = int(c.length)
+
+
+def kvq_cache_reset(cache: KVCache, stream=None):
+    """Empty the cache for reuse (asynchronous on `stream`): zero the block
+    statistics and set length to 0."""
+    c = cache.c_struct()
+    _check("kvq_cache_reset", lib().kvq_cache_reset(ctypes.byref(c), _stream(stream)))
     cache.length = int(c.length)
 
 

@@ -20,6 +20,31 @@ FLAGS = [
 ]
 
 
+STAMP = LIB + ".srchash"  # hash of the sources and flags the library was built from
+
+
+def source_hash() -> str:
+    """sha256 over the sources (csrc/, include/kvq.h) and the compiler flags."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(sources(), key=os.path.basename):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    # the flags with the repository's location taken out (the tree is built
+    # in one place and may run from another)
+    h.update(" ".join(f.replace(ROOT, "<root>") for f in FLAGS).encode())
+    return h.hexdigest()
+
+
+def is_current() -> bool:
+    """True when libkvq.so exists and was built from the present sources."""
+    if not os.path.exists(LIB) or not os.path.exists(STAMP):
+        return False
+    with open(STAMP) as fh:
+        return fh.read().strip() == source_hash()
+
+
 def build(verbose: bool = False) -> str:
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
     cmd = [HIPCC, *FLAGS, *srcs, "-o", LIB + ".tmp"]
@@ -33,11 +58,15 @@ def build(verbose: bool = False) -> str:
     if verbose and err.strip():
         print(err, file=sys.stderr)
     os.replace(LIB + ".tmp", LIB)
+    with open(STAMP + ".tmp", "w") as fh:
+        fh.write(source_hash() + "\n")
+    os.replace(STAMP + ".tmp", STAMP)
     return LIB
 
 
 def sources():
-    return [os.path.join(CSRC, s) for s in os.listdir(CSRC)] + [os.path.join(ROOT, "include", "kvq.h")]
+    return [os.path.join(CSRC, s) for s in os.listdir(CSRC) if s.endswith((".hip", ".hpp", ".h"))] + \
+        [os.path.join(ROOT, "include", "kvq.h")]
 
 
 if __name__ == "__main__":

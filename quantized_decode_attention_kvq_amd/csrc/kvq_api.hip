@@ -243,6 +243,18 @@ kvq_status kvq_quantize_append(kvq_cache *c, int64_t n_new, void *stream) {
     return KVQ_OK;
 }
 
+kvq_status kvq_cache_reset(kvq_cache *c, void *stream) {
+    kvq_status st = check_shape(c);
+    if (st != KVQ_OK) return st;
+    if (!c->k_err || !c->v_err) return KVQ_ERR_INVALID_ARG;
+    if (!aligned(c->k_err, 4) || !aligned(c->v_err, 4)) return KVQ_ERR_ALIGNMENT;
+    const int64_t n = (int64_t)c->batch * c->kv_heads * (c->capacity / kvq::BLK);
+    hipError_t e = kvq::launch_zero_stats(c->k_err, c->v_err, n, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e);
+    c->length = 0;
+    return KVQ_OK;
+}
+
 kvq_status kvq_bounds(const kvq_cache *c, const uint16_t *q, int32_t q_heads, float sm_scale,
                       float tau_k, float tau_v, float *kb, float *vb, uint8_t *mask, void *stream) {
     kvq_status st = check_shape(c);

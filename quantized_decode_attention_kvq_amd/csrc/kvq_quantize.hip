@@ -134,6 +134,24 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(AppendArgs a) {
     }
 }
 
+// Zeroes n floats of each statistics array (a fill kernel rather than a
+// memset node, so that the call can be captured into a graph).
+__global__ __launch_bounds__(256) void zero_stats_kernel(float *k_err, float *v_err, int64_t n) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+        k_err[i] = 0.0f;
+        v_err[i] = 0.0f;
+    }
+}
+
+hipError_t launch_zero_stats(float *k_err, float *v_err, int64_t n, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    const int64_t want = (n + 255) / 256;
+    const unsigned grid = (unsigned)(want < 1024 ? want : 1024);
+    hipLaunchKernelGGL(zero_stats_kernel, dim3(grid), dim3(256), 0, s, k_err, v_err, n);
+    return hipGetLastError();
+}
+
 hipError_t launch_append(const AppendArgs &a, int batch, int64_t nblk, hipStream_t s) {
     dim3 grid((unsigned)nblk, (unsigned)a.hkv, (unsigned)batch);
     if (a.key_rot)

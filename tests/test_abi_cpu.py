@@ -72,6 +72,17 @@ def test_append_validation():
     assert L().kvq_quantize_append(ctypes.byref(c), 1, None) == INVALID
 
 
+def test_reset_validation():
+    # every case fails before anything is enqueued, and length is kept
+    for kw, status in [({"batch": 0}, INVALID), ({"capacity": 100}, INVALID), ({"head_dim": 64}, UNSUPPORTED),
+                       ({"k_err": None}, INVALID), ({"v_err": None}, INVALID),
+                       ({"k_err": FAKE + 2}, ALIGNMENT), ({"v_err": FAKE + 1}, ALIGNMENT)]:
+        c = cache(cap=256, length=100, **kw)
+        assert L().kvq_cache_reset(ctypes.byref(c), None) == status, kw
+        assert c.length == 100
+    assert L().kvq_cache_reset(None, None) == INVALID
+
+
 @pytest.mark.parametrize("q_heads,tk,tv,status", [
     (3, 0.0, 0.0, INVALID),           # not a multiple of kv_heads (4)
     (4 * 17, 0.0, 0.0, UNSUPPORTED),  # G = 17 > 16
@@ -141,3 +152,14 @@ def test_codec_validation():
     assert L().kvq_cache_bytes(ctypes.byref(cache(codec=1)), out) == OK
     assert L().kvq_cache_bytes(ctypes.byref(cache(codec=2)), out) == UNSUPPORTED
     assert L().kvq_quantize_append(ctypes.byref(cache(codec=-1)), 1, None) == UNSUPPORTED
+
+
+def test_library_matches_sources(monkeypatch):
+    # the loaded library was built from the present sources; one built from
+    # other sources is refused rather than loaded
+    assert kvq._build.is_current()
+    monkeypatch.setattr(kvq._build, "source_hash", lambda: "0" * 64)
+    assert not kvq._build.is_current()
+    monkeypatch.setattr(kvq, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built from the present sources"):
+        kvq.lib()

@@ -140,3 +140,28 @@ def make(w: Workload, device="cpu"):
                     k[b, h, tok[i]] = u * (w.needle_dot * (1 - i / (4 * w.needles)) / dmin)
 
     return dict(q=q.half(), k16=k.half(), v16=v.half())
+
+
+def needle_over_haystack(T, sm, seed=2001, needle_nats=17.0, offset=1.0, G=1, device="cpu"):
+    """One (batch, KV head) group of T tokens: a haystack of N(0,1) keys (so
+    logits sm * q.k about N(0,1)) whose values carry a per-channel mean offset
+    of +-offset (seeded signs) plus N(0, 0.25^2) noise, and one needle at a
+    seeded position whose key lies along the unit sum u of the group's G
+    queries, scaled so that its smallest logit over the heads is needle_nats,
+    with N(0,1) values.  Returns dict(q, k16, v16, needle) as fp16 tensors of
+    shapes [1][G][128], [1][1][cap][128] and the needle's position."""
+    g = _gen(device, seed)
+    cap = (T + BLK - 1) // BLK * BLK
+    q = _normal((1, G, D), g, device)
+    k = torch.zeros((1, 1, cap, D), dtype=torch.float32, device=device)
+    v = torch.zeros((1, 1, cap, D), dtype=torch.float32, device=device)
+    k[0, 0, :T] = _normal((T, D), g, device)
+    signs = torch.where(_normal((D,), g, device) >= 0, 1.0, -1.0)
+    v[0, 0, :T] = offset * signs + 0.25 * _normal((T, D), g, device)
+    pos = int(torch.randint(0, T, (1,), generator=g, device=device))
+    u = q[0].sum(0)
+    u = u / u.norm()
+    dmin = float((q[0] @ u).min().clamp(min=1e-3))
+    k[0, 0, pos] = u * (needle_nats / (sm * dmin))
+    v[0, 0, pos] = _normal((D,), g, device)
+    return dict(q=q.half(), k16=k.half(), v16=v.half(), needle=pos)
