@@ -63,6 +63,9 @@ def lib():
         L.kvqo_certificate.argtypes = [i32, i32, i32, i64, i64, P, f32, f32, f32, ctypes.c_double,
                                        P, P, P, P, P, P, P, P, P, P, P, P, P, i32]
         L.kvqo_certificate.restype = None
+        L.kvqo_certify_masked.argtypes = [i32, i32, i32, i64, i64, P, f32, P, ctypes.c_double, P,
+                                          P, P, P, P, P, P, P, P, P, P, P, P, P, i32]
+        L.kvqo_certify_masked.restype = None
         dbl = ctypes.c_double
         L.kvqo_adaptive.argtypes = [i32, i32, i32, i64, i64, P, f32, f32, f32, dbl, dbl, dbl, dbl] + [P] * 20 + [i32]
         L.kvqo_quant_k_row_rot.argtypes = [P, P, P, P]
@@ -232,6 +235,27 @@ class Cache:
                                _p(r["e_val"]), _p(r["recomputed"]), int(self.key_rotation))
         return r
 
+
+    def certify_masked(self, q, sm, masks, tau_out=float("inf"), force=None):
+        """As certificate, under fallback masks given by the caller (uint8
+        [B][Hkv][nblocks]) instead of the bounds' masks, with the FP16
+        recompute also forced where force (uint8 [B][Hq], optional) is set."""
+        q = _c(q, np.float16)
+        B, Hq, d = q.shape
+        assert B == self.B and d == D and Hq % self.Hkv == 0
+        nb = self.nblocks
+        m = np.zeros((B, self.Hkv, max(nb, 1)), np.uint8)
+        m[:, :, :nb] = np.asarray(masks, np.uint8)[:, :, :nb]
+        f = None if force is None else _c(np.asarray(force, np.uint8).reshape(B, Hq), np.uint8)
+        r = {k: np.zeros((B, Hq), np.float64) for k in ("cert", "e_key", "e_val")}
+        r["out"] = np.zeros((B, Hq, D), np.float64)
+        r["recomputed"] = np.zeros((B, Hq), np.uint8)
+        lib().kvqo_certify_masked(B, Hq, self.Hkv, self.cap, self.length, _p(q), sm, _p(m), float(tau_out),
+                                  None if f is None else _p(f), _p(self.k16), _p(self.v16), _p(self.k_codes),
+                                  _p(self.k_scales), _p(self.v_codes), _p(self.v_scales), _p(self.k_err),
+                                  _p(self.v_err), _p(r["out"]), _p(r["cert"]), _p(r["e_key"]),
+                                  _p(r["e_val"]), _p(r["recomputed"]), int(self.key_rotation))
+        return r
 
     def adaptive(self, q, sm, tau_k, tau_v, tau_cov, tau_vc=float("inf"), tau_rank=1.0, tau_out=float("inf")):
         """Adaptive precision with the ranking check and rungs 1-3 (see

@@ -691,6 +691,22 @@ static void certify_masked(int B, int Hq, int Hkv, int64_t cap, int64_t length, 
         }
 }
 
+/* The decode, certificate and rung-3 recompute under fallback masks given by
+ * the caller (m: uint8 [B][Hkv][nblk], bit 0 keys, bit 1 values from FP16)
+ * rather than formed from the bounds, with the recompute also forced where
+ * force[b][h] is set (force may be NULL).  Lets a caller evaluate the method
+ * under another side's decisions (promotions taken on fp32 block masses). */
+void kvqo_certify_masked(int B, int Hq, int Hkv, int64_t cap, int64_t length, const uint16_t *q,
+                         float sm, const uint8_t *m, double tau_out, const uint8_t *force,
+                         const uint16_t *k16, const uint16_t *v16, const int8_t *k_codes,
+                         const uint16_t *k_scales, const uint8_t *v_codes, const uint16_t *v_scales,
+                         const float *k_err, const float *v_err, double *out, double *cert,
+                         double *e_key, double *e_val, uint8_t *recomputed, int key_rot)
+{
+    certify_masked(B, Hq, Hkv, cap, length, q, sm, m, tau_out, force, k16, v16, k_codes, k_scales,
+                   v_codes, v_scales, k_err, v_err, out, cert, e_key, e_val, recomputed, key_rot);
+}
+
 /* -------------------------------------------------------- adaptive precision */
 
 /* Block log-masses of one (b, query head) over blocks [0, nblk):

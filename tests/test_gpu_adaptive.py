@@ -5,11 +5,15 @@ The promotions and the ranking are decisions the GPU takes on fp32 block
 masses and the oracle on fp64 ones, so near the boundary either side of a
 tie is correct.  The checks therefore bracket the GPU: its masks must lie
 between the oracle's masks at tau_cov - DELTA (and tau_vc * (1 + DELTA)) and
-at tau_cov + DELTA (tau_vc * (1 - DELTA)); its promoted counts likewise; its
-discordant-pair counts may differ from the oracle's by at most the pairs the
-oracle finds within EPS of a tie, and its flags must match wherever that
-margin cannot cross tau_rank.  Where a group's masks equal the oracle's,
-outputs (2e-3) and certificates (1e-3 relative) are compared too.  The
+at tau_cov + DELTA (tau_vc * (1 - DELTA)), DELTA = 1e-5 in cumulative mass
+(fp32 sums of at most a few thousand block masses are good to about 1e-6);
+its promoted counts likewise; its discordant-pair counts may differ from the
+oracle's by at most the pairs the oracle finds within EPS of a tie, and its
+flags must match wherever that margin cannot cross tau_rank.  Every group's
+outputs (2e-3) and certificates (1e-3 relative) are then compared with the
+oracle evaluated under the GPU's own masks and recompute decisions
+(certify_masked), so that no group goes unchecked where the two sides' fp32
+and fp64 promotions legitimately differ.  The
 planted needle case (an outlier channel the query ignores reorders two
 blocks under INT8) must be flagged and recomputed to dense attention.
 Method: "Runtime-Certified Bounded-Error Quantized Attention", Methodology 3
@@ -29,7 +33,7 @@ from kvq_testlib import OUT_TOL, SM, gpu_cache, normwise_err, oracle_cache, smal
 pytestmark = pytest.mark.gpu
 
 INF = float("inf")
-DELTA = 1e-3  # cumulative-mass margin of the promotion bracket
+DELTA = 1e-5  # cumulative-mass margin of the promotion bracket
 EPS = 1e-3    # natural-log margin of a near tie in the ranking check
 
 
@@ -68,9 +72,9 @@ def _run(name, d, w, T, frac, tau_cov, tau_vc=INF, tau_rank=1.0, tau_out=INF, ap
     ks = g["kstar"].cpu().numpy()
     assert np.all(lo["kstar"] <= ks) and np.all(ks <= hi["kstar"])
     same = np.all(m == ref["masks"], axis=-1)  # [B][Hkv]: groups decided alike
+    print(f"  groups with the oracle's masks: {same.mean():.3f}", flush=True)
     if exact:
         assert same.all()
-    assert same.mean() >= 0.75, f"only {same.mean():.2f} of the groups match the oracle's masks"
     # ranking check where the head promotes the oracle's set
     nd = g["ndisc"].cpu().numpy()
     rec = g["recomputed"].cpu().numpy()
@@ -91,16 +95,18 @@ def _run(name, d, w, T, frac, tau_cov, tau_vc=INF, tau_rank=1.0, tau_out=INF, ap
                 assert rec[b, h] == int(lo_flag), (b, h)
             checked += 1
     assert checked > 0
-    # outputs and certificates where the masks and recompute decisions agree
+    # every group: outputs and certificates against the oracle under the
+    # GPU's masks, recomputing exactly the heads the GPU recomputed
     out = g["out"].float().cpu().numpy()
     cert = g["cert"].cpu().numpy().astype(np.float64)
-    for b in range(w.B):
-        for h in range(w.Hq):
-            if not same[b, h // w.G] or rec[b, h] != ref["recomputed"][b, h]:
-                continue
-            err = normwise_err(out[b, h], ref["out"][b, h])
-            assert np.isfinite(err) and err <= OUT_TOL, (b, h, err)
-            np.testing.assert_allclose(cert[b, h], ref["cert"][b, h], rtol=1e-3, atol=1e-9)
+    under = oc.certify_masked(q, SM, m, INF, force=rec)
+    err = normwise_err(out, under["out"])
+    assert np.all(np.isfinite(err)) and err.max() <= OUT_TOL, (np.unravel_index(err.argmax(), err.shape), err.max())
+    np.testing.assert_allclose(cert, under["cert"], rtol=1e-3, atol=1e-9)
+    # the certificate rung under those masks: heads clear of tau_out by the
+    # certificate's tolerance take the oracle's decision
+    if tau_out != INF:
+        assert np.all(rec[under["cert"] > tau_out * (1 + 1e-3)] == 1)
     return ref, g
 
 
@@ -186,3 +192,11 @@ def test_ranking_check_over_many_promoted_blocks():
     w = small("llama3_8b_32k", B=1, T=80000)
     ref, g = _run(w.name, workloads.make(w), w, w.T, w.fallback_frac, 0.9999, tau_rank=0.3)
     assert g["kstar"].cpu().numpy().max() > 1024
+
+
+def test_selection_beyond_the_register_path():
+    # more than 2048 blocks per head: the selection keeps its block masses in
+    # LDS instead of registers
+    w = small("llama3_8b_32k", B=1, Hkv=2, Hq=8, T=140000)
+    ref, g = _run(w.name, workloads.make(w), w, w.T, w.fallback_frac, 0.99, tau_rank=0.3)
+    assert (w.T + 63) // 64 > 2048 and g["kstar"].cpu().numpy().max() > 0

@@ -110,8 +110,8 @@ def test_rotated_adaptive_bracketed():
     oc = oracle_cache(d, w.T, key_rotation=True)
     q = d["q"].numpy()
     tk, tv = taus_for(oc, q, w.fallback_frac)
-    lo = oc.adaptive(q, SM, tk, tv, 0.995 - 1e-3, tau_rank=0.3)
-    hi = oc.adaptive(q, SM, tk, tv, 0.995 + 1e-3, tau_rank=0.3)
+    lo = oc.adaptive(q, SM, tk, tv, 0.995 - 1e-5, tau_rank=0.3)
+    hi = oc.adaptive(q, SM, tk, tv, 0.995 + 1e-5, tau_rank=0.3)
     ref = oc.adaptive(q, SM, tk, tv, 0.995, tau_rank=0.3)
     c = gpu_cache(d, w.T, key_rotation=True)
     nb = (w.T + 63) // 64
@@ -120,14 +120,14 @@ def test_rotated_adaptive_bracketed():
     torch.cuda.synchronize()
     m = mask.cpu().numpy()
     assert np.all((lo["masks"] & 1) <= (m & 1)) and np.all((m & 1) <= (hi["masks"] & 1))
-    same = np.all(m == ref["masks"], axis=-1)
-    assert same.mean() >= 0.75
+    # every group against the oracle under the GPU's masks and recompute
+    # decisions (fp32 and fp64 promotions may legitimately differ at ties)
     out = g["out"].float().cpu().numpy()
     rec = g["recomputed"].cpu().numpy()
-    for b in range(w.B):
-        for h in range(w.Hq):
-            if same[b, h // w.G] and rec[b, h] == ref["recomputed"][b, h]:
-                assert normwise_err(out[b, h], ref["out"][b, h]) <= OUT_TOL
+    under = oc.certify_masked(q, SM, m, float("inf"), force=rec)
+    err = normwise_err(out, under["out"])
+    assert np.all(np.isfinite(err)) and err.max() <= OUT_TOL, f"{err.max():.3e}"
+    np.testing.assert_allclose(g["cert"].cpu().numpy().astype(np.float64), under["cert"], rtol=1e-3, atol=1e-9)
 
 
 def test_valu_kernel_refuses_rotated_cache():

@@ -184,3 +184,46 @@ def test_recompute_rung_gives_dense_heads():
     np.testing.assert_allclose(r["out"][sel], dense[sel], rtol=0, atol=1e-12)
     np.testing.assert_array_equal(r["out"][~sel], base["out"][~sel])
     np.testing.assert_array_equal(r["cert"], base["cert"])
+
+
+# ------------------------------------------- under masks given by the caller
+
+def _sdpa64_kv(q, k, v, G):
+    qt = torch.from_numpy(q.astype(np.float64))[:, :, None, :]
+    kt = torch.from_numpy(k.astype(np.float64)).repeat_interleave(G, dim=1).contiguous()
+    vt = torch.from_numpy(v.astype(np.float64)).repeat_interleave(G, dim=1).contiguous()
+    return torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=SM)[:, :, 0, :].numpy()
+
+
+def test_certify_masked_against_sdpa():
+    """certify_masked under caller masks: all blocks on FP16 is dense SDPA
+    with a zero certificate; all blocks certified is SDPA over the
+    dequantized keys (codes x scale) and values (nibbles x group scale);
+    keys on FP16 with certified values is SDPA over FP16 keys and
+    dequantized values; the bounds' own masks reproduce certificate(); a
+    forced head comes out dense."""
+    w, q, k16, v16 = case("llama3_8b_32k", B=2, T=333)
+    oc = oracle.Cache(k16, v16, w.T)
+    T, nb = w.T, oc.nblocks
+    kq = oc.k_codes[:, :, :T].astype(np.float64) * oc.k_scales[:, :, :T, None].astype(np.float64)
+    vq = oc.v_codes_unpacked()[:, :, :T].astype(np.float64) * \
+        np.repeat(oc.v_scales[:, :, :T].astype(np.float64), 32, axis=-1)
+    k, v = k16[:, :, :T], v16[:, :, :T]
+    shape = (w.B, w.Hkv, nb)
+    for bits, kk, vv in [(3, k, v), (0, kq, vq), (1, k, vq), (2, kq, v)]:
+        r = oc.certify_masked(q, SM, np.full(shape, bits, np.uint8))
+        np.testing.assert_allclose(r["out"], _sdpa64_kv(q, kk, vv, w.G), rtol=0, atol=1e-12)
+        if bits == 3:
+            assert np.all(r["cert"] == 0)
+        assert not r["recomputed"].any()
+    tk, tv = taus(oc, q, 0.1)
+    _, _, m = oc.bounds(q, SM, tk, tv)
+    r = oc.certify_masked(q, SM, m)
+    c = oc.certificate(q, SM, tk, tv)
+    for key in ("out", "cert", "e_key", "e_val", "recomputed"):
+        np.testing.assert_array_equal(r[key], c[key])
+    force = np.zeros((w.B, w.Hq), np.uint8)
+    force[1, 5] = 1
+    r = oc.certify_masked(q, SM, np.zeros(shape, np.uint8), force=force)
+    assert r["recomputed"].sum() == 1 and r["recomputed"][1, 5] == 1
+    np.testing.assert_allclose(r["out"][1, 5], sdpa64(q, k16, v16, w.G, T)[1, 5], rtol=0, atol=1e-12)
