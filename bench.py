@@ -8,8 +8,9 @@ the online softmax and the merge of the splits, by the last workgroup of each
 first).  Inputs are resident in HBM when
 the timed region starts.  Several layers' caches ("replicas") are cycled so
 that consecutive steps never find their KV stream in the 256 MB Infinity
-Cache, as in a real multi-layer decode; by default the steps of those
-layers are captured in one HIP graph, replayed steps / layers times.
+Cache, as in a real multi-layer decode; by default the steps of up to 32
+layers (cycling those caches) are captured in one HIP graph, as a 32-layer
+decoder's per-token graph holds its layers, and replayed.
 
 Prints one JSON line:
   value      effective KV bandwidth of the step: algorithmic bytes / step time
@@ -76,7 +77,7 @@ def parse():
     p.add_argument("--unfused", action="store_true",
                    help="step as two calls (kvq_quantize_append, kvq_decode_attn) instead of kvq_append_decode")
     p.add_argument("--graph", type=int, default=1,
-                   help="1: replay the steps from captured HIP graphs (the cycled layers' steps in one graph); "
+                   help="1: replay the steps from captured HIP graphs (up to 32 layer steps in one graph); "
                         "0: eager launches")
     p.add_argument("--no-certify", action="store_true",
                    help="skip timing the step with the per-head output certificate (kvq_decode_attn_cert)")
@@ -237,14 +238,22 @@ def bench_quantize(args, w):
     }), flush=True)
 
 
+GRAPH_STEPS = 32  # layer steps per captured graph: a Llama-3-8B per-token graph holds 32 layers
+
+
+def graph_steps(args):
+    return min(args.steps, GRAPH_STEPS)
+
+
 def timed_steps(args, R, step, stream):
     """Milliseconds per step over exactly args.steps steps (step(i, stream)
     launches step i on layer cache i % R), after args.warmup untimed ones:
     (host wall clock between synchronisations, HIP events recorded on the
     stream the steps run on, right before the first and after the last).
-    With args.graph, the R layers' steps are captured in one HIP graph
-    (plus one of the first steps % R layers) and replayed; otherwise every
-    step is launched eagerly."""
+    With args.graph, the steps of up to 32 layers (cycling the R layer
+    caches) are captured in one HIP graph, as a decoder's per-token graph
+    holds its layers, plus one graph of the remaining steps, and replayed;
+    otherwise every step is launched eagerly."""
     import torch
 
     for i in range(args.warmup):
@@ -252,6 +261,7 @@ def timed_steps(args, R, step, stream):
     torch.cuda.synchronize()
     if args.graph:
         side = torch.cuda.Stream()
+        n_g = graph_steps(args)
 
         def capture(n):
             g = torch.cuda.CUDAGraph()
@@ -259,18 +269,17 @@ def timed_steps(args, R, step, stream):
                 for r in range(n):
                     step(r, torch.cuda.current_stream())
             return g
-        full = capture(R)
-        rem = args.steps % R
+        full = capture(n_g)
+        rem = args.steps % n_g
         part = capture(rem) if rem else None
         torch.cuda.synchronize()
 
         def run_all():
-            for _ in range(args.steps // R):
+            for _ in range(args.steps // n_g):
                 full.replay()
             if part is not None:
                 part.replay()
-        for _ in range(max(1, args.warmup // R)):
-            full.replay()
+        full.replay()  # untimed: the graph's first replay
         torch.cuda.synchronize()
     else:
         def run_all():
@@ -477,9 +486,9 @@ def main():
     torch.cuda.synchronize()
 
     # timed loop: exactly `steps` steps between synchronisations, launched
-    # eagerly or replayed from captured HIP graphs (append + decode + merge of
-    # each of the R layers in one graph, as a decoder's per-token graph holds
-    # every layer)
+    # eagerly or replayed from captured HIP graphs (the fused step of up to 32
+    # layers in one graph, cycling the R layer caches, as a decoder's
+    # per-token graph holds every layer)
     ms_step, ms_step_ev = timed_steps(args, R, lambda i, strm: step(i, strm=strm), stream)
 
     # the dominant kernel's launch time.  The fused step on the matrix-core
@@ -563,7 +572,7 @@ def main():
             "fallback_blocks_value": round(float(((m >> 1) & 1).mean()), 5),
             "tau_k": tau_k if np.isfinite(tau_k) else "inf", "tau_v": tau_v if np.isfinite(tau_v) else "inf",
             "layers_cycled": R,
-            "kernel": args.kernel, "splits": args.splits, "hip_graph": bool(args.graph), "steps_per_graph": R if args.graph else None,
+            "kernel": args.kernel, "splits": args.splits, "hip_graph": bool(args.graph), "steps_per_graph": graph_steps(args) if args.graph else None,
             "fused_append": not args.unfused,
             "tier2": args.tier2,
             "key_codec": "rotate_k (tolerances of the plain codec)" if args.key_rotation else "plain",

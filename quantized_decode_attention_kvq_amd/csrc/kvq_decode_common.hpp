@@ -46,6 +46,8 @@ __device__ __forceinline__ void compute_masks(const DecodeArgs &a, int64_t bh, i
     __syncthreads();
 }
 
+constexpr int FOLD_REG = 8;  // split counts the split merge handles in registers
+
 // Device-coherent (agent-scope) stores and loads: values written by one
 // workgroup and read by another of the same launch, which may run on another
 // XCD with its own L2.
@@ -75,24 +77,36 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 // Writes this workgroup's partial (running max, running sum, unnormalised
 // accumulator) of split `split` for the G heads of (b, kvh).  Running maxima
-// are in log2 units (scores scaled by sm * log2(e)).  wm/wl: [nw][16]
-// per-wave running max/sum, wacc: [nw][gp][128] per-wave accumulators, all in
-// LDS and complete (a barrier has been passed) on entry.
-__device__ __forceinline__ void write_partial(const DecodeArgs &a, int64_t bh, int split, int nw,
-                                              int gp, const float (*wm)[16], const float (*wl)[16],
+// are in log2 units (scores scaled by sm * log2(e)).  wm/wl: [NWT][16]
+// per-wave running max/sum, wacc: [NWT][gp][128] per-wave accumulators, all in
+// LDS and complete (a barrier has been passed) on entry.  Each thread reads
+// its NWT values of each array before any arithmetic (one LDS round trip),
+// then combines them in wave order.
+template <int NWT>
+__device__ __forceinline__ void write_partial(const DecodeArgs &a, int64_t bh, int split, int gp,
+                                              const float (*wm)[16], const float (*wl)[16],
                                               const float *wacc) {
     const int g = a.g;
     for (int idx = threadIdx.x; idx < g * D; idx += blockDim.x) {
         const int h = idx / D, j = idx % D;
+        float mw[NWT], lw[NWT], aw[NWT];
+#pragma unroll
+        for (int w = 0; w < NWT; ++w) {
+            mw[w] = wm[w][h];
+            lw[w] = wl[w][h];
+            aw[w] = wacc[(w * gp + h) * D + j];
+        }
         float M = -__builtin_huge_valf();
-        for (int w = 0; w < nw; ++w) M = fmaxf(M, wm[w][h]);
+#pragma unroll
+        for (int w = 0; w < NWT; ++w) M = fmaxf(M, mw[w]);
         float L = 0.0f, A = 0.0f;
         if (M != -__builtin_huge_valf()) {
-            for (int w = 0; w < nw; ++w) {
-                if (wm[w][h] == -__builtin_huge_valf()) continue;
-                const float f = __builtin_amdgcn_exp2f(wm[w][h] - M);
-                L += wl[w][h] * f;
-                A += wacc[(w * gp + h) * D + j] * f;
+#pragma unroll
+            for (int w = 0; w < NWT; ++w) {
+                if (mw[w] == -__builtin_huge_valf()) continue;
+                const float f = __builtin_amdgcn_exp2f(mw[w] - M);
+                L += lw[w] * f;
+                A += aw[w] * f;
             }
         }
         const int64_t p = (bh * a.splits + split) * g + h;
@@ -132,9 +146,50 @@ __device__ __forceinline__ void fold_merge(const DecodeArgs &a, int64_t bh, int6
     __syncthreads();
     if (!last_lds) return;
     const int g = a.g, S = a.splits, nt = blockDim.x;
+    const float2 *pml = a.part_ml + bh * S * g;                  // split s, head h at [s * g + h]
+    const float *pacc = a.part_acc + bh * S * g * D;             // split s, head h, channel j at [(s g + h) D + j]
+    if (S <= FOLD_REG) {
+        // up to FOLD_REG splits: each thread loads its head's (m, l) of every
+        // split and its channel's accumulators at once (one round of
+        // device-coherent loads), then merges in split order
+        for (int i = threadIdx.x; i < g * D; i += nt) {
+            const int h = i / D, j = i % D;
+            float ms[FOLD_REG], ls[FOLD_REG], as[FOLD_REG];
+#pragma unroll
+            for (int s_ = 0; s_ < FOLD_REG; ++s_) {
+                if (s_ < S) {
+                    const float *e = reinterpret_cast<const float *>(pml + s_ * g + h);
+                    ms[s_] = ld_agent(e);
+                    ls[s_] = ld_agent(e + 1);
+                    as[s_] = ld_agent(pacc + ((int64_t)s_ * g + h) * D + j);
+                }
+            }
+            float M = NEG_INF;
+#pragma unroll
+            for (int s_ = 0; s_ < FOLD_REG; ++s_)
+                if (s_ < S) M = fmaxf(M, ms[s_]);
+            float L = 0.0f;
+            if (M != NEG_INF) {
+#pragma unroll
+                for (int s_ = 0; s_ < FOLD_REG; ++s_)
+                    if (s_ < S && ms[s_] != NEG_INF) L += ls[s_] * __builtin_amdgcn_exp2f(ms[s_] - M);
+            }
+            float o = 0.0f;
+#pragma unroll
+            for (int s_ = 0; s_ < FOLD_REG; ++s_) {
+                if (s_ < S) {
+                    const float w = (L > 0.0f && ms[s_] != NEG_INF) ? __builtin_amdgcn_exp2f(ms[s_] - M) / L : 0.0f;
+                    o += w * as[s_];
+                }
+            }
+            a.out[(b * a.hq + kvh * g + h) * D + j] = (uint16_t)f2h_rn(o);
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) __hip_atomic_store(a.arrive + bh, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
     float2 *wml = reinterpret_cast<float2 *>(lds);               // [G][S] (m, l) of every split
     float2 *hml = reinterpret_cast<float2 *>(lds) + g * S;       // [G] (M, L)
-    const float2 *pml = a.part_ml + bh * S * g;                  // split s, head h at [s * g + h]
     for (int i = threadIdx.x; i < g * S; i += nt) {
         const int h = i / S, s_ = i % S;
         const float *e = reinterpret_cast<const float *>(pml + s_ * g + h);
@@ -151,7 +206,6 @@ __device__ __forceinline__ void fold_merge(const DecodeArgs &a, int64_t bh, int6
         hml[h] = make_float2(M, L);
     }
     __syncthreads();
-    const float *pacc = a.part_acc + bh * S * g * D;             // split s, head h, channel j at [(s g + h) D + j]
     for (int i = threadIdx.x; i < g * D; i += nt) {
         const int h = i / D, j = i % D;
         const float M = hml[h].x, L = hml[h].y;

@@ -987,7 +987,7 @@ __device__ __forceinline__ void decode_group(const DecodeArgs &a, const int spli
         }
     }
     __syncthreads();
-    write_partial(a, bh, split, NW, 16, wm, wl, wacc);
+    write_partial<NW>(a, bh, split, 16, wm, wl, wacc);
     if (!CERT && a.arrive) {
         __syncthreads();  // the wave merge's LDS is read; the ring is free for the split merge
         fold_merge(a, bh, b, kvh, &ring[0][0][0]);
@@ -1457,7 +1457,7 @@ __device__ __forceinline__ void decode_group_stream(const DecodeArgs &a, const i
         }
     }
     __syncthreads();
-    write_partial(a, bh, split, NW, 16, wm, wl, wacc);
+    write_partial<NW>(a, bh, split, 16, wm, wl, wacc);
     if (a.arrive) {
         __syncthreads();  // the wave merge's LDS is read; the ring is free for the split merge
         fold_merge(a, bh, b, kvh, &ring[0][0][0]);

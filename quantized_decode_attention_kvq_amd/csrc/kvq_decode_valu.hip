@@ -254,7 +254,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
         }
     }
     __syncthreads();
-    write_partial(a, bh, split, NW, GP, wm, wl, wacc);
+    write_partial<NW>(a, bh, split, GP, wm, wl, wacc);
 }
 
 // ------------------------------------------------------------ split merge
