@@ -30,12 +30,17 @@
 //   that the C registers of subtiles 0 and 1 provide.
 //
 // Grid (splits, Hkv, B), NW = 8 waves, one workgroup per CU (two waves per
-// SIMD: one wave's VALU and matrix work hides the other's latencies).  After
-// the fallback masks of its (b, kvh) are known, a workgroup takes an equal
-// share of the group's work in steps, in block order, lists the blocks the
-// share touches, and its waves claim the share's steps one at a time from
-// an LDS counter at issue time, so that the waves of a workgroup finish
-// together however the fallback blocks fall.  Each wave streams its steps
+// SIMD: one wave's VALU and matrix work hides the other's latencies).  Two
+// variants.  The general one (decode_group): after the fallback masks of its
+// (b, kvh) are known, a workgroup takes an equal share of the group's work in
+// steps, in block order, lists the blocks the share touches, and its waves
+// claim the share's steps one at a time from an LDS counter at issue time, so
+// that the waves of a workgroup finish together however the fallback blocks
+// fall.  The streaming one (decode_group_stream, up to STREAM_MAX_NB blocks,
+// no certificate or promotions): the first half-blocks of each split's home
+// range are copied before the masks are known, the rest of the group's work
+// is cut into equal ranges of a step pool, and blocks are found from 64-block
+// windows instead of a table.  Each wave streams its steps
 // through its own 3-stage LDS ring: the quantized data of a half (4 KB key
 // codes, 2 KB value codes, key and value scales) is copied HBM -> LDS by
 // global_load_lds (no registers held while in flight), so two halves are in
@@ -48,7 +53,9 @@
 // step, of either kind, issues exactly 8 copy instructions, so the waits
 // stay compile-time constants, and no global load is ever waited on while
 // later steps are in flight.
-// Waves and splits are merged by log-sum-exp in a second kernel.
+// Waves are merged by log-sum-exp in LDS; the splits of a group are merged
+// by the last of its workgroups to finish, in the same launch (the
+// certificate path merges in a second kernel).
 #include "kvq_decode_common.hpp"
 #include "kvq_mfma.hpp"
 #include "kvq_quant_row.hpp"
