@@ -12,6 +12,11 @@ Cache, as in a real multi-layer decode; by default the steps of up to 32
 layers (cycling those caches) are captured in one HIP graph, as a 32-layer
 decoder's per-token graph holds its layers, and replayed.
 
+The GPU's power management holds a lower clock for the first milliseconds of
+sustained load (measured per launch: 1.6-2.4 GHz, and the decode kernel's time
+follows it), so the timed steps follow 20 ms of untimed replays of the same
+graph, as in a decoder that runs the step continuously.
+
 Prints one JSON line:
   value      effective KV bandwidth of the step: algorithmic bytes / step time
              (GB/s, 1e9 B/s); tokens_per_s and pct_of_hbm_peak beside it.
@@ -20,7 +25,9 @@ Prints one JSON line:
              matrix-core path the fused step is one kernel (append, decode,
              and the split merge done by the last workgroup of each group):
              its bytes are the step's, and its launch time comes from HIP
-             events on the stream around the timed loop.  Elsewhere (VALU
+             events on the stream around a second pass of the timed loop's
+             steps (queued behind a spin kernel, so that the span is the
+             kernels' own and not the host's submission latency).  Elsewhere (VALU
              kernel, --unfused) it is the split-K kernel: the decode's bytes
              but the output, timed by events around each of the same steps
              run again eagerly (the library records one after the split-K
@@ -120,17 +127,24 @@ def append_bytes(B, Hkv, n=1):
     return B * Hkv * n * (512 + 128 + 2 + 64 + 8 + 8)
 
 
-def traffic_from_counters(path=PROFILE_COUNTERS):
-    """HBM bytes per launch of the profiled kernel (the split-K decode, or
-    the bulk append for APPEND_COUNTERS): FETCH_SIZE + WRITE_SIZE, each scaled
-    by the same counter's reading on a plain 1 GiB copy, from the committed
-    rocprofv3 counter runs, or None when they are absent or were taken on
-    other kernel sources."""
+def traffic_from_counters(path=PROFILE_COUNTERS, kernel=None, workload=None, nbytes=None):
+    """HBM bytes per launch of the profiled kernel (the decode step, or the
+    bulk append for APPEND_COUNTERS): FETCH_SIZE + WRITE_SIZE, each scaled by
+    the same counter's reading on a plain 1 GiB copy, from the committed
+    rocprofv3 counter runs, or None when they are absent, were taken on other
+    kernel sources, or (when given) on another kernel, workload or byte
+    count per launch."""
     if not os.path.exists(path):
         return None
     try:
         c = json.load(open(path))
         if c.get("kernel_source_hash") != kernel_source_hash():
+            return None
+        if kernel is not None and c.get("kernel") != kernel:
+            return None
+        if workload is not None and c.get("workload") != workload:
+            return None
+        if nbytes is not None and int(c.get("algorithmic_bytes_per_launch", -1)) != int(nbytes):
             return None
         return float(c["hbm_bytes_per_launch"])
     except (OSError, ValueError, KeyError):
@@ -239,6 +253,7 @@ def bench_quantize(args, w):
 
 
 GRAPH_STEPS = 32  # layer steps per captured graph: a Llama-3-8B per-token graph holds 32 layers
+WARM_S = 0.02  # untimed replays before the timed steps, in seconds of sustained load
 
 
 def graph_steps(args):
@@ -247,9 +262,11 @@ def graph_steps(args):
 
 def timed_steps(args, R, step, stream):
     """Milliseconds per step over exactly args.steps steps (step(i, stream)
-    launches step i on layer cache i % R), after args.warmup untimed ones:
-    (host wall clock between synchronisations, HIP events recorded on the
-    stream the steps run on, right before the first and after the last).
+    launches step i on layer cache i % R), after args.warmup untimed ones and
+    20 ms of untimed replays (the GPU's clock settles under sustained load):
+    (host wall clock between synchronisations; HIP events recorded on the
+    stream around a second pass of the same steps, which a spin kernel ahead
+    of them keeps from starting before the steps are submitted).
     With args.graph, the steps of up to 32 layers (cycling the R layer
     caches) are captured in one HIP graph, as a decoder's per-token graph
     holds its layers, plus one graph of the remaining steps, and replayed;
@@ -279,20 +296,41 @@ def timed_steps(args, R, step, stream):
                 full.replay()
             if part is not None:
                 part.replay()
-        full.replay()  # untimed: the graph's first replay
+        # untimed: the graph's first replay, then replays for 20 ms, so that the
+        # timed steps run at the clock the GPU settles at under sustained load
+        # (it holds a lower one for the first milliseconds; a decoder serving
+        # tokens runs this step continuously)
+        full.replay()
         torch.cuda.synchronize()
+        tw = time.perf_counter()
+        while time.perf_counter() - tw < WARM_S:
+            full.replay()
+            torch.cuda.synchronize()
     else:
         def run_all():
             for i in range(args.steps):
                 step(i, stream)
+        tw = time.perf_counter()
+        while time.perf_counter() - tw < WARM_S:
+            run_all()
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    e0.record(torch.cuda.current_stream())
     run_all()
-    e1.record(torch.cuda.current_stream())
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / args.steps * 1e3
+    # the same steps again between HIP events, queued behind a short spin
+    # kernel: the first event is then taken once the host has submitted the
+    # steps, so the span is the kernels' own (back to back in a graph), not
+    # the host's submission latency before the first one
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    strm = torch.cuda.current_stream()
+    if hasattr(torch.cuda, "_sleep"):
+        torch.cuda._sleep(500000)  # about 0.2 ms of spinning at 2.4 GHz
+    e0.record(strm)
+    run_all()
+    e1.record(strm)
+    torch.cuda.synchronize()
     return wall, e0.elapsed_time(e1) / args.steps
 
 
@@ -502,8 +540,9 @@ def main():
     if one_kernel:
         split_ms = call_ms = ms_step_ev
         merge_ms = 0.0
-        launch_source = (f"HIP events on the stream around the timed loop's {args.steps} steps "
-                         f"({'graph-replayed' if args.graph else 'eager'}), one kernel per step")
+        launch_source = (f"HIP events on the stream around a second pass of the timed loop's {args.steps} "
+                         f"{'graph-replayed' if args.graph else 'eager'} steps, queued behind a spin kernel "
+                         "(so the span starts at the first kernel, not at the host's submission); one kernel per step")
     else:
         evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
         for e3 in evs:
@@ -545,10 +584,10 @@ def main():
     # output to the merge
     split_bytes = step_bytes if one_kernel else dec_bytes - w.B * w.Hq * 256
     split_gbs = split_bytes / (split_ms * 1e-3) / 1e9
-    traffic = traffic_from_counters()
     nblk = (w.T + 63) // 64
     kname = "decode_valu_kernel" if args.kernel == "valu" or w.G > 16 else (
         "decode_stream_kernel" if nblk <= 2048 and args.kernel != "mfma_table" else "decode_mfma_kernel")
+    traffic = traffic_from_counters(kernel=kname, workload=w.name, nbytes=split_bytes)
     line = {
         "metric": "quantized-KV decode attention: effective KV GB/s (% of HBM peak), tokens/s",
         "value": round(gbs, 2),
