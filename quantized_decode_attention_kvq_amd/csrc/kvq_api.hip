@@ -89,7 +89,8 @@ WsLayout ws_layout(const kvq_cache *c, int32_t g, int64_t splits, size_t slots) 
 
 // Adaptive workspace: the decode workspace, then [lhat float x B*Hq*NBc]
 // [phead uint8 x B*Hq*NBc] [promote uint8 x B*Hkv*NBc] [step statistics
-// float2 x B*Hkv*NBc*8*G], each padded to 256 B.
+// float2 x B*Hkv*G*NBc*8, each head's blocks and slots contiguous], each
+// padded to 256 B.
 struct AdaptLayout {
     size_t lhat, phead, promote, step, qrot, total;
 };

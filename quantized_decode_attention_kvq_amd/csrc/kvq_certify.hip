@@ -26,23 +26,28 @@ namespace kvq {
 
 namespace {
 
-// FP16 block log-mass (log2 units) of block i < nb for head hl of group bh,
-// from the decode's statistics of the block's valid 8-token slots (a
-// 16-token step fills its first slot and empties the second).  The loads
-// are unconditional (slots past the valid ones re-read the last valid one)
-// so that they issue together.
-__device__ __forceinline__ float fp16_block_logmass(const DecodeArgs &a, int64_t bh, int64_t i, int hl) {
-    constexpr float NEG_INF = -__builtin_huge_valf();
+// FP16 block log-mass (log2 units) of one block of one head: the log2 of
+// the sum over the block's valid 8-token slots of l * 2^m, from the
+// decode's statistics (m, l) of those slots (a 16-token step fills its first
+// slot and empties the second).  A head's slots are contiguous, 8 per block.
+__device__ __forceinline__ int block_slots(const DecodeArgs &a, int64_t i) {
     const int64_t left = a.length - i * BLK;
-    const int nst = left >= BLK ? 8 : (int)((left + 7) / 8);
-    const float2 *st = a.step_ml + (bh * a.nbc + i) * 8 * a.g + hl;
-    float2 p[8];
+    return left >= BLK ? 8 : (int)((left + 7) / 8);
+}
+
+__device__ __forceinline__ float block_logmass(const float4 (&p)[4], int nst) {
+    constexpr float NEG_INF = -__builtin_huge_valf();
+    float m[8], l[8], L[8], M = NEG_INF;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) p[k] = st[(k < nst ? k : nst - 1) * a.g];
-    float L[8], M = NEG_INF;
+    for (int k = 0; k < 4; ++k) {
+        m[2 * k] = p[k].x;
+        l[2 * k] = p[k].y;
+        m[2 * k + 1] = p[k].z;
+        l[2 * k + 1] = p[k].w;
+    }
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-        L[k] = (k < nst && p[k].y > 0.0f) ? p[k].x + __log2f(p[k].y) : NEG_INF;
+        L[k] = (k < nst && l[k] > 0.0f) ? m[k] + __log2f(l[k]) : NEG_INF;
         M = fmaxf(M, L[k]);
     }
     if (M == NEG_INF) return NEG_INF;
@@ -53,61 +58,147 @@ __device__ __forceinline__ float fp16_block_logmass(const DecodeArgs &a, int64_t
     return M + __log2f(s);
 }
 
-// Promoted blocks per head up to which the ranking check counts every pair.
-constexpr int PAIRWISE_MAX = 1024;
-
-// First index in [lo, hi) of an ascending run whose key is >= k (lower) or
-// > k (upper); keys (x, y) compare lexicographically, or by y alone when x
-// is null.
-template <bool UPPER>
-__device__ __forceinline__ int run_bound(const float *x, const float *y, int lo, int hi, float kx, float ky) {
-    while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        const float xm = x ? x[mid] : 0.0f, ym = y[mid];
-        const float kxx = x ? kx : 0.0f;
-        const bool before = UPPER ? (xm < kxx || (xm == kxx && ym <= ky)) : (xm < kxx || (xm == kxx && ym < ky));
-        if (before)
-            lo = mid + 1;
-        else
-            hi = mid;
-    }
-    return lo;
+// Order-preserving image of a float as an unsigned integer (-0 as +0):
+// for non-NaN a, b, a < b exactly when ord_key(a) < ord_key(b).
+__device__ __forceinline__ uint32_t ord_key(float x) {
+    uint32_t u = __float_as_uint(x);
+    if (u == 0x80000000u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// One bottom-up pass of a stable merge sort over n keys in LDS (run width w
-// to 2w): an element of a left run moves past the right run's smaller keys,
-// one of a right run past the left run's smaller or equal keys (binary
-// searches, so every element is placed independently).  With x null the key
-// is y alone, and the return value counts, over this thread's right-run
-// elements, the left-run keys strictly above them: summed over the passes,
-// the inversions of the sequence.
-__device__ __forceinline__ int merge_pass(const float *x, const float *y, float *nx, float *ny, int n, int w) {
+// Thread t's blocks are t, t + 256, t + 512, ...  The promoted flag, INT8
+// log-mass and FP16 log-mass of its blocks c, c + 256, ..., c + 256 (KR - 1),
+// every load issued before any is used; blocks at or past nb re-read block
+// nb - 1 and come back unpromoted.
+template <int KR>
+__device__ __forceinline__ void load_blocks(const DecodeArgs &a, const uint8_t *ph, const float *lh, const float4 *sth,
+                                            int c, int nb, bool *fr, float *ar, float *fpr) {
+    uint8_t f[KR];
+    float4 p[KR][4];
+#pragma unroll
+    for (int k = 0; k < KR; ++k) {
+        const int i = c + 256 * k < nb ? c + 256 * k : nb - 1;
+        f[k] = ph[i];
+        ar[k] = lh[i];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) p[k][u] = sth[4 * i + u];
+    }
+#pragma unroll
+    for (int k = 0; k < KR; ++k) {
+        const int i = c + 256 * k < nb ? c + 256 * k : nb - 1;
+        fr[k] = (c + 256 * k < nb) & (f[k] != 0);
+        fpr[k] = block_logmass(p[k], block_slots(a, i));
+    }
+}
+
+// Promoted blocks per head up to which the ranking check counts every pair.
+constexpr int PAIRWISE_MAX = 256;
+
+// One pass (runs of w to 2w, w a power of two) of a bottom-up stable merge
+// sort of n keys in LDS, held in arrays padded from n up to the next power
+// of two with keys above every real one.  Each element counts, by binary
+// lifting over the whole sibling run (log2(w) + 1 steps, one LDS read
+// each), the sibling keys that go before it -- smaller ones for an element
+// of a left run, smaller or equal ones for an element of a right run -- and
+// moves past them.  E elements per thread (c + tid + 256 e) search together.
+// Returns, over this thread's right-run elements, the left-run keys strictly
+// above them: summed over the passes, the strict inversions of the sequence.
+template <typename Key, int E>
+__device__ __forceinline__ int merge_pass(const Key *src, Key *dst, int n, int w) {
+    constexpr uint32_t KB = sizeof(Key);
+    const char *sb = reinterpret_cast<const char *>(src);
     int inv = 0;
-    for (int i = threadIdx.x; i < n; i += blockDim.x) {
-        const int r0 = i / (2 * w) * (2 * w);
-        const int le = r0 + w < n ? r0 + w : n, re = r0 + 2 * w < n ? r0 + 2 * w : n;
-        const float kx = x ? x[i] : 0.0f, ky = y[i];
-        int dst;
-        if (i < le) {
-            dst = i + (run_bound<false>(x, y, le, re, kx, ky) - le);
-        } else {
-            const int ub = run_bound<true>(x, y, r0, le, kx, ky);
-            dst = r0 + (i - le) + (ub - r0);
-            inv += le - ub;
+    for (int c = 0; c < n; c += 256 * E) {
+        uint32_t off[E];  // byte offset of the sibling run's start plus the count so far
+        Key key[E], kk[E];
+        bool right[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const int i = c + (int)threadIdx.x + 256 * e;
+            const int ii = i < n ? i : n - 1;  // past the end: a copy of the last key, never written
+            const int r0 = ii & ~(2 * w - 1);
+            right[e] = ii - r0 >= w;
+            off[e] = (uint32_t)(right[e] ? r0 : r0 + w) * KB;  // the sibling run
+            key[e] = src[ii];
+            // "smaller or equal" as "smaller than key + 1" (no real key is the
+            // largest value of the type)
+            kk[e] = right[e] ? key[e] + 1 : key[e];
         }
-        if (x) nx[dst] = kx;
-        ny[dst] = ky;
+        for (int s = w >> 1; s >= 1; s >>= 1) {
+            const uint32_t step = (uint32_t)s * KB;
+            Key v[E];
+#pragma unroll
+            for (int e = 0; e < E; ++e) v[e] = *reinterpret_cast<const Key *>(sb + off[e] + step - KB);
+#pragma unroll
+            for (int e = 0; e < E; ++e) off[e] += v[e] < kk[e] ? step : 0u;
+        }
+        {
+            Key v[E];
+#pragma unroll
+            for (int e = 0; e < E; ++e) v[e] = *reinterpret_cast<const Key *>(sb + off[e]);
+#pragma unroll
+            for (int e = 0; e < E; ++e) off[e] += v[e] < kk[e] ? KB : 0u;
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const int i = c + (int)threadIdx.x + 256 * e;
+            if (i < n) {
+                const int r0 = i & ~(2 * w - 1);
+                const int pos = (int)(off[e] / KB) - (right[e] ? r0 : r0 + w);
+                dst[right[e] ? i - w + pos : i + pos] = key[e];
+                if (right[e]) inv += w - pos;
+            }
+        }
     }
     return inv;
 }
 
+// Both merge sorts of the ranking check with E elements per thread and
+// search: the (INT8, FP16) key pairs kp[0 .. n) by their 64-bit keys, then
+// their FP16 halves, counting strict inversions.  kp and kq are the pair
+// buffers (padded to np2); the FP16 halves use kq's memory.
+template <int E>
+__device__ __forceinline__ int sort_and_count(uint64_t *kp, uint64_t *kq, int n) {
+    uint64_t *src = kp, *dst = kq;
+    for (int w = 1; w < n; w *= 2) {
+        merge_pass<uint64_t, E>(src, dst, n, w);
+        __syncthreads();
+        uint64_t *t = src;
+        src = dst;
+        dst = t;
+    }
+    // src holds the pairs sorted by (INT8, FP16); dst's memory takes the two
+    // 32-bit buffers of the second sort (their padding written here too)
+    uint32_t *fs = reinterpret_cast<uint32_t *>(dst), *fd = fs + ADAPT_MAX_NB;
+    const int np2 = n > 1 ? 1 << (32 - __builtin_clz(n - 1)) : 1;
+    for (int i = threadIdx.x; i < np2; i += 256) {
+        fs[i] = i < n ? (uint32_t)src[i] : 0xFFFFFFFFu;
+        fd[i] = 0xFFFFFFFFu;
+    }
+    __syncthreads();
+    int cnt = 0;
+    for (int w = 1; w < n; w *= 2) {
+        cnt += merge_pass<uint32_t, E>(fs, fd, n, w);
+        __syncthreads();
+        uint32_t *t = fs;
+        fs = fd;
+        fd = t;
+    }
+    return cnt;
+}
+
 // Ranking-consistency check of one head (Methodology 3): its promoted blocks
-// are compacted into LDS with their INT8 and FP16 log-masses, the pairs
-// ordered oppositely are counted (every pair up to PAIRWISE_MAX blocks, by
-// merge sorts above), and the head is inconsistent when they exceed tau_rank
-// of all pairs.  All 256 threads take part; every thread returns the result.
-__device__ bool ranking_inconsistent(const DecodeArgs &a, int64_t bh, int64_t head, int hl, float *pa, float *pf,
-                                     float *qa, float *qf, int *wcnt, int *bcast) {
+// are compacted into LDS as keys pairing the order-preserving images of
+// their INT8 and FP16 log-masses, the pairs ordered oppositely by the two
+// are counted (every pair up to PAIRWISE_MAX blocks, by merge sorts above),
+// and the head is inconsistent when they exceed tau_rank of all pairs.  The
+// integer images compare exactly like the log-masses, so a pair is
+// discordant when one log-mass is strictly lower and the other strictly
+// higher (log-masses are finite or -inf here; a NaN, from non-finite
+// inputs, leaves the count unspecified).  All 256 threads take part; every
+// thread returns the result.
+__device__ bool ranking_inconsistent(const DecodeArgs &a, int64_t bh, int64_t head, int hl, uint64_t *kp,
+                                     uint64_t *kq, int *wcnt, int *bcast) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     if (a.nb == 0) {  // uniform: no barrier is skipped by part of the workgroup
         if (tid == 0 && a.ndisc) a.ndisc[head] = 0;
@@ -115,30 +206,29 @@ __device__ bool ranking_inconsistent(const DecodeArgs &a, int64_t bh, int64_t he
     }
     const uint8_t *ph = a.phead + head * a.nbc;
     const float *lh = a.lhat + head * a.nbc;
-    // thread t takes blocks [t*K, t*K + K): count its promoted blocks, scan
-    // the counts over the workgroup, then write the entries (pair order is
-    // irrelevant to the count)
+    const float4 *sth = reinterpret_cast<const float4 *>(a.step_ml + (bh * a.g + hl) * a.nbc * 8);
+    // thread t takes blocks t, t + 256, ...: count its promoted blocks, scan
+    // the counts over the workgroup, then write the keys (pair order is
+    // irrelevant to the count).  Up to KR blocks per thread stay in
+    // registers between the count and the writes; more are counted from
+    // their flags, then loaded KR at a time.
     const int nb = (int)a.nb, K = (nb + 255) / 256;
-    const int i0 = tid * K < nb ? tid * K : nb, i1 = i0 + K < nb ? i0 + K : nb;
-    // up to KR blocks per thread: every load issued at once (the log-masses
-    // of blocks that turn out not promoted are simply unused)
-    constexpr int KR = 4;
+    constexpr int KR = 8;
     bool fr[KR];
     float ar[KR], fpr[KR];
     int mine = 0;
     if (K <= KR) {
-#pragma unroll
-        for (int k = 0; k < KR; ++k) {
-            // unconditional loads at a clamped, in-range block
-            const int i = i0 + k < nb ? i0 + k : nb - 1;
-            fr[k] = i0 + k < i1 && ph[i] != 0;
-            ar[k] = lh[i];
-            fpr[k] = fp16_block_logmass(a, bh, i, hl);
-        }
+        load_blocks<KR>(a, ph, lh, sth, tid, nb, fr, ar, fpr);
 #pragma unroll
         for (int k = 0; k < KR; ++k) mine += fr[k] ? 1 : 0;
     } else {
-        for (int i = i0; i < i1; ++i) mine += ph[i] != 0;
+        for (int c = tid; c < nb; c += 256 * 16) {
+            uint8_t f[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) f[u] = ph[c + 256 * u < nb ? c + 256 * u : nb - 1];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) mine += (c + 256 * u < nb && f[u] != 0) ? 1 : 0;
+        }
     }
     const int incl = wave_incl_scan_int(mine);
     if (lane == 63) wcnt[wave] = incl;
@@ -149,68 +239,69 @@ __device__ bool ranking_inconsistent(const DecodeArgs &a, int64_t bh, int64_t he
         pos += w < wave ? wcnt[w] : 0;
         n += wcnt[w];
     }
-    if (K <= KR) {
+    auto put = [&](float aa, float ff) {
+        kp[pos++] = ((uint64_t)ord_key(aa) << 32) | ord_key(ff);
+    };
+    if (K > KR) {
+        for (int c = tid; c < nb; c += 256 * KR) {
+            load_blocks<KR>(a, ph, lh, sth, c, nb, fr, ar, fpr);
+#pragma unroll
+            for (int k = 0; k < KR; ++k)
+                if (fr[k]) put(ar[k], fpr[k]);
+        }
+    } else {
 #pragma unroll
         for (int k = 0; k < KR; ++k)
-            if (fr[k]) {
-                pa[pos] = ar[k];
-                pf[pos] = fpr[k];
-                ++pos;
-            }
-    } else {
-        for (int i = i0; i < i1; ++i)
-            if (ph[i] != 0) {
-                pa[pos] = lh[i];
-                pf[pos] = fp16_block_logmass(a, bh, i, hl);
-                ++pos;
-            }
+            if (fr[k]) put(ar[k], fpr[k]);
     }
+    // the merge sorts' padding: keys above every real one up to the next
+    // power of two, in both pair buffers
+    const int np2 = n > 1 ? 1 << (32 - __builtin_clz(n - 1)) : 1;
+    if (n > PAIRWISE_MAX)
+        for (int i = n + tid; i < np2; i += 256) kp[i] = kq[i] = ~0ull;
     __syncthreads();
-    // Discordant pairs: (a_i - a_j)(f_i - f_j) < 0.
     int cnt = 0;
     if (n <= PAIRWISE_MAX) {
-        // every pair, 8 at a time (independent LDS reads)
-        for (int i = tid; i < n; i += 256) {
-            const float ai = pa[i], fi = pf[i];
-            int j = i + 1;
-            for (; j + 8 <= n; j += 8) {
-                float aj[8], fj[8];
+        // Discordant pairs one by one, 8 partners at a time: thread i takes
+        // the partners i + 1, ..., i + (n - 1) / 2 (mod n), and for even n
+        // the opposite one i + n / 2 when i < n / 2 -- every pair once, and
+        // about n / 2 of them per thread.
+        static_assert(PAIRWISE_MAX <= 256, "one row per thread");
+        const int i = tid;
+        if (i < n) {
+            const uint64_t ki = kp[i];
+            const uint32_t ai = (uint32_t)(ki >> 32), fi = (uint32_t)ki;
+            const int nd = (n - 1) / 2 + ((n % 2 == 0 && i < n / 2) ? 1 : 0);
+            auto disc = [&](uint64_t kj) {
+                const uint32_t aj = (uint32_t)(kj >> 32), fj = (uint32_t)kj;
+                return ((ai < aj && fi > fj) || (ai > aj && fi < fj)) ? 1 : 0;
+            };
+            int d = 1;
+            for (; d + 8 <= nd + 1; d += 8) {
+                uint64_t kj[8];
 #pragma unroll
                 for (int u = 0; u < 8; ++u) {
-                    aj[u] = pa[j + u];
-                    fj[u] = pf[j + u];
+                    const int j = i + d + u;
+                    kj[u] = kp[j < n ? j : j - n];
                 }
 #pragma unroll
-                for (int u = 0; u < 8; ++u) cnt += ((ai - aj[u]) * (fi - fj[u]) < 0.0f) ? 1 : 0;
+                for (int u = 0; u < 8; ++u) cnt += disc(kj[u]);
             }
-            for (; j < n; ++j) cnt += ((ai - pa[j]) * (fi - pf[j]) < 0.0f) ? 1 : 0;
+            for (; d <= nd; ++d) {
+                const int j = i + d;
+                cnt += disc(kp[j < n ? j : j - n]);
+            }
         }
     } else {
-        // Sorted by (a, f), a pair tied in a has f ascending and a pair tied
-        // in f is never strictly inverted, so the count is the number of
-        // strict inversions of the f sequence in that order: a merge sort by
-        // (a, f), then a merge sort by f counting, per pass, the left-run keys
-        // above each right-run key.  O(n log n) in log2(n) barrier-separated
-        // passes each (the binary searches are dependent LDS reads, so below
-        // PAIRWISE_MAX promoted blocks the pairs are cheaper).
-        float *ca = pa, *cf = pf, *na = qa, *nf = qf;
-        for (int w = 1; w < n; w *= 2) {
-            merge_pass(ca, cf, na, nf, n, w);
-            __syncthreads();
-            float *t = ca;
-            ca = na;
-            na = t;
-            t = cf;
-            cf = nf;
-            nf = t;
-        }
-        for (int w = 1; w < n; w *= 2) {  // ca and na are free: na takes the f keys of the next pass
-            cnt += merge_pass(nullptr, cf, nullptr, na, n, w);
-            __syncthreads();
-            float *t = cf;
-            cf = na;
-            na = t;
-        }
+        // Sorted by (INT8, FP16), a pair tied in INT8 has FP16 ascending and
+        // a pair tied in FP16 is never strictly inverted, so the count is the
+        // number of strict inversions of the FP16 sequence in that order.
+        if (n <= 512)
+            cnt = sort_and_count<2>(kp, kq, n);
+        else if (n <= 1024)
+            cnt = sort_and_count<4>(kp, kq, n);
+        else
+            cnt = sort_and_count<8>(kp, kq, n);
     }
     cnt = wave_total_sum_int(cnt);
     __syncthreads();  // every thread has read wcnt
@@ -237,8 +328,7 @@ template <bool RANK>
 __global__ __launch_bounds__(256) void merge_cert_kernel(DecodeArgs a) {
     __shared__ float2 red[4][64];
     __shared__ float qn_lds;
-    __shared__ float pa[RANK ? ADAPT_MAX_NB : 1], pf[RANK ? ADAPT_MAX_NB : 1];
-    __shared__ float qa[RANK ? ADAPT_MAX_NB : 1], qf[RANK ? ADAPT_MAX_NB : 1];  // merge-sort buffers
+    __shared__ uint64_t kp[RANK ? ADAPT_MAX_NB : 1], kq[RANK ? ADAPT_MAX_NB : 1];  // ranking keys, merge-sort buffers
     __shared__ int wcnt[4], bcast;
     const int h = blockIdx.x;
     const int64_t kvh = blockIdx.y, b = blockIdx.z;
@@ -264,18 +354,29 @@ __global__ __launch_bounds__(256) void merge_cert_kernel(DecodeArgs a) {
     if (e1.x != NEG_INF) L += e1.y * __builtin_amdgcn_exp2f(e1.x - M);
     L = wave_total_sum(L);
     const float *pacc = a.part_acc + (bh * S * g + h) * D + 2 * lane;  // split s at pacc[s * g * D]
+    // wave w sums the splits w, w + 4, ... in order, 8 of them loaded at once
     float2 acc = make_float2(0.0f, 0.0f);
-#pragma unroll 8
-    for (int s = wave; s < S; s += 4) {
-        const float m_s = pml[s * g].x;
-        const float w = (L > 0.0f && m_s != NEG_INF) ? __builtin_amdgcn_exp2f(m_s - M) / L : 0.0f;
-        const float2 v = *reinterpret_cast<const float2 *>(pacc + (int64_t)s * g * D);
-        acc.x += w * v.x;
-        acc.y += w * v.y;
+    for (int s0 = wave; s0 < S; s0 += 32) {
+        float ms[8];
+        float2 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int s = s0 + 4 * u < S ? s0 + 4 * u : S - 1;  // past the end: a re-read, not added
+            ms[u] = pml[s * g].x;
+            v[u] = *reinterpret_cast<const float2 *>(pacc + (int64_t)s * g * D);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            if (s0 + 4 * u < S) {
+                const float w = (L > 0.0f && ms[u] != NEG_INF) ? __builtin_amdgcn_exp2f(ms[u] - M) / L : 0.0f;
+                acc.x += w * v[u].x;
+                acc.y += w * v[u].y;
+            }
+        }
     }
     red[wave][lane] = acc;
     __syncthreads();
-    const bool inconsistent = RANK && ranking_inconsistent(a, bh, head, h, pa, pf, qa, qf, wcnt, &bcast);
+    const bool inconsistent = RANK && ranking_inconsistent(a, bh, head, h, kp, kq, wcnt, &bcast);
     if (wave == 0) {
         float2 o = red[0][lane];
 #pragma unroll

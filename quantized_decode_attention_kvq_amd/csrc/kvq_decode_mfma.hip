@@ -314,8 +314,9 @@ __device__ __forceinline__ void issue_fb(const DecodeArgs &a, int64_t bh, int64_
 // softmax uses exp2.  State: m_run / l_run of head m (this lane's column; l as
 // this lane's share of the 8-position groups) and the P.V accumulators.
 // RANK: a step of FP16 keys also writes, per head, its largest score and the
-// sum of exp2(score - that) over its valid tokens to rank_out[head] (the FP16
-// block masses of the ranking check).
+// sum of exp2(score - that) over its valid tokens to rank_out[head * rank_hs]
+// (the FP16 block masses of the ranking check; each head's statistics slots
+// are contiguous, rank_hs apart).
 struct WaveState {
     float m_run, l_run;
     float4_t acc[8];
@@ -333,6 +334,7 @@ template <bool CERT, bool RANK, bool ROT, typename Mid>
 __device__ __forceinline__ void process_step(const uint8_t *stage, uint32_t mk, int p_lo, int p_hi,
                                              const uint4 (&qb)[4], const uint4 (&qrh)[4], const uint4 (&qrl)[4],
                                              float sml2, WaveState &w, int lane, float eta, float2 *rank_out,
+                                             int64_t rank_hs,
                                              int g, Mid &&mid) {
     const int m = lane & 15, g4 = lane >> 4;
     const bool partial = p_lo > 0 || p_hi < 32;  // wave-uniform
@@ -426,9 +428,9 @@ __device__ __forceinline__ void process_step(const uint8_t *stage, uint32_t mk, 
             for (int i = 0; i < 4; ++i) es += (sc[e][i] == NEG_INF) ? 0.0f : __builtin_amdgcn_exp2f(sc[e][i] - bmax);
         es = sum_across_rows(es);
         if (g4 == 0 && m < g) {
-            rank_out[m] = make_float2(bmax, es);
+            rank_out[m * rank_hs] = make_float2(bmax, es);
             // a 16-token step fills two 8-token statistics slots
-            if (!(mk & 2u)) rank_out[g + m] = make_float2(NEG_INF, 0.0f);
+            if (!(mk & 2u)) rank_out[m * rank_hs + 1] = make_float2(NEG_INF, 0.0f);
         }
     }
     const float m_new = fmaxf(w.m_run, bmax);
@@ -954,9 +956,8 @@ __device__ __forceinline__ void decode_group(const DecodeArgs &a, const int spli
         if (nvalid > 0)
             process_step<CERT, RANK, ROT>(stage, mk, p_lo, p_lo + nvalid, qb, qrh, qrl, sml2, ws, lane,
                                      CERT ? h2f(teta_lds[blk - blo]) : 0.0f,
-                                     RANK ? a.step_ml + ((bh * a.nbc + blk) * 8 + sub * (8 / steps_of(mk))) * g
-                                          : nullptr,
-                                     g, mid);
+                                     RANK ? a.step_ml + (bh * g * a.nbc + blk) * 8 + sub * (8 / steps_of(mk)) : nullptr,
+                                     a.nbc * 8, g, mid);
         else
             mid();
         return true;
@@ -1437,7 +1438,7 @@ __device__ __forceinline__ void decode_group_stream(const DecodeArgs &a, const i
         const int nvalid = keep ? (int)(left < step_len ? (left > 0 ? left : 0) : step_len) : 0;
         if (nvalid > 0)
             process_step<false, false, ROT>(stage, mk, p_lo, p_lo + nvalid, qb, qrh, qrl, sml2, ws, lane, 0.0f,
-                                            nullptr, g, mid);
+                                            nullptr, 0, g, mid);
         else
             mid();
         live &= ~(1u << s);

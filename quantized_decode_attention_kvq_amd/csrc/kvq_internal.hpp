@@ -73,7 +73,7 @@ struct DecodeArgs {
     // adaptive precision (null otherwise): promoted tiles per (b, kvh,
     // block) [B*Hkv][nbc] (bit 0 key, bit 1 value), OR-ed into the bound
     // masks; with the certificate, per FP16 key step its per-head largest
-    // score and exp2-sum, [B*Hkv][nbc][8][G] (log2 units), and for the
+    // score and exp2-sum, [B*Hkv][G][nbc][8] (log2 units), and for the
     // ranking check in the certificate merge each head's own key promotions
     // [B][Hq][nbc], its INT8 block log-masses [B][Hq][nbc], the discordant
     // pair counts [B][Hq] (or null) and tau_rank
