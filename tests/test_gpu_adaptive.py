@@ -187,11 +187,11 @@ def test_empty_cache():
 
 
 @pytest.mark.parametrize("kw,tau_cov,kmin,kmax", [
-    (dict(B=1, T=80000), 0.9999, 1025, 2048),                  # 8 searches in flight per thread
-    (dict(B=1, Hkv=1, Hq=4, T=140000), 1.5, 2049, 1 << 30),   # one element after another
+    (dict(B=1, T=80000), 0.9999, 1025, 2048),                  # up to 8 elements per thread
+    (dict(B=1, Hkv=1, Hq=4, T=140000), 1.5, 2049, 1 << 30),   # chunks of 2048 one after another
 ])
 def test_ranking_check_over_many_promoted_blocks(kw, tau_cov, kmin, kmax):
-    # heads promoting more than 1024 blocks: the discordant pairs are counted
+    # heads promoting more than 256 blocks: the discordant pairs are counted
     # by the merge sorts instead of pair by pair
     w = small("llama3_8b_32k", **kw)
     ref, g = _run(w.name, workloads.make(w), w, w.T, w.fallback_frac, tau_cov, tau_rank=0.3)
