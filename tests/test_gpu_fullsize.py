@@ -17,7 +17,7 @@ import torch
 import oracle
 import quantized_decode_attention_kvq_amd as kvq
 import workloads
-from kvq_testlib import OUT_TOL, SM, normwise_err
+from kvq_testlib import OUT_TOL, SM, normwise_err, taus_for
 
 pytestmark = pytest.mark.gpu
 
@@ -119,3 +119,40 @@ def test_bulk_quantize_full_size_sampled(rot):
             ]
             for name, g, o in pairs:
                 np.testing.assert_array_equal(g.cpu().numpy(), o, err_msg=f"{name} head {h} window {t0}")
+
+
+def test_automatic_kernel_past_the_matrix_core_limit():
+    # 1,050,000 tokens per sequence: 16,407 blocks, more than the matrix-core
+    # kernel lists (128 blocks per split, 128 splits), so the automatic choice
+    # is the VALU kernel, which appends with the append kernel first.  One
+    # (b, kvh) group of four query heads, checked whole against the oracle.
+    T = 1_050_000
+    w = workloads.WORKLOADS["llama3_8b_32k"].scaled(B=1, Hkv=1, Hq=4, T=T)
+    print(f"[full size] automatic kernel at {w}", flush=True)
+    d = workloads.make(w, "cuda")
+    q = d["q"].contiguous()
+    oc = oracle.Cache(d["k16"].cpu().numpy(), d["v16"].cpu().numpy(), T)
+    tk, tv = taus_for(oc, q.cpu().numpy(), w.fallback_frac)
+    ref, omask = oc.attention(q.cpu().numpy(), SM, tk, tv)
+    nb = (T + 63) // 64
+    assert nb > 128 * 128
+    c = kvq.KVCache(w.B, w.Hkv, w.cap, k16=d["k16"], v16=d["v16"])
+    kvq.kvq_quantize_append(c, T - 1)
+    out = torch.empty_like(q)
+    mask = torch.full((1, 1, nb), 0xEE, dtype=torch.uint8, device="cuda")
+    kvq.kvq_append_decode(c, q, SM, tk, tv, out=out, mask_out=mask)
+    torch.cuda.synchronize()
+    assert c.length == T
+    _check_group_tier1(c, oc, 0, 0, T)
+    np.testing.assert_array_equal(mask.cpu().numpy(), omask)
+    err = normwise_err(out.float().cpu().numpy(), ref)
+    assert np.all(np.isfinite(err)) and err.max() <= OUT_TOL, err.max()
+    # the same decode through the VALU kernel by name gives the same bits, and
+    # the matrix-core kernel refuses the sequence
+    out_v = torch.empty_like(q)
+    kvq.kvq_decode_attn(c, q, SM, tk, tv, out=out_v, kernel=kvq.KERNEL_VALU)
+    torch.cuda.synchronize()
+    assert torch.equal(out_v, out)
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.kvq_decode_attn(c, q, SM, tk, tv, kernel=kvq.KERNEL_MFMA)
+    assert "unsupported" in str(e.value)
