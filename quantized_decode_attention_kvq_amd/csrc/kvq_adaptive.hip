@@ -27,6 +27,7 @@
 // keys).
 #include "kvq_decode_common.hpp"
 #include "kvq_mfma.hpp"
+#include "kvq_quant_row.hpp"
 
 namespace kvq {
 
@@ -66,8 +67,13 @@ __global__ __launch_bounds__(64) void rotate_query_kernel(AdaptArgs a) {
 // lane (row m, k-group g4) holds channels 32 g4 + 8 kc .. +8 of token m for
 // instruction kc (32 contiguous code bytes per lane), and the q operand uses
 // the same channel order.  Result lane (head m, g4): tokens 4 g4 .. +3.
+// With a.t_new >= 0 the wave of that token's block first appends it (the
+// fused append's arithmetic: the row quantized by lanes 0-15, its tier-1
+// bytes and its block's statistics written as the append kernel would) and
+// scores the block with the token's fresh codes and scale.
 template <bool ROT>
 __global__ __launch_bounds__(256) void score_int8_kernel(AdaptArgs a) {
+    __shared__ __attribute__((aligned(16))) uint8_t nk_lds[4][D], nv_lds[4][D];  // the appended token's codes
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int m = lane & 15, g4 = lane >> 4;
     const int64_t kvh = blockIdx.y, b = blockIdx.z;
@@ -89,12 +95,69 @@ __global__ __launch_bounds__(256) void score_int8_kernel(AdaptArgs a) {
         const int64_t i = ((int64_t)blockIdx.x * 4 + wave) * BPW + r;
         if (i >= a.nb) break;
         const int64_t t0 = i * BLK;
+        // the appended token, when it lies in this block (wave-uniform)
+        const bool app = a.t_new >= 0 && a.t_new / BLK == i;
+        const int p_new = app ? (int)(a.t_new % BLK) : -1;
+        uint32_t nks = 0u;
+        if (app) {
+            const int64_t row = bh * a.cap + a.t_new;
+            RowQuant rq = {};
+            if (lane < 16) {
+                rq = quant_row16(load_row16(a.c.k16 + row * D, a.c.v16 + row * D, lane), ROT, lane);
+                *reinterpret_cast<uint2 *>(&nk_lds[wave][8 * lane]) = make_uint2(rq.kc[0], rq.kc[1]);
+                *reinterpret_cast<uint2 *>(&nv_lds[wave][8 * lane]) = make_uint2(rq.vc[0], rq.vc[1]);
+                // tier-1 bytes: key codes, key scale, value scales
+                *reinterpret_cast<uint2 *>(a.c.k_codes + row * D + 8 * lane) = make_uint2(rq.kc[0], rq.kc[1]);
+                if (lane == 0) a.c.k_scales[row] = (uint16_t)rq.ksb;
+                if ((lane & 3) == 0) a.c.v_scales[row * 4 + (lane >> 2)] = (uint16_t)rq.vsb;
+            }
+            nks = __builtin_amdgcn_readfirstlane(rq.ksb);
+            const uint32_t kerr = __builtin_amdgcn_readfirstlane(__float_as_uint(rq.kerr));
+            const uint32_t verr = __builtin_amdgcn_readfirstlane(__float_as_uint(rq.verr));
+            // value nibbles: a new block starts with the token's nibble in
+            // byte (c, 0) and zeros elsewhere; else the token's nibble is
+            // replaced in its byte (clear, then set: same address, in order)
+            uint8_t *vblk = a.c.v_codes + (bh * a.nbc + i) * (D * BLK / 2);
+            if (p_new == 0) {
+                for (int k = lane; k < D * 2; k += 64)
+                    *reinterpret_cast<uint4 *>(vblk + 16 * k) =
+                        make_uint4((k & 1) ? 0u : (uint32_t)(nv_lds[wave][k >> 1] & 0x0Fu), 0u, 0u, 0u);
+            } else {
+#pragma unroll
+                for (int k = 0; k < 2; ++k) {
+                    const int ch = lane + 64 * k;
+                    const int byte = ch * (BLK / 2) + (p_new >> 1);
+                    const int sh = 8 * (byte & 3) + 4 * (p_new & 1);
+                    unsigned int *word = reinterpret_cast<unsigned int *>(vblk + (byte & ~3));
+                    atomicAnd(word, ~(0x0Fu << sh));
+                    atomicOr(word, (uint32_t)(nv_lds[wave][ch] & 0x0Fu) << sh);
+                }
+            }
+            // block statistics: max with the earlier tokens' (non-negative
+            // floats and +Inf order like their bit patterns), or the token's
+            // own for a new block
+            if (lane == 0) {
+                const int64_t si = bh * a.nbc + i;
+                if (p_new > 0) {
+                    atomicMax(reinterpret_cast<unsigned int *>(a.c.k_err + si), kerr);
+                    atomicMax(reinterpret_cast<unsigned int *>(a.c.v_err + si), verr);
+                } else {
+                    a.c.k_err[si] = __uint_as_float(kerr);
+                    a.c.v_err[si] = __uint_as_float(verr);
+                }
+            }
+        }
         float sc[4][4];
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
             const int8_t *row = a.c.k_codes + (bh * a.cap + t0 + 16 * tt + m) * D + 32 * g4;
-            const uint4 c0 = *reinterpret_cast<const uint4 *>(row);
-            const uint4 c1 = *reinterpret_cast<const uint4 *>(row + 16);
+            uint4 c0 = *reinterpret_cast<const uint4 *>(row);
+            uint4 c1 = *reinterpret_cast<const uint4 *>(row + 16);
+            if (app && 16 * tt + m == p_new) {
+                // the appended row, from this launch's quantization
+                c0 = *reinterpret_cast<const uint4 *>(&nk_lds[wave][32 * g4]);
+                c1 = *reinterpret_cast<const uint4 *>(&nk_lds[wave][32 * g4 + 16]);
+            }
             float4_t acc = {0.f, 0.f, 0.f, 0.f};
             const uint4 a0 = i8x8_to_h8(c0.x, c0.y), a1 = i8x8_to_h8(c0.z, c0.w);
             const uint4 a2 = i8x8_to_h8(c1.x, c1.y), a3 = i8x8_to_h8(c1.z, c1.w);
@@ -109,7 +172,10 @@ __global__ __launch_bounds__(256) void score_int8_kernel(AdaptArgs a) {
                 acc = mfma(a3, qrl[3], acc);
             }
             const uint2 ks = *reinterpret_cast<const uint2 *>(a.c.k_scales + bh * a.cap + t0 + 16 * tt + 4 * g4);
-            const uint32_t kw[4] = {ks.x & 0xFFFFu, ks.x >> 16, ks.y & 0xFFFFu, ks.y >> 16};
+            uint32_t kw[4] = {ks.x & 0xFFFFu, ks.x >> 16, ks.y & 0xFFFFu, ks.y >> 16};
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr)
+                if (app && 16 * tt + 4 * g4 + rr == p_new) kw[rr] = nks;
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
                 const int64_t t = t0 + 16 * tt + 4 * g4 + rr;

@@ -89,8 +89,8 @@ WsLayout ws_layout(const kvq_cache *c, int32_t g, int64_t splits, size_t slots) 
 
 // Adaptive workspace: the decode workspace, then [lhat float x B*Hq*NBc]
 // [phead uint8 x B*Hq*NBc] [promote uint8 x B*Hkv*NBc] [step statistics
-// float2 x B*Hkv*G*NBc*8, each head's blocks and slots contiguous], each
-// padded to 256 B.
+// float2 x B*Hkv*G*NBc*8, each head's blocks and slots contiguous] [rotated
+// query, fp16 hi and lo parts x B*Hq*2*128], each padded to 256 B.
 struct AdaptLayout {
     size_t lhat, phead, promote, step, qrot, total;
 };
@@ -312,9 +312,9 @@ bool bad_tol(float t) { return t != t || t < 0.0f; }
 
 // Decode over the cache's tokens; with append, token `length` (already in
 // k16/v16) is first quantized into tier 1 and joins the decode: fused into
-// the matrix-core kernel, or as an append launch before the VALU kernel (and
-// before the scoring pass of the adaptive decode).  On success with append,
-// c->length grows by one.
+// the matrix-core kernel (or, in the adaptive decode, into the scoring pass
+// that runs first), or as an append launch before the VALU kernel.  On
+// success with append, c->length grows by one.
 kvq_status decode_impl(kvq_cache *c, const uint16_t *q, int32_t q_heads, float sm_scale, float tau_k,
                        float tau_v, uint16_t *out, uint8_t *mask_out, void *workspace, size_t ws_bytes,
                        void *stream, int32_t kernel, int32_t splits, void *split_done, bool append,
@@ -376,9 +376,8 @@ kvq_status decode_impl(kvq_cache *c, const uint16_t *q, int32_t q_heads, float s
     if (scratch_ws && (certify || ad || nbh > (int64_t)KVQ_SCRATCH_MAX_GROUPS || w.total > ws_bytes))
         return KVQ_ERR_WORKSPACE;
 
-    if (append && (!mf || ad)) {
-        // no fused path in the VALU kernel, and the adaptive scoring pass
-        // reads the new token's codes: append first
+    if (append && !mf) {
+        // no fused path in the VALU kernel: append first
         if ((st = kvq_quantize_append(c, 1, stream)) != KVQ_OK) return st;
         append = false;
     }
@@ -443,6 +442,10 @@ kvq_status decode_impl(kvq_cache *c, const uint16_t *q, int32_t q_heads, float s
         aa.hq = q_heads;
         aa.g = g;
         aa.key_rot = a.key_rot;
+        // the scoring pass appends the new token (it reads its codes first);
+        // the decode then finds it in tier 1
+        aa.t_new = a.t_new;
+        a.t_new = -1;
         aa.sm = sm_scale;
         aa.tau_cov = ad->tau_cov;
         aa.tau_vc = ad->tau_vc;

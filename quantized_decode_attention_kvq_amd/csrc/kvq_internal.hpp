@@ -95,6 +95,7 @@ struct AdaptArgs {
     int32_t *kstar;          // [B][Hq] blocks each head promotes, or null
     uint16_t *qrot;          // [B][Hq][2][D] rotated query, fp16 hi and lo parts (rotated codec)
     int64_t cap, length, nbc, nb;
+    int64_t t_new;           // token the scoring pass appends first (its rows in k16/v16), or -1
     int32_t hkv, hq, g;
     int32_t key_rot;         // KVQ_CODEC_ROTATE_K
     float sm, tau_cov, tau_vc;

@@ -28,7 +28,7 @@ import torch
 import oracle
 import quantized_decode_attention_kvq_amd as kvq
 import workloads
-from kvq_testlib import OUT_TOL, SM, gpu_cache, normwise_err, oracle_cache, small, taus_for
+from kvq_testlib import OUT_TOL, SM, assert_tier1_equal, gpu_cache, normwise_err, oracle_cache, small, taus_for
 
 pytestmark = pytest.mark.gpu
 
@@ -64,6 +64,9 @@ def _run(name, d, w, T, frac, tau_cov, tau_vc=INF, tau_rank=1.0, tau_out=INF, ap
                                      append=append, mask_out=mask)
     torch.cuda.synchronize()
     assert c.length == T
+    if append:
+        # the scoring pass appended the token: tier 1 as the oracle quantized it
+        assert_tier1_equal(c, oc, T)
     m = mask.cpu().numpy()
     # promotions bracketed by the oracle at the nudged tolerances (per bit)
     for bit in (1, 2):
@@ -124,8 +127,9 @@ def test_adaptive_group_sizes_and_value_promotion(name, kw, tau_vc):
     _run(name, workloads.make(w), w, w.T, w.fallback_frac, 0.9, tau_vc=tau_vc, tau_rank=0.2)
 
 
-def test_adaptive_with_append_and_certificate_recompute():
-    w = small("llama3_8b_32k", B=2, T=777)
+@pytest.mark.parametrize("T", [777, 641])  # the appended token inside a block / opening one
+def test_adaptive_with_append_and_certificate_recompute(T):
+    w = small("llama3_8b_32k", B=2, T=T)
     _run(w.name, workloads.make(w), w, w.T, w.fallback_frac, 0.9, tau_rank=0.5, tau_out=5.0, append=True)
 
 

@@ -103,21 +103,26 @@ def test_rotated_certificate(tau_out):
     assert np.all(np.isfinite(err)) and err.max() <= OUT_TOL, f"{err.max():.3e}"
 
 
-def test_rotated_adaptive_bracketed():
+@pytest.mark.parametrize("append", [False, True])
+def test_rotated_adaptive_bracketed(append):
     w = small("llama3_8b_32k_niah", B=2, T=900)
     d = workloads.make(w)
-    print("[rotation] adaptive", flush=True)
+    print(f"[rotation] adaptive append={append}", flush=True)
     oc = oracle_cache(d, w.T, key_rotation=True)
     q = d["q"].numpy()
     tk, tv = taus_for(oc, q, w.fallback_frac)
     lo = oc.adaptive(q, SM, tk, tv, 0.995 - 1e-5, tau_rank=0.3)
     hi = oc.adaptive(q, SM, tk, tv, 0.995 + 1e-5, tau_rank=0.3)
     ref = oc.adaptive(q, SM, tk, tv, 0.995, tau_rank=0.3)
-    c = gpu_cache(d, w.T, key_rotation=True)
+    c = gpu_cache(d, w.T - 1 if append else w.T, key_rotation=True)
     nb = (w.T + 63) // 64
     mask = torch.full((w.B, w.Hkv, nb), 0xEE, dtype=torch.uint8, device="cuda")
-    g = kvq.kvq_decode_attn_adaptive(c, d["q"].cuda(), SM, tk, tv, 0.995, tau_rank=0.3, mask_out=mask)
+    g = kvq.kvq_decode_attn_adaptive(c, d["q"].cuda(), SM, tk, tv, 0.995, tau_rank=0.3, mask_out=mask,
+                                     append=append)
     torch.cuda.synchronize()
+    assert c.length == w.T
+    if append:
+        assert_tier1_equal(c, oc, w.T)
     m = mask.cpu().numpy()
     assert np.all((lo["masks"] & 1) <= (m & 1)) and np.all((m & 1) <= (hi["masks"] & 1))
     # every group against the oracle under the GPU's masks and recompute
