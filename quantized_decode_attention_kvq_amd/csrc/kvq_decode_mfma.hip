@@ -87,6 +87,17 @@ __device__ __forceinline__ uint4 i4x8_to_h8(uint32_t x) {
                       __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d));
 }
 
+// 4 int4 codes (the low 16 bits, nibble k = token k) -> fp16 (n0, n1),
+// (n2, n3): each nibble moved under the low half or the high half of a dword
+// and widened as the low nibbles are above.  Exact.
+__device__ __forceinline__ uint2 i4x4_to_h4(uint32_t x) {
+    const half2_t lo_bias = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+    const uint32_t a = (x & 0xFu) | ((x & 0xF0u) << 12), b = ((x >> 8) & 0xFu) | ((x & 0xF000u) << 4);
+    const half2_t ha = __builtin_bit_cast(half2_t, a ^ 0x64086408u) + lo_bias;
+    const half2_t hb = __builtin_bit_cast(half2_t, b ^ 0x64086408u) + lo_bias;
+    return make_uint2(__builtin_bit_cast(uint32_t, ha), __builtin_bit_cast(uint32_t, hb));
+}
+
 __device__ __forceinline__ uint32_t pack_h2(float a, float b) {
     const float2_t v = {a, b};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, half2_t));
@@ -327,15 +338,107 @@ struct WaveState {
     uint32_t smax, amax;
 };
 
+// A 16-token step whose keys alone fall back (mask 1), compact: tokens
+// p_lo .. p_hi-1 of the half (p_lo = 0 or 16) are rows 0 .. 15 of one Q.K^T
+// subtile (token r from chunk r/4, lane slot 16st + 4dg + r%4 of the stage),
+// so result lane (head m, g4) holds tokens 4 g4 .. +3 of the step, and those
+// same 4 tokens are that lane's k-slots of a v_mfma_f32_16x16x16_f16 P.V:
+// A = the value codes of channel 16mt + m for them (4 nibbles at byte
+// p_lo/2 + 2 g4 of the channel's 16), B = p * s_v in fp16 (one rounding of p,
+// one of the product, as for a certified half).  Same online softmax,
+// certificate parts and ranking statistics as process_step.
+template <bool CERT, bool RANK, typename Mid>
+__device__ __forceinline__ void process_key16(const uint8_t *stage, int p_lo, int p_hi, const uint4 (&qb)[4],
+                                              float sml2, WaveState &w, int lane, float eta, float2 *rank_out,
+                                              int64_t rank_hs, int g, Mid &&mid) {
+    const int m = lane & 15, g4 = lane >> 4;
+    float4_t c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+        c = mfma(*reinterpret_cast<const uint4 *>(stage + FB_K16 + 1024 * (m >> 2) + 16 * (16 * st + 4 * g4 + (m & 3))),
+                 qb[st], c);
+    mid();
+    const int nv = p_hi - p_lo;  // valid tokens of the step
+    float sc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sc[i] = (4 * g4 + i < nv) ? c[i] * sml2 : NEG_INF;
+    float bmax = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    bmax = max_across_rows(bmax);
+    if (RANK && rank_out) {
+        float es = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) es += (sc[i] == NEG_INF) ? 0.0f : __builtin_amdgcn_exp2f(sc[i] - bmax);
+        es = sum_across_rows(es);
+        if (g4 == 0 && m < g) {
+            rank_out[m * rank_hs] = make_float2(bmax, es);
+            rank_out[m * rank_hs + 1] = make_float2(NEG_INF, 0.0f);  // a 16-token step fills two 8-token slots
+        }
+    }
+    const float m_new = fmaxf(w.m_run, bmax);
+    const float alpha = (m_new == NEG_INF) ? 1.0f : __builtin_amdgcn_exp2f(w.m_run - m_new);
+    float pv[4];
+    float psum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        pv[i] = (sc[i] == NEG_INF) ? 0.0f : __builtin_amdgcn_exp2f(sc[i] - m_new);
+        psum += pv[i];
+    }
+    w.m_run = m_new;
+    w.l_run = w.l_run * alpha + psum;
+    if (CERT) w.e_run = w.e_run * alpha + psum * eta;
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) w.acc[mt] *= alpha;
+    }
+    // P.V over the lane's 4 tokens
+    const half2_t p01 = __builtin_bit_cast(half2_t, pack_h2(pv[0], pv[1]));
+    const half2_t p23 = __builtin_bit_cast(half2_t, pack_h2(pv[2], pv[3]));
+    const int tp = p_lo + 4 * g4;  // the lane's first token, as a position of the half
+    uint16_t vn[8];
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+        vn[mt] = *reinterpret_cast<const uint16_t *>(stage + ST_V + (mt >> 2) * 1024 + 16 * (16 * (mt & 3) + m) +
+                                                     (tp >> 1));
+    // value scales of the 4 tokens: dwords of groups (0,1) and (2,3); tokens
+    // outside the step carry other tokens' scales (stale past `length`): 0
+    const uint4 s01 = *reinterpret_cast<const uint4 *>(stage + ST_VS + 4 * tp);
+    const uint4 s23 = *reinterpret_cast<const uint4 *>(stage + ST_VS + 128 + 4 * tp);
+    uint32_t a01[4] = {s01.x, s01.y, s01.z, s01.w}, a23[4] = {s23.x, s23.y, s23.z, s23.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        if (4 * g4 + i >= nv) a01[i] = a23[i] = 0u;
+    if (CERT) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            w.smax = umax(w.smax, umax(umax(a01[i] & 0xFFFFu, a01[i] >> 16), umax(a23[i] & 0xFFFFu, a23[i] >> 16)));
+    }
+#pragma unroll
+    for (int gg = 0; gg < 4; ++gg) {
+        // (s of token 0, token 1) and (token 2, token 3) for group gg
+        const uint32_t *sg = gg < 2 ? a01 : a23;
+        const uint32_t sel = (gg & 1) ? 0x07060302u : 0x05040100u;
+        const uint32_t s01g = __builtin_amdgcn_perm(sg[1], sg[0], sel), s23g = __builtin_amdgcn_perm(sg[3], sg[2], sel);
+        const uint2 bop = make_uint2(__builtin_bit_cast(uint32_t, p01 * __builtin_bit_cast(half2_t, s01g)),
+                                     __builtin_bit_cast(uint32_t, p23 * __builtin_bit_cast(half2_t, s23g)));
+        w.acc[2 * gg] = mfma16(i4x4_to_h4(vn[2 * gg]), bop, w.acc[2 * gg]);
+        w.acc[2 * gg + 1] = mfma16(i4x4_to_h4(vn[2 * gg + 1]), bop, w.acc[2 * gg + 1]);
+    }
+}
+
 // ROT: the key codes are those of Hadamard-rotated keys, scored against the
 // rotated query (qrh + qrl, its fp16 high and low parts); FP16 key rows use
-// the query itself.
-template <bool CERT, bool RANK, bool ROT, typename Mid>
+// the query itself.  K16: key-only fallback steps take the compact path
+// (process_key16).
+template <bool CERT, bool RANK, bool ROT, bool K16, typename Mid>
 __device__ __forceinline__ void process_step(const uint8_t *stage, uint32_t mk, int p_lo, int p_hi,
                                              const uint4 (&qb)[4], const uint4 (&qrh)[4], const uint4 (&qrl)[4],
                                              float sml2, WaveState &w, int lane, float eta, float2 *rank_out,
                                              int64_t rank_hs,
                                              int g, Mid &&mid) {
+    if (K16 && mk == 1u) {
+        process_key16<CERT, RANK>(stage, p_lo, p_hi, qb, sml2, w, lane, eta, rank_out, rank_hs, g, mid);
+        return;
+    }
     const int m = lane & 15, g4 = lane >> 4;
     const bool partial = p_lo > 0 || p_hi < 32;  // wave-uniform
 
@@ -597,7 +700,7 @@ __device__ __forceinline__ uint16_t f16_up(float x) {
 // CERT: also the per-head output certificate's per-split parts (the
 // mass-weighted value error, the largest certified value scale and
 // fallback |v|, and the largest certified block errors).
-template <bool CERT, bool RANK, bool ROT>
+template <bool CERT, bool RANK, bool ROT, bool K16>
 __device__ __forceinline__ void decode_group(const DecodeArgs &a, const int split, const int64_t kvh,
                                              const int64_t b) {
     // NW waves x NSTAGE stages x 6656 B of ring.  Before the stream starts, the
@@ -954,7 +1057,7 @@ __device__ __forceinline__ void decode_group(const DecodeArgs &a, const int spli
         const int64_t left = a.length - (blk * BLK + step_len * sub);
         const int nvalid = (int)(left < step_len ? (left > 0 ? left : 0) : step_len);
         if (nvalid > 0)
-            process_step<CERT, RANK, ROT>(stage, mk, p_lo, p_lo + nvalid, qb, qrh, qrl, sml2, ws, lane,
+            process_step<CERT, RANK, ROT, K16>(stage, mk, p_lo, p_lo + nvalid, qb, qrh, qrl, sml2, ws, lane,
                                      CERT ? h2f(teta_lds[blk - blo]) : 0.0f,
                                      RANK ? a.step_ml + (bh * g * a.nbc + blk) * 8 + sub * (8 / steps_of(mk)) : nullptr,
                                      a.nbc * 8, g, mid);
@@ -1437,7 +1540,7 @@ __device__ __forceinline__ void decode_group_stream(const DecodeArgs &a, const i
         const int64_t left = a.length - ((int64_t)blk * BLK + step_len * sub);
         const int nvalid = keep ? (int)(left < step_len ? (left > 0 ? left : 0) : step_len) : 0;
         if (nvalid > 0)
-            process_step<false, false, ROT>(stage, mk, p_lo, p_lo + nvalid, qb, qrh, qrl, sml2, ws, lane, 0.0f,
+            process_step<false, false, ROT, false>(stage, mk, p_lo, p_lo + nvalid, qb, qrh, qrl, sml2, ws, lane, 0.0f,
                                             nullptr, 0, g, mid);
         else
             mid();
@@ -1484,7 +1587,10 @@ bool stream_supports(const DecodeArgs &a) {
 
 template <bool CERT, bool RANK, bool ROT>
 __global__ __launch_bounds__(NW * 64, NW / 4) void decode_mfma_kernel(DecodeArgs a) {
-    decode_group<CERT, RANK, ROT>(a, blockIdx.x, blockIdx.y, blockIdx.z);
+    // the compact key-only fallback steps in the adaptive decode, where the
+    // promoted tiles make them common (elsewhere their extra registers cost
+    // more than they save)
+    decode_group<CERT, RANK, ROT, RANK && !ROT>(a, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
 // Index of the rank-th group i in [0, n) (in index order) with a set byte
@@ -1532,7 +1638,7 @@ __global__ __launch_bounds__(NW * 64, NW / 4) void decode_mfma_gated_kernel(Deco
     for (int rank = blockIdx.y;; rank += gridDim.y) {
         const int64_t bh = nth_set(a.gate, a.g, nbh, rank, wcnt, &pick);
         if (bh < 0) break;
-        decode_group<false, false, ROT>(a, blockIdx.x, bh % a.hkv, bh / a.hkv);
+        decode_group<false, false, ROT, false>(a, blockIdx.x, bh % a.hkv, bh / a.hkv);  // tolerances 0: no key-only step
     }
 }
 

@@ -20,6 +20,14 @@ __device__ __forceinline__ float4_t mfma(uint4 a, uint4 b, float4_t c) {
                                                   __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
 }
 
+// v_mfma_f32_16x16x16_f16: A lane l holds row l%16, k-slots [4*(l/16), +4);
+// B lane l holds column l%16, the same k-slots; the result as above.
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4_t mfma16(uint2 a, uint2 b, float4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(half4_t, a), __builtin_bit_cast(half4_t, b), c,
+                                                 0, 0, 0);
+}
+
 // 4 int8 codes -> 2 x fp16 pairs (exact): offset code u = c + 128 under the
 // fp16 exponent of 1024 reads as 1024 + u; minus 1152 leaves c.
 __device__ __forceinline__ uint2 i8x4_to_h4(uint32_t x) {
