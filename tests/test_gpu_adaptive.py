@@ -121,7 +121,9 @@ def test_adaptive_matches_oracle(tau_cov):
 
 @pytest.mark.parametrize("name,kw,tau_vc", [("single_head", dict(T=1024), INF),
                                             ("stress_fallback", dict(B=2, T=700), 1e-3),
-                                            ("llama3_70b_128k", dict(B=1, T=1300), 1e-4)])
+                                            ("llama3_70b_128k", dict(B=1, T=1300), 1e-4),
+                                            ("llama3_8b_32k", dict(B=1, Hkv=2, Hq=6, T=1000), INF),    # G = 3
+                                            ("llama3_8b_32k", dict(B=1, Hkv=2, Hq=32, T=1000), INF)])  # G = 16
 def test_adaptive_group_sizes_and_value_promotion(name, kw, tau_vc):
     w = small(name, **kw)
     _run(name, workloads.make(w), w, w.T, w.fallback_frac, 0.9, tau_vc=tau_vc, tau_rank=0.2)
