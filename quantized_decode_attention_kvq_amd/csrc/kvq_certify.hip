@@ -187,33 +187,19 @@ __device__ __forceinline__ int sort_and_count(uint64_t *kp, uint64_t *kq, int n)
     return cnt;
 }
 
-// Ranking-consistency check of one head (Methodology 3): its promoted blocks
-// are compacted into LDS as keys pairing the order-preserving images of
-// their INT8 and FP16 log-masses, the pairs ordered oppositely by the two
-// are counted (every pair up to PAIRWISE_MAX blocks, by merge sorts above),
-// and the head is inconsistent when they exceed tau_rank of all pairs.  The
-// integer images compare exactly like the log-masses, so a pair is
-// discordant when one log-mass is strictly lower and the other strictly
-// higher (log-masses are finite or -inf here; a NaN, from non-finite
-// inputs, leaves the count unspecified).  All 256 threads take part; every
-// thread returns the result.
-__device__ bool ranking_inconsistent(const DecodeArgs &a, int64_t bh, int64_t head, int hl, uint64_t *kp,
-                                     uint64_t *kq, int *wcnt, int *bcast) {
+// The promoted blocks of one head, compacted into kp[0 .. n) as keys pairing
+// the order-preserving images of their INT8 and FP16 log-masses; returns n.
+// Thread t takes blocks t, t + 256, ...: it counts its promoted blocks, the
+// counts are scanned over the workgroup, and each thread writes its keys at
+// its offset (pair order is irrelevant to the count).  A head of at most
+// 256 KR blocks keeps each thread's blocks in registers between the count
+// and the writes; a longer one is counted from its flags, then loaded KR
+// blocks at a time.  All 256 threads take part.
+template <int KR>
+__device__ __forceinline__ int compact_keys(const DecodeArgs &a, const uint8_t *ph, const float *lh,
+                                            const float4 *sth, int nb, uint64_t *kp, int *wcnt) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    if (a.nb == 0) {  // uniform: no barrier is skipped by part of the workgroup
-        if (tid == 0 && a.ndisc) a.ndisc[head] = 0;
-        return false;
-    }
-    const uint8_t *ph = a.phead + head * a.nbc;
-    const float *lh = a.lhat + head * a.nbc;
-    const float4 *sth = reinterpret_cast<const float4 *>(a.step_ml + (bh * a.g + hl) * a.nbc * 8);
-    // thread t takes blocks t, t + 256, ...: count its promoted blocks, scan
-    // the counts over the workgroup, then write the keys (pair order is
-    // irrelevant to the count).  Up to KR blocks per thread stay in
-    // registers between the count and the writes; more are counted from
-    // their flags, then loaded KR at a time.
-    const int nb = (int)a.nb, K = (nb + 255) / 256;
-    constexpr int KR = 8;
+    const int K = (nb + 255) / 256;
     bool fr[KR];
     float ar[KR], fpr[KR];
     int mine = 0;
@@ -254,6 +240,38 @@ __device__ bool ranking_inconsistent(const DecodeArgs &a, int64_t bh, int64_t he
         for (int k = 0; k < KR; ++k)
             if (fr[k]) put(ar[k], fpr[k]);
     }
+    return n;
+}
+
+// Ranking-consistency check of one head (Methodology 3): its promoted blocks
+// are compacted into LDS as keys pairing the order-preserving images of
+// their INT8 and FP16 log-masses, the pairs ordered oppositely by the two
+// are counted (every pair up to PAIRWISE_MAX blocks, by merge sorts above),
+// and the head is inconsistent when they exceed tau_rank of all pairs.  The
+// integer images compare exactly like the log-masses, so a pair is
+// discordant when one log-mass is strictly lower and the other strictly
+// higher (log-masses are finite or -inf here; a NaN, from non-finite
+// inputs, leaves the count unspecified).  All 256 threads take part; every
+// thread returns the result.
+__device__ bool ranking_inconsistent(const DecodeArgs &a, int64_t bh, int64_t head, int hl, uint64_t *kp,
+                                     uint64_t *kq, int *wcnt, int *bcast) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (a.nb == 0) {  // uniform: no barrier is skipped by part of the workgroup
+        if (tid == 0 && a.ndisc) a.ndisc[head] = 0;
+        return false;
+    }
+    const uint8_t *ph = a.phead + head * a.nbc;
+    const float *lh = a.lhat + head * a.nbc;
+    const float4 *sth = reinterpret_cast<const float4 *>(a.step_ml + (bh * a.g + hl) * a.nbc * 8);
+    // up to 8 blocks per thread are held in registers between the count and
+    // the writes, as many as the head has (one load round and one log-mass
+    // each); longer heads are counted from their flags, then loaded 8 blocks
+    // at a time
+    const int nb = (int)a.nb, K = (nb + 255) / 256;
+    const int n = K <= 1   ? compact_keys<1>(a, ph, lh, sth, nb, kp, wcnt)
+                  : K <= 2 ? compact_keys<2>(a, ph, lh, sth, nb, kp, wcnt)
+                  : K <= 4 ? compact_keys<4>(a, ph, lh, sth, nb, kp, wcnt)
+                           : compact_keys<8>(a, ph, lh, sth, nb, kp, wcnt);
     // the merge sorts' padding: keys above every real one up to the next
     // power of two, in both pair buffers
     const int np2 = n > 1 ? 1 << (32 - __builtin_clz(n - 1)) : 1;
@@ -319,8 +337,9 @@ __device__ bool ranking_inconsistent(const DecodeArgs &a, int64_t bh, int64_t he
 
 // One workgroup per query head h of (b, kvh).  The output merge is the
 // split merge's (every wave forms M and L; wave w sums the splits w, w + 4,
-// ..., lane l holds channels 2l and 2l + 1); wave 1 then gathers the
-// certificate's parts of the splits (two per lane, summed in double).  RANK
+// ..., lane l holds channels 2l and 2l + 1); wave 1 then combines the
+// certificate's parts of the splits, loaded at the start with the split
+// statistics (two per lane, summed in double).  RANK
 // (adaptive decode): the head's ranking check runs first, and an
 // inconsistent head is flagged for the recompute like one whose certificate
 // exceeds tau_out.
@@ -348,6 +367,21 @@ __global__ __launch_bounds__(256) void merge_cert_kernel(DecodeArgs a) {
     const float2 *pml = a.part_ml + bh * S * g + h;  // split s at pml[s * g]
     const float2 e0 = lane < S ? pml[lane * g] : make_float2(NEG_INF, 0.0f);
     const float2 e1 = lane + 64 < S ? pml[(lane + 64) * g] : make_float2(NEG_INF, 0.0f);
+    // wave 1's certificate parts of the splits (two per lane), loaded with
+    // the split statistics: used only at the end
+    float pe[2] = {0.0f, 0.0f};
+    float2 psa[2] = {make_float2(0.0f, 0.0f), make_float2(0.0f, 0.0f)}, pkv = make_float2(0.0f, 0.0f);
+    if (wave == 1) {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int r = lane + 64 * k;
+            if (r < S) {
+                pe[k] = a.part_e[(bh * S + r) * g + h];
+                psa[k] = a.part_sa[bh * S + r];
+            }
+        }
+        pkv = a.part_kv[bh];
+    }
     const float M = wave_total_max(fmaxf(e0.x, e1.x));  // DPP moves
     float L = 0.0f;
     if (e0.x != NEG_INF) L += e0.y * __builtin_amdgcn_exp2f(e0.x - M);
@@ -399,9 +433,9 @@ __global__ __launch_bounds__(256) void merge_cert_kernel(DecodeArgs a) {
                 if (e.x != NEG_INF) {
                     const double f = (double)__builtin_amdgcn_exp2f(e.x - M);
                     Ld += (double)e.y * f;
-                    E += (double)a.part_e[(bh * S + r) * g + h] * f;
+                    E += (double)pe[k] * f;
                 }
-                const float2 sa = a.part_sa[bh * S + r];
+                const float2 sa = psa[k];
                 smax = fmaxf(smax, sa.x);
                 amax = max_keep_nan(amax, sa.y);  // a NaN value keeps the certificate NaN
             }
@@ -414,7 +448,7 @@ __global__ __launch_bounds__(256) void merge_cert_kernel(DecodeArgs a) {
             amax = max_keep_nan(amax, __shfl_xor(amax, o));
         }
         if (lane == 0) {
-            const float2 kv = a.part_kv[bh];
+            const float2 kv = pkv;
             const double e_val = Ld > 0.0 ? E / Ld : 0.0;
             const double delta = (double)key_bound(a.sm, qn_lds, kv.x);
             const double r1 = 7.0 * (double)smax + (double)kv.y;
