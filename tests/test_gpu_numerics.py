@@ -78,3 +78,33 @@ def test_needle_over_offset_haystack(G, kname, kern):
         err, m = _run(d, T, frac, kern)
         print(f"  frac {frac}: max normwise err {err.max():.3e}, fallback blocks {int((m != 0).sum())}", flush=True)
         assert np.all(np.isfinite(err)) and err.max() <= OUT_TOL, f"frac {frac}: {err.max():.3e}"
+
+
+@pytest.mark.parametrize("kname,kern", KERNELS)
+def test_query_dynamic_range(kname, kern):
+    """Queries far from N(0,1): outlier channels 50x and 300x the rest, heads
+    scaled by 1e-3 and 1e2, a head that is zero but for one channel, and a
+    zero head.  The fp16 query enters the products exactly, so a head's
+    largest channel does not cost its small ones precision (a fixed-point
+    query with 16 bits against max|q| did: 2.6e-3 here)."""
+    w = small("llama3_8b_32k", B=2)
+    print(f"[numerics] query dynamic range, kernel {kname}", flush=True)
+    d = workloads.make(w)
+    q = d["q"].float()
+    g = torch.Generator().manual_seed(7)
+    for b in range(w.B):
+        for h in range(w.Hq):
+            c = torch.randperm(128, generator=g)[:2]
+            q[b, h, c[0]] *= 50.0
+            if h % 4 == 1:
+                q[b, h, c[1]] *= 300.0
+    q[0, 2] *= 1e-3
+    q[1, 3] *= 1e2
+    q[0, 5] = 0.0
+    q[0, 5, 17] = 3.0
+    q[1, 6] = 0.0
+    d["q"] = q.half()
+    assert torch.isfinite(d["q"]).all()
+    err, m = _run(d, w.T, 0.01, kern)
+    print(f"  max normwise err {err.max():.3e}, fallback k {np.mean(m & 1):.4f} v {np.mean(m >> 1):.4f}", flush=True)
+    assert np.all(np.isfinite(err)) and err.max() <= OUT_TOL, f"{err.max():.3e}"
