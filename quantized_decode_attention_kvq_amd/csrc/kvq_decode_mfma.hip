@@ -375,12 +375,13 @@ __device__ __forceinline__ void process_key16(const uint8_t *stage, int p_lo, in
         }
     }
     const float m_new = fmaxf(w.m_run, bmax);
-    const float alpha = (m_new == NEG_INF) ? 1.0f : __builtin_amdgcn_exp2f(w.m_run - m_new);
+    const float m_use = (m_new == NEG_INF) ? 0.0f : m_new;  // as in process_step
+    const float alpha = __builtin_amdgcn_exp2f(w.m_run - m_use);
     float pv[4];
     float psum = 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        pv[i] = (sc[i] == NEG_INF) ? 0.0f : __builtin_amdgcn_exp2f(sc[i] - m_new);
+        pv[i] = __builtin_amdgcn_exp2f(sc[i] - m_use);
         psum += pv[i];
     }
     w.m_run = m_new;
@@ -537,15 +538,18 @@ __device__ __forceinline__ void process_step(const uint8_t *stage, uint32_t mk, 
         }
     }
     const float m_new = fmaxf(w.m_run, bmax);
-    // a step with no finite score so far leaves m_new at -inf
-    const float alpha = (m_new == NEG_INF) ? 1.0f : __builtin_amdgcn_exp2f(w.m_run - m_new);
+    // exp2(-inf) is 0: against a finite reference a -inf score weighs 0, and
+    // a -inf running max scales its sum and accumulators (still 0) by 0.  A
+    // step with no finite score so far leaves m_new at -inf; 0 stands in.
+    const float m_use = (m_new == NEG_INF) ? 0.0f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(w.m_run - m_use);
     float pv[2][4];
     float psum = 0.0f;
 #pragma unroll
     for (int e = 0; e < 2; ++e)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            pv[e][i] = (sc[e][i] == NEG_INF) ? 0.0f : __builtin_amdgcn_exp2f(sc[e][i] - m_new);
+            pv[e][i] = __builtin_amdgcn_exp2f(sc[e][i] - m_use);
             psum += pv[e][i];
         }
     w.m_run = m_new;
