@@ -362,8 +362,13 @@ kvq_status decode_impl(kvq_cache *c, const uint16_t *q, int32_t q_heads, float s
     const bool mf = k == KVQ_KERNEL_MFMA;
     // one round of matrix-core workgroups (a second round evens out groups
     // with many FP16 tiles, but pays the set-up twice: measured 3% faster on
-    // the needle workload's adaptive step and 4% slower on the diffuse one)
-    const int64_t s = nb > 0 ? choose_splits(c, nb, splits, mf ? 1 : 4, mf ? kvq::MFMA_MAX_BPS : kvq::MAX_BPS) : 1;
+    // the needle workload's adaptive step and 4% slower on the diffuse one).
+    // The streaming kernel (plain decode) has no per-split block limit, so a
+    // long sequence keeps one round there too: 8 splits of 256 blocks for
+    // the 128k workload instead of 16 of 128 in two rounds.
+    const bool use_stream = mf && !certify && !ad && !no_stream && kvq::stream_fits(nb);
+    const int64_t max_bps = use_stream ? nb : (mf ? (int64_t)kvq::MFMA_MAX_BPS : (int64_t)kvq::MAX_BPS);
+    const int64_t s = nb > 0 ? choose_splits(c, nb, splits, mf ? 1 : 4, max_bps) : 1;
     const int64_t bps = nb > 0 ? (nb + s - 1) / s : 1;
     const int64_t s_eff = nb > 0 ? (nb + bps - 1) / bps : 1;
     // offsets for the largest split count, so that passes with different

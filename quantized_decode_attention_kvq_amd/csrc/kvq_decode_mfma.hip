@@ -1584,6 +1584,8 @@ __global__ __launch_bounds__(NW * 64, NW / 4) void decode_stream_kernel(DecodeAr
     decode_group_stream<ROT>(a, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
+bool stream_fits(int64_t nb) { return nb >= 1 && nb <= STREAM_MAX_NB; }
+
 bool stream_supports(const DecodeArgs &a) {
     return !a.cert_mode && !a.gate && !a.promote && !a.step_ml && a.nb >= 1 && a.nb <= STREAM_MAX_NB &&
            a.bps >= 1;

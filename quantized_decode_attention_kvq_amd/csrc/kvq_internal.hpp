@@ -120,6 +120,10 @@ hipError_t launch_merge(const DecodeArgs &a, int batch, hipStream_t s);
 // The merge of a certified decode: outputs, per-head certificates, recompute flags.
 hipError_t launch_merge_cert(const DecodeArgs &a, int batch, hipStream_t s);
 bool mfma_supports(int g);
+// True when a plain decode (no certificate, no promotions) of nb blocks per
+// sequence runs the streaming matrix-core kernel, which takes any number of
+// blocks per split (the table kernel at most MFMA_MAX_BPS).
+bool stream_fits(int64_t nb);
 
 // adaptive precision: INT8 scoring pass (a.nb > 0) and selection (the
 // ranking check runs in the certificate merge when a.step_ml is set)
