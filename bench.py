@@ -26,8 +26,9 @@ Prints one JSON line:
              and the split merge done by the last workgroup of each group):
              its bytes are the step's, and its launch time comes from HIP
              events on the stream around a second pass of the timed loop's
-             steps (queued behind a spin kernel, so that the span is the
-             kernels' own and not the host's submission latency).  Elsewhere (VALU
+             steps (queued behind a third, untimed pass, so that the span is
+             the kernels' own, not the host's submission latency, and the GPU
+             stays under load).  Elsewhere (VALU
              kernel, --unfused) it is the split-K kernel: the decode's bytes
              but the output, timed by events around each of the same steps
              run again eagerly (the library records one after the split-K
@@ -265,8 +266,8 @@ def timed_steps(args, R, step, stream):
     launches step i on layer cache i % R), after args.warmup untimed ones and
     20 ms of untimed replays (the GPU's clock settles under sustained load):
     (host wall clock between synchronisations; HIP events recorded on the
-    stream around a second pass of the same steps, which a spin kernel ahead
-    of them keeps from starting before the steps are submitted).
+    stream around a second pass of the same steps, queued behind a third,
+    untimed one that keeps them from starting before they are submitted).
     With args.graph, the steps of up to 32 layers (cycling the R layer
     caches) are captured in one HIP graph, as a decoder's per-token graph
     holds its layers, plus one graph of the remaining steps, and replayed;
@@ -319,14 +320,15 @@ def timed_steps(args, R, step, stream):
     run_all()
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / args.steps * 1e3
-    # the same steps again between HIP events, queued behind a short spin
-    # kernel: the first event is then taken once the host has submitted the
-    # steps, so the span is the kernels' own (back to back in a graph), not
-    # the host's submission latency before the first one
+    # the same steps again between HIP events, queued behind one more untimed
+    # pass of them: the first event is then taken once the host has submitted
+    # the steps, so the span is the kernels' own (back to back in a graph),
+    # not the host's submission latency before the first one, and the GPU is
+    # under load throughout (an idle spin ahead of them let its clock drop,
+    # and the timed steps then ran up to 15% slower than the wall-clock pass)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     strm = torch.cuda.current_stream()
-    if hasattr(torch.cuda, "_sleep"):
-        torch.cuda._sleep(500000)  # about 0.2 ms of spinning at 2.4 GHz
+    run_all()
     e0.record(strm)
     run_all()
     e1.record(strm)
@@ -541,8 +543,9 @@ def main():
         split_ms = call_ms = ms_step_ev
         merge_ms = 0.0
         launch_source = (f"HIP events on the stream around a second pass of the timed loop's {args.steps} "
-                         f"{'graph-replayed' if args.graph else 'eager'} steps, queued behind a spin kernel "
-                         "(so the span starts at the first kernel, not at the host's submission); one kernel per step")
+                         f"{'graph-replayed' if args.graph else 'eager'} steps, queued behind a third, untimed pass "
+                         "(so the span starts at the first kernel, not at the host's submission, and the GPU stays "
+                         "under load); one kernel per step")
     else:
         evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
         for e3 in evs:
