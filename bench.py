@@ -68,7 +68,8 @@ APPEND_COUNTERS = os.path.join(ROOT, "profiles", "append_counters.json")
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--steps", type=int, default=200,
+                   help="timed steps (200 decode steps of one layer take about 16 ms at 32k)")
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="llama3_8b_32k")
     p.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma", "mfma_table"])
